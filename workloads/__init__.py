@@ -1,0 +1,264 @@
+"""Seeded synthetic inputs for MLA paged latent decode.
+
+This module only builds inputs: random numbers, their rounding to the storage
+formats (bf16 and OCP fp8 e4m3fn, done by torch's CPU casts), page tables and
+sequence lengths.  It holds none of the attention arithmetic, so both the
+float64 oracle and the GPU path can take their inputs from here without
+sharing any part of the computation.
+
+Cache layout (Triton MLA page, "data flow" section): one pool of pages of
+shape ``[num_blocks, page_size, head_size]`` where each row is the single
+latent vector ``[kv_c (kv_lora_rank) | k_pe (rope 64)]``; ``block_table[b, j]``
+names the physical page that holds logical block ``j`` of sequence ``b``
+(lshu.cn article, section 11).
+
+The five workloads below are the decode shapes this library is measured and
+checked on.  Every array is built from ``numpy.random.default_rng(seed)``
+with a fixed draw order (seq_lens, page permutation, q, pool), so a seed
+always gives identical bytes.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+BF16 = "bf16"
+FP8_E4M3 = "fp8_e4m3"
+
+# fp32(192 ** -0.5): the softmax scale of a DeepSeek-V3 style head
+# (qk_nope 128 + qk_rope 64).  Kept as the fp32-rounded value.
+DSV3_SCALE = float(np.float32(192.0 ** -0.5))
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    seed: int
+    batch: int
+    num_heads: int
+    head_size: int          # D_qk = kv_lora_rank + 64
+    kv_lora_rank: int       # D_v
+    page_size: int
+    num_blocks: int
+    kv_dtype: str           # BF16 or FP8_E4M3
+    k_scale: float
+    scale: float
+    seq_lens_fixed: Optional[Sequence[int]] = None
+    seq_len_range: Optional[tuple] = None   # inclusive (lo, hi), uniform draw
+    seq_len_head: Optional[Sequence[int]] = None  # fixed leading lengths, rest drawn
+    parity_splits: Sequence[int] = (1,)
+    description: str = ""
+
+    def draw_seq_lens(self, rng: np.random.Generator) -> np.ndarray:
+        if self.seq_lens_fixed is not None:
+            return np.asarray(self.seq_lens_fixed, dtype=np.int32)
+        head = list(self.seq_len_head or [])
+        lo, hi = self.seq_len_range
+        rest = rng.integers(lo, hi, size=self.batch - len(head), endpoint=True)
+        return np.concatenate([np.asarray(head, np.int64), rest]).astype(np.int32)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload(
+            name="tiny", seed=1, batch=2, num_heads=16, head_size=576, kv_lora_rank=512,
+            page_size=16, num_blocks=16, kv_dtype=BF16, k_scale=1.0, scale=DSV3_SCALE,
+            seq_lens_fixed=(37, 100), parity_splits=(1, 4),
+            description="B=2 H=16 D=576 bf16, page 16, 16 pages, seq_lens {37,100}"),
+        Workload(
+            name="dsv3", seed=2, batch=64, num_heads=128, head_size=576, kv_lora_rank=512,
+            page_size=64, num_blocks=8192, kv_dtype=BF16, k_scale=1.0, scale=DSV3_SCALE,
+            seq_len_range=(1024, 8192), parity_splits=(16, 1),
+            description="B=64 H=128 D=576/512 bf16, page 64, 8192 pages, seq_lens U[1024,8192]"),
+        Workload(
+            name="skewed", seed=3, batch=8, num_heads=128, head_size=576, kv_lora_rank=512,
+            page_size=64, num_blocks=4096, kv_dtype=BF16, k_scale=1.0, scale=DSV3_SCALE,
+            seq_len_head=(131072,), seq_len_range=(512, 4096), parity_splits=(256, 1),
+            description="B=8 H=128 D=576 bf16, seq_lens {131072, 7 x U[512,4096]}, page 64"),
+        Workload(
+            name="h320", seed=4, batch=256, num_heads=16, head_size=320, kv_lora_rank=256,
+            page_size=16, num_blocks=65536, kv_dtype=BF16, k_scale=1.0, scale=DSV3_SCALE,
+            seq_len_range=(256, 4096), parity_splits=(8, 1),
+            description="B=256 H=16 D=320/256 bf16, page 16, seq_lens U[256,4096]"),
+        Workload(
+            name="fp8", seed=5, batch=128, num_heads=128, head_size=576, kv_lora_rank=512,
+            page_size=64, num_blocks=16384, kv_dtype=FP8_E4M3, k_scale=float(np.float32(0.05)),
+            scale=DSV3_SCALE, seq_len_range=(2048, 8192), parity_splits=(16, 1),
+            description="B=128 H=128 D=576 fp8 e4m3 cache (k_scale 0.05), page 64, U[2048,8192]"),
+    ]
+}
+
+
+@dataclasses.dataclass
+class DecodeInputs:
+    """One decode batch, every array in its storage format (raw bits)."""
+    workload: Workload
+    q_bits: np.ndarray          # uint16 [B, H, D]  (bf16 bits)
+    kv_bits: np.ndarray         # uint16 [NB, P, D] (bf16) or uint8 [NB, P, D] (fp8)
+    block_table: np.ndarray     # int32 [B, max_blocks_per_seq]
+    seq_lens: np.ndarray        # int32 [B]
+
+    @property
+    def kv_dtype(self) -> str:
+        return self.workload.kv_dtype
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (round-to-nearest-even, via torch's CPU cast)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def f32_to_e4m3fn_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to OCP fp8 e4m3fn (RNE), saturating to +-448 first."""
+    import torch
+    x = np.clip(np.ascontiguousarray(x, dtype=np.float32), -448.0, 448.0)
+    t = torch.from_numpy(x).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+def make_block_table(rng: np.random.Generator, seq_lens: np.ndarray, page_size: int,
+                     num_blocks: int) -> np.ndarray:
+    """Each sequence takes the next ceil(n/P) pages of one seeded permutation
+    of the pool; unused entries are 0."""
+    pages_per_seq = [(int(n) + page_size - 1) // page_size for n in seq_lens]
+    need = sum(pages_per_seq)
+    if need > num_blocks:
+        raise ValueError(f"pool of {num_blocks} pages cannot hold {need} pages")
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    width = max(1, max(pages_per_seq) if pages_per_seq else 1)
+    table = np.zeros((len(seq_lens), width), dtype=np.int32)
+    at = 0
+    for b, k in enumerate(pages_per_seq):
+        table[b, :k] = perm[at:at + k]
+        at += k
+    return table
+
+
+def _normal_f32(rng: np.random.Generator, shape, chunk: int = 1 << 24) -> np.ndarray:
+    out = np.empty(int(np.prod(shape)), dtype=np.float32)
+    for s in range(0, out.size, chunk):
+        e = min(out.size, s + chunk)
+        out[s:e] = rng.standard_normal(e - s, dtype=np.float32)
+    return out.reshape(shape)
+
+
+def generate(workload: Workload | str, *, seq_lens: Optional[Sequence[int]] = None,
+             batch: Optional[int] = None, num_blocks: Optional[int] = None) -> DecodeInputs:
+    """Build the seeded inputs of a workload.
+
+    ``seq_lens``/``batch``/``num_blocks`` override the workload (used for
+    edge cases); the seed and the draw order stay the same.
+    """
+    w = WORKLOADS[workload] if isinstance(workload, str) else workload
+    rng = np.random.default_rng(w.seed)
+    if seq_lens is not None:
+        sl = np.asarray(seq_lens, dtype=np.int32)
+    else:
+        sl = w.draw_seq_lens(rng)
+    if batch is not None:
+        sl = sl[:batch]
+    nb = num_blocks if num_blocks is not None else w.num_blocks
+    table = make_block_table(rng, sl, w.page_size, nb)
+    B = len(sl)
+    q = _normal_f32(rng, (B, w.num_heads, w.head_size))
+    q_bits = f32_to_bf16_bits(q)
+    pool = _normal_f32(rng, (nb, w.page_size, w.head_size))
+    if w.kv_dtype == BF16:
+        kv_bits = f32_to_bf16_bits(pool)
+    else:
+        kv_bits = f32_to_e4m3fn_bits(pool / np.float32(w.k_scale))
+    return DecodeInputs(workload=w, q_bits=q_bits, kv_bits=kv_bits, block_table=table,
+                        seq_lens=sl)
+
+
+def small_case(*, seed: int, batch: int, num_heads: int, head_size: int, kv_lora_rank: int,
+               page_size: int, seq_lens: Sequence[int], kv_dtype: str = BF16,
+               k_scale: float = 1.0, extra_pages: int = 3, scale: float = DSV3_SCALE,
+               table_pad: int = 0) -> DecodeInputs:
+    """A custom small batch (edge cases, ragged lengths) with the same recipe."""
+    pages = sum((int(n) + page_size - 1) // page_size for n in seq_lens) + extra_pages
+    w = Workload(name=f"case{seed}", seed=seed, batch=batch, num_heads=num_heads,
+                 head_size=head_size, kv_lora_rank=kv_lora_rank, page_size=page_size,
+                 num_blocks=max(1, pages), kv_dtype=kv_dtype, k_scale=k_scale, scale=scale,
+                 seq_lens_fixed=tuple(int(n) for n in seq_lens))
+    inp = generate(w)
+    if table_pad:
+        inp.block_table = np.pad(inp.block_table, ((0, 0), (0, table_pad)))
+    return inp
+
+
+# ---------------------------------------------------------------- input transforms
+# These rearrange or poison inputs without touching values that are read.
+
+def referenced_slots(inp: DecodeInputs) -> np.ndarray:
+    """Boolean mask [NB, P]: True where a (page, slot) holds a token some
+    sequence reads."""
+    P = inp.workload.page_size
+    used = np.zeros(inp.kv_bits.shape[:2], dtype=bool)
+    for b, n in enumerate(inp.seq_lens):
+        n = int(n)
+        for j in range((n + P - 1) // P):
+            k = min(P, n - j * P)
+            used[inp.block_table[b, j], :k] = True
+    return used
+
+
+def poison_unreferenced(inp: DecodeInputs, *, poison_table: bool = True) -> DecodeInputs:
+    """Fill every unreferenced page row (including the tail slots of each
+    sequence's last page) with NaN, and point unused block_table entries at a
+    fully poisoned page when one exists."""
+    used = referenced_slots(inp)
+    kv = inp.kv_bits.copy()
+    nan = np.uint16(0x7FC0) if inp.kv_dtype == BF16 else np.uint8(0x7F)
+    kv[~used] = nan
+    table = inp.block_table.copy()
+    if poison_table:
+        free_pages = np.nonzero(~used.any(axis=1))[0]
+        if free_pages.size:
+            P = inp.workload.page_size
+            for b, n in enumerate(inp.seq_lens):
+                k = (int(n) + P - 1) // P
+                table[b, k:] = free_pages[0]
+    return dataclasses.replace(inp, kv_bits=kv, block_table=table)
+
+
+def permute_pages(inp: DecodeInputs, seed: int) -> DecodeInputs:
+    """Move every physical page to a new seeded position and remap the
+    block table so that each sequence still sees the same rows."""
+    rng = np.random.default_rng(seed)
+    nb = inp.kv_bits.shape[0]
+    new_of_old = rng.permutation(nb).astype(np.int32)
+    kv = np.empty_like(inp.kv_bits)
+    kv[new_of_old] = inp.kv_bits
+    table = new_of_old[inp.block_table]
+    return dataclasses.replace(inp, kv_bits=kv, block_table=table.astype(np.int32))
+
+
+def subset(inp: DecodeInputs, batches: Sequence[int]) -> DecodeInputs:
+    """The same pool with only the chosen sequences, in the given order."""
+    idx = np.asarray(batches, dtype=np.int64)
+    return dataclasses.replace(inp, q_bits=inp.q_bits[idx].copy(),
+                               block_table=inp.block_table[idx].copy(),
+                               seq_lens=inp.seq_lens[idx].copy())
+
+
+def expected_tokens(w: Workload) -> float:
+    """Expected total context tokens of a workload (mean of its length draw)."""
+    if w.seq_lens_fixed is not None:
+        return float(sum(w.seq_lens_fixed))
+    head = list(w.seq_len_head or [])
+    lo, hi = w.seq_len_range
+    return float(sum(head) + (w.batch - len(head)) * (lo + hi) / 2.0)
+
+
+__all__ = [
+    "BF16", "FP8_E4M3", "DSV3_SCALE", "Workload", "WORKLOADS", "DecodeInputs", "generate",
+    "small_case", "f32_to_bf16_bits", "f32_to_e4m3fn_bits", "make_block_table",
+    "referenced_slots", "poison_unreferenced", "permute_pages", "subset", "expected_tokens",
+]
