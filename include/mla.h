@@ -1,0 +1,192 @@
+/*
+ * mla.h -- C ABI of libmla: MLA (multi-head latent attention) paged decode
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes.  At one decode step every sequence b has one
+ * query per head, q[b, h, 0:D] = [q_nope (D_v) | q_pe (64)], and a paged
+ * cache of latent rows [kv_c (D_v = kv_lora_rank) | k_pe (64)], one row per
+ * context position.  All H heads read the same row stream as a single-head K
+ * (multi-query attention), and V is the first D_v columns of that same row
+ * ("Triton と MLA" page, section データフロー / data flow: the cache is passed
+ * to the decode kernel as a one-head K cache and its leading kv_lora_rank
+ * slice as V).  Position t of sequence b lives in physical page
+ * block_table[b][t / page_size], slot t % page_size ("vLLM 中 Attention
+ * Kernel 如何并行处理多个请求", section 十一).  A decode query sees every
+ * position, so there is no mask (same article, section 九).  Outputs:
+ *
+ *     s[t]      = scale * sum_d q[b,h,d] * K[t,d]        (d < D, t < n_b)
+ *     lse[b,h]  = ln sum_t exp(s[t])                      (natural log)
+ *     o[b,h,:]  = sum_t exp(s[t] - lse[b,h]) * K[t, 0:D_v]
+ *
+ * lse is always returned and is a natural logarithm ("Triton と MLA" page,
+ * 設計動機: lse is returned for cross-shard merging and lse_base_on_e
+ * defaults to true; "AttentionBackend" page, Limites et échecs: ln versus
+ * log2 must not be mixed).  For an fp8 cache one per-layer scale k_scale
+ * multiplies every element of K and V; for a bf16 cache k_scale is ignored
+ * ("Triton と MLA" page, データフロー: k_scale = v_scale = the layer's
+ * _k_scale, and the fp8 check is a no-op for bf16 caches).
+ *
+ * How it is computed.  Stage 1 splits each sequence's positions into
+ * segments and runs an online softmax (running max, running sum, rescaled
+ * accumulator; article section 七) over 32-position tiles of each segment.
+ * Each segment yields a partial (o_s, lse_s); a sequence covered by a single
+ * segment is written to o/lse directly.  Stage 2 merges the partials of the
+ * other sequences with the log-sum-exp rule of article section 十二.  Both
+ * stages run as HIP kernels on the caller's stream.
+ *
+ * Conventions for every function below.
+ *   - Device pointers are HIP device addresses owned by the caller; the
+ *     library never allocates, frees, copies to the host or synchronises.
+ *   - Arguments are checked on the host before anything is enqueued; on any
+ *     error the function returns a non-zero mla_status and enqueues nothing.
+ *   - The contents of block_table entries are trusted: a page index outside
+ *     [0, num_blocks) is undefined behaviour (the kernels do not check it).
+ *   - Entry points are re-entrant; concurrent calls must use distinct
+ *     workspaces and outputs.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,      /* a required pointer is NULL                                   */
+  MLA_ERR_HEAD_SIZE = 2, /* head_size not 576 or 320, or kv_lora_rank != head_size - 64
+                            ("Triton と MLA" page, 設計動機 and 境界と失敗: only these two
+                            head sizes are accepted)                                    */
+  MLA_ERR_PAGE_SIZE = 3, /* page_size not a positive multiple of 16, or the page_size
+                            argument differs from shape->page_size ("AttentionBackend"
+                            page, Limites et échecs: block sizes are multiples of 16)   */
+  MLA_ERR_DTYPE = 4,     /* q not bf16 (an fp8 query is refused: "Triton と MLA" page,
+                            境界と失敗), kv not bf16/fp8 e4m3fn, o not bf16/fp32        */
+  MLA_ERR_SHAPE = 5,     /* batch < 1, num_heads not a positive multiple of 16,
+                            num_blocks < 1 (empty cache), max_blocks_per_seq < 1, or a
+                            size whose byte count overflows                              */
+  MLA_ERR_SPLITS = 6,    /* num_kv_splits < 1 or above MLA_MAX_KV_SPLITS, or an unknown
+                            split mode                                                   */
+  MLA_ERR_WORKSPACE = 7, /* workspace NULL or smaller than mla_workspace_size() for the
+                            same shape, split mode and split count                       */
+  MLA_ERR_LAUNCH = 8,    /* HIP reported an error when the kernels were enqueued        */
+  MLA_ERR_ARGUMENT = 9   /* a non-finite or non-positive scale / k_scale, or num_cus < 1 */
+} mla_status;
+
+typedef enum mla_dtype {
+  MLA_BF16 = 0,     /* bfloat16                                                       */
+  MLA_FP8_E4M3 = 1, /* OCP fp8 e4m3fn: bias 7, max 448, no infinity (cache only)      */
+  MLA_FP32 = 2      /* float32 (output only)                                          */
+} mla_dtype;
+
+/* How stage 1 divides the positions of a batch among workgroups.
+ *
+ * MLA_SPLIT_PER_SEQUENCE -- the split-KV layout of the "Triton と MLA" page
+ *   (num_kv_splits per request, workspace [B, S] partials): sequence b is cut
+ *   into S segments of C_b = roundup(ceil(n_b / S), 32) positions; segment s
+ *   covers [s*C_b, min((s+1)*C_b, n_b)) and may be empty.  With S == 1 every
+ *   sequence is reduced by one workgroup in a fixed order: the result of a
+ *   sequence does not depend on the rest of the batch and is bitwise
+ *   reproducible (the page's batch-invariant mode forces one split), and no
+ *   workspace is needed.
+ *
+ * MLA_SPLIT_BALANCED -- the batch's 32-position tiles, sequence after
+ *   sequence, are cut into S equal runs ("work units"), one per workgroup and
+ *   head chunk, so that every workgroup streams the same amount of cache
+ *   whatever the mix of lengths.  A unit may hold the end of one sequence and
+ *   the start of the next.  Results are reproducible run to run for the same
+ *   batch, but a sequence's rounding may depend on the other lengths.
+ */
+typedef enum mla_split_mode {
+  MLA_SPLIT_PER_SEQUENCE = 0,
+  MLA_SPLIT_BALANCED = 1
+} mla_split_mode;
+
+#define MLA_MAX_KV_SPLITS 65536
+#define MLA_ROPE_DIM 64
+
+/* Problem shape.  Layouts (all row-major, densely packed unless noted):
+ *   q           [batch, num_heads, head_size]              q_dtype (bf16)
+ *   kv_cache    [num_blocks, page_size, head_size]         kv_dtype; row =
+ *               [kv_c (kv_lora_rank) | k_pe (64)]
+ *   block_table [batch, max_blocks_per_seq]                int32; entries at
+ *               index >= ceil(seq_lens[b] / page_size) are never read
+ *   seq_lens    [batch]                                    int32, >= 0
+ *   o           [batch, num_heads, kv_lora_rank]           o_dtype
+ *   lse         [batch, num_heads]                         float32
+ */
+typedef struct mla_shape {
+  int32_t batch;              /* B >= 1                                     */
+  int32_t num_heads;          /* H, a multiple of 16                        */
+  int32_t head_size;          /* D: 576 or 320                              */
+  int32_t kv_lora_rank;       /* D_v = D - 64: 512 or 256                   */
+  int32_t page_size;          /* P, a multiple of 16                        */
+  int32_t num_blocks;         /* pages in the pool, >= 1                    */
+  int32_t max_blocks_per_seq; /* block_table row stride in entries, >= 1    */
+  int32_t q_dtype;            /* mla_dtype: MLA_BF16                        */
+  int32_t kv_dtype;           /* mla_dtype: MLA_BF16 or MLA_FP8_E4M3        */
+  int32_t o_dtype;            /* mla_dtype: MLA_BF16 or MLA_FP32            */
+} mla_shape;
+
+/* The split count of the "Triton と MLA" page (主要ファイル,
+ * _compute_num_kv_splits): one split per 512 positions of the longest
+ * sequence, capped at twice the number of compute units.  Read as
+ * clamp(ceil(max_seq_len / 512), 1, 2 * num_cus).  Pure host function;
+ * returns 0 if num_cus < 1. */
+int32_t mla_pages_split_count(int32_t max_seq_len, int32_t num_cus);
+
+/* Choose a split mode and count for a batch, and the workspace it needs.
+ *   max_seq_len    longest sequence in the batch (host-side metadata)
+ *   total_seq_len  sum of the batch's lengths, or <= 0 if unknown (then
+ *                  batch * max_seq_len is assumed)
+ *   num_cus        compute units of the device (256 on MI355X)
+ *   deterministic  non-zero: MLA_SPLIT_PER_SEQUENCE with one split (no
+ *                  workspace, batch-invariant, see above)
+ * Otherwise the balanced mode is chosen with enough units to fill the device.
+ * The same function is meant to run when the workspace is reserved and when
+ * decode is called, so the two always agree ("Triton と MLA" page, 境界と失敗:
+ * stage 2 must see the split count stage 1 used).  Pure host function, no HIP
+ * call.  Outputs may not be NULL. */
+mla_status mla_plan(const mla_shape* shape, int32_t max_seq_len, int64_t total_seq_len,
+                    int32_t num_cus, int32_t deterministic, int32_t* split_mode,
+                    int32_t* num_kv_splits, size_t* workspace_bytes);
+
+/* Bytes of device workspace mla_decode needs for this shape, split mode and
+ * split count (0 when none is needed: per-sequence mode with one split).
+ * Returns 0 as well for an invalid shape or mode; mla_decode rejects those.
+ * Pure host function. */
+size_t mla_workspace_size(const mla_shape* shape, int32_t split_mode, int32_t num_kv_splits);
+
+/* Enqueue one MLA decode step on `hip_stream` (a hipStream_t, NULL for the
+ * null stream) of the current HIP device.
+ *   q, kv_cache, block_table, seq_lens   inputs, layouts as in mla_shape
+ *   scale          softmax scale applied to q.K (e.g. 192^-0.5), finite > 0
+ *   page_size      must equal shape->page_size
+ *   k_scale        per-layer dequantisation scale of an fp8 cache (finite > 0);
+ *                  ignored for a bf16 cache
+ *   num_kv_splits, split_mode   as returned by mla_plan (or chosen freely)
+ *   o, lse         outputs, every [b, h] entry is overwritten; a sequence
+ *                  with seq_lens[b] == 0 gets o = 0 and lse = -inf
+ *   workspace      device buffer of at least
+ *                  mla_workspace_size(shape, split_mode, num_kv_splits) bytes
+ *                  (may be NULL when that size is 0); contents on return are
+ *                  unspecified
+ * Returns MLA_OK once the kernels are enqueued; results are ready when the
+ * stream reaches them.  Inputs are not modified. */
+mla_status mla_decode(const mla_shape* shape, const void* q, const void* kv_cache,
+                      const int32_t* block_table, const int32_t* seq_lens, float scale,
+                      int32_t page_size, float k_scale, int32_t num_kv_splits,
+                      int32_t split_mode, void* o, float* lse, void* workspace,
+                      size_t workspace_bytes, void* hip_stream);
+
+/* A static, human-readable name for a status code (never NULL). */
+const char* mla_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,220 @@
+"""MLA paged latent decode for MI355X (gfx950): Python binding of libmla.
+
+A thin ctypes layer over the C ABI in ``include/mla.h``.  It only marshals
+arguments (shapes, dtypes, raw device pointers, the current HIP stream);
+every step of the decode runs in libmla's HIP kernels.  torch provides device
+memory and streams.  There is no fallback: if libmla.so is missing or cannot
+be loaded, every call raises.
+
+    o, lse = mla_decode(q, kv_cache, block_table, seq_lens, scale, page_size,
+                        k_scale, num_kv_splits)
+
+``q`` [B, H, D] bf16 = [q_nope (D_v) | q_pe (64)]; ``kv_cache``
+[num_blocks, page_size, D] bf16 or fp8 e4m3fn with rows [kv_c | k_pe];
+``block_table`` [B, max_blocks_per_seq] int32; ``seq_lens`` [B] int32.
+Returns ``o`` [B, H, D_v] (bf16 by default) and ``lse`` [B, H] float32
+(natural log).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+from . import _build
+
+__all__ = [
+    "MlaError", "mla_decode", "mla_plan", "mla_workspace_size", "mla_pages_split_count",
+    "mla_status_string", "SPLIT_PER_SEQUENCE", "SPLIT_BALANCED", "library_path", "load_library",
+    "MLA_BF16", "MLA_FP8_E4M3", "MLA_FP32",
+]
+
+MLA_OK, MLA_ERR_NULL, MLA_ERR_HEAD_SIZE, MLA_ERR_PAGE_SIZE, MLA_ERR_DTYPE = 0, 1, 2, 3, 4
+MLA_ERR_SHAPE, MLA_ERR_SPLITS, MLA_ERR_WORKSPACE, MLA_ERR_LAUNCH, MLA_ERR_ARGUMENT = 5, 6, 7, 8, 9
+MLA_BF16, MLA_FP8_E4M3, MLA_FP32 = 0, 1, 2
+SPLIT_PER_SEQUENCE, SPLIT_BALANCED = 0, 1
+MLA_MAX_KV_SPLITS = 65536
+
+
+class MlaShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "num_heads", "head_size", "kv_lora_rank", "page_size", "num_blocks",
+        "max_blocks_per_seq", "q_dtype", "kv_dtype", "o_dtype")]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_LIB = None
+
+
+def library_path() -> str:
+    return _build.LIB_PATH
+
+
+def load_library():
+    """Load libmla.so (building it first only if it does not exist)."""
+    global _LIB
+    if _LIB is None:
+        path = _build.ensure_built()
+        lib = ctypes.CDLL(path)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        shp = ctypes.POINTER(MlaShape)
+        lib.mla_pages_split_count.argtypes = [i32, i32]
+        lib.mla_pages_split_count.restype = i32
+        lib.mla_plan.argtypes = [shp, i32, i64, i32, i32, ctypes.POINTER(i32),
+                                 ctypes.POINTER(i32), ctypes.POINTER(sz)]
+        lib.mla_plan.restype = i32
+        lib.mla_workspace_size.argtypes = [shp, i32, i32]
+        lib.mla_workspace_size.restype = sz
+        lib.mla_decode.argtypes = [shp, vp, vp, vp, vp, ctypes.c_float, i32, ctypes.c_float, i32,
+                                   i32, vp, vp, vp, sz, vp]
+        lib.mla_decode.restype = i32
+        lib.mla_status_string.argtypes = [i32]
+        lib.mla_status_string.restype = ctypes.c_char_p
+        _LIB = lib
+    return _LIB
+
+
+def mla_status_string(status: int) -> str:
+    return load_library().mla_status_string(int(status)).decode()
+
+
+def _raise(status: int, what: str):
+    msg = f"{what}: {mla_status_string(status)}"
+    if status in (MLA_ERR_HEAD_SIZE, MLA_ERR_PAGE_SIZE):
+        raise ValueError(msg)
+    if status == MLA_ERR_DTYPE:
+        raise NotImplementedError(msg)
+    raise MlaError(status, msg)
+
+
+def make_shape(batch, num_heads, head_size, page_size, num_blocks, max_blocks_per_seq,
+               kv_dtype=MLA_BF16, o_dtype=MLA_BF16, q_dtype=MLA_BF16,
+               kv_lora_rank: Optional[int] = None) -> MlaShape:
+    return MlaShape(int(batch), int(num_heads), int(head_size),
+                    int(head_size - 64 if kv_lora_rank is None else kv_lora_rank),
+                    int(page_size), int(num_blocks), int(max_blocks_per_seq), int(q_dtype),
+                    int(kv_dtype), int(o_dtype))
+
+
+def mla_pages_split_count(max_seq_len: int, num_cus: int) -> int:
+    return int(load_library().mla_pages_split_count(int(max_seq_len), int(num_cus)))
+
+
+def mla_workspace_size(shape: MlaShape, split_mode: int, num_kv_splits: int) -> int:
+    return int(load_library().mla_workspace_size(ctypes.byref(shape), int(split_mode),
+                                                 int(num_kv_splits)))
+
+
+def mla_plan(shape: MlaShape, max_seq_len: int, total_seq_len: int = 0, num_cus: int = 256,
+             deterministic: bool = False) -> Tuple[int, int, int]:
+    """Returns (split_mode, num_kv_splits, workspace_bytes)."""
+    mode, splits, ws = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_size_t()
+    st = load_library().mla_plan(ctypes.byref(shape), int(max_seq_len), int(total_seq_len),
+                                 int(num_cus), 1 if deterministic else 0, ctypes.byref(mode),
+                                 ctypes.byref(splits), ctypes.byref(ws))
+    if st != MLA_OK:
+        _raise(st, "mla_plan")
+    return mode.value, splits.value, ws.value
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _kv_code(kv_cache, kv_dtype):
+    torch = _torch()
+    if kv_dtype is not None:
+        return {"bf16": MLA_BF16, "fp8_e4m3": MLA_FP8_E4M3}.get(kv_dtype, kv_dtype)
+    if kv_cache.dtype == torch.bfloat16:
+        return MLA_BF16
+    if kv_cache.dtype == torch.float8_e4m3fn:
+        return MLA_FP8_E4M3
+    return -1
+
+
+def _dtype_code(t):
+    torch = _torch()
+    return {torch.bfloat16: MLA_BF16, torch.float32: MLA_FP32,
+            torch.float8_e4m3fn: MLA_FP8_E4M3}.get(t, -1)
+
+
+def shape_of(q, kv_cache, block_table, *, kv_dtype=None, o_dtype=None) -> MlaShape:
+    torch = _torch()
+    if q.dim() != 3 or kv_cache.dim() != 3 or block_table.dim() != 2:
+        raise ValueError("expected q [B,H,D], kv_cache [num_blocks,page,D], block_table [B,W]")
+    B, H, D = q.shape
+    return make_shape(B, H, D, kv_cache.shape[1], kv_cache.shape[0], block_table.shape[1],
+                      kv_dtype=_kv_code(kv_cache, kv_dtype),
+                      o_dtype=_dtype_code(o_dtype or torch.bfloat16),
+                      q_dtype=_dtype_code(q.dtype))
+
+
+def mla_decode(q, kv_cache, block_table, seq_lens, scale: float, page_size: int,
+               k_scale: float = 1.0, num_kv_splits: Optional[int] = None, o=None, lse=None, *,
+               split_mode: Optional[int] = None, workspace=None, kv_dtype=None,
+               o_dtype=None, max_seq_len: Optional[int] = None,
+               total_seq_len: Optional[int] = None, num_cus: Optional[int] = None,
+               deterministic: bool = False, stream=None):
+    """Enqueue one MLA decode step on the current (or given) stream.
+
+    When ``num_kv_splits`` is None the split plan comes from ``mla_plan``
+    (which needs ``max_seq_len``; it is read from ``seq_lens`` when not
+    given).  When ``num_kv_splits`` is given without ``split_mode``, the
+    per-sequence split layout is used.  Missing ``o``/``lse``/``workspace``
+    are allocated with torch.  Returns (o, lse)."""
+    torch = _torch()
+    lib = load_library()
+    if not (q.is_cuda and kv_cache.is_cuda and block_table.is_cuda and seq_lens.is_cuda):
+        raise ValueError("mla_decode needs device tensors (HIP)")
+    for name, t in (("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
+                    ("seq_lens", seq_lens)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    if o is not None:
+        o_dtype = o.dtype
+    shape = shape_of(q, kv_cache, block_table, kv_dtype=kv_dtype, o_dtype=o_dtype)
+    B, H = shape.batch, shape.num_heads
+    if num_kv_splits is None:
+        if max_seq_len is None:
+            max_seq_len = int(seq_lens.max().item()) if B else 0
+            if total_seq_len is None:
+                total_seq_len = int(seq_lens.sum().item())
+        if num_cus is None:
+            num_cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        split_mode, num_kv_splits, _ = mla_plan(shape, max_seq_len, total_seq_len or 0,
+                                                num_cus, deterministic)
+    elif split_mode is None:
+        split_mode = SPLIT_PER_SEQUENCE
+    ws_need = mla_workspace_size(shape, split_mode, num_kv_splits)
+    if o is None:
+        o = torch.empty((B, H, shape.kv_lora_rank), dtype=o_dtype or torch.bfloat16,
+                        device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if (tuple(o.shape) != (B, H, shape.kv_lora_rank) or tuple(lse.shape) != (B, H)
+            or lse.dtype != torch.float32 or not o.is_contiguous() or not lse.is_contiguous()):
+        raise ValueError("o must be [B,H,kv_lora_rank] and lse [B,H] float32, contiguous")
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    st = lib.mla_decode(ctypes.byref(shape), q.data_ptr(), kv_cache.data_ptr(),
+                        block_table.data_ptr(), seq_lens.data_ptr(), float(scale),
+                        int(page_size), float(k_scale), int(num_kv_splits), int(split_mode),
+                        o.data_ptr(), lse.data_ptr(), ws_ptr, int(ws_bytes), stream)
+    if st != MLA_OK:
+        _raise(st, "mla_decode")
+    return o, lse

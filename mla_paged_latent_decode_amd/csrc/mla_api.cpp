@@ -1,0 +1,203 @@
+// Host side of libmla: argument checks, the split planner, workspace sizing
+// and the C ABI of include/mla.h.  Everything here is plain host C++; the only
+// GPU work is enqueued by mla::launch_decode (mla_kernels.hip).
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "mla.h"
+#include "mla_internal.h"
+
+namespace mla {
+
+static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+WorkspaceLayout workspace_layout(int32_t batch, int32_t heads, int32_t d_v, int32_t split_mode,
+                                 int32_t num_splits) {
+  WorkspaceLayout w;
+  if (batch < 1 || heads < 1 || d_v < 1 || num_splits < 1) return w;
+  if (split_mode == MLA_SPLIT_PER_SEQUENCE) {
+    if (num_splits == 1) return w;  // one segment per sequence: written directly
+    w.slots = (int64_t)batch * num_splits;
+  } else if (split_mode == MLA_SPLIT_BALANCED) {
+    // slot of (unit u, sequence b) is u + b: both grow along the tile stream,
+    // so u + b is distinct for every segment, and below U + B.
+    w.slots = (int64_t)num_splits + batch;
+  } else {
+    return w;
+  }
+  const int64_t o_bytes = w.slots * heads * (int64_t)d_v * 4;
+  const int64_t lse_off = align_up(o_bytes, 256);
+  const int64_t total = lse_off + align_up(w.slots * heads * 4, 256);
+  w.o_bytes = (size_t)o_bytes;
+  w.lse_offset = (size_t)lse_off;
+  w.total = (size_t)total;
+  return w;
+}
+
+HeadTiling head_tiling(int32_t heads) {
+  HeadTiling t;
+  t.heads_per_wave = heads % 32 == 0 ? 32 : 16;
+  const int groups = heads / t.heads_per_wave;
+  t.waves = groups % 4 == 0 ? 4 : (groups % 2 == 0 ? 2 : 1);
+  t.head_chunks = groups / t.waves;
+  return t;
+}
+
+// LDS bytes of one stage-1 workgroup (ring depth chosen in mla_kernels.hip).
+static int64_t stage1_lds_bytes(const mla_shape& s) {
+  const HeadTiling t = head_tiling(s.num_heads);
+  const int64_t tile = (int64_t)kTile * s.head_size * 2;
+  int nbuf = 4;
+  if (t.waves < 4 && s.head_size == 576) nbuf = 2;
+  return nbuf * tile;
+}
+
+}  // namespace mla
+
+using namespace mla;
+
+static mla_status check_shape(const mla_shape* s) {
+  if (!s) return MLA_ERR_NULL;
+  if (!((s->head_size == 576 && s->kv_lora_rank == 512) ||
+        (s->head_size == 320 && s->kv_lora_rank == 256)))
+    return MLA_ERR_HEAD_SIZE;
+  if (s->page_size <= 0 || s->page_size % 16 != 0) return MLA_ERR_PAGE_SIZE;
+  if (s->q_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (s->kv_dtype != MLA_BF16 && s->kv_dtype != MLA_FP8_E4M3) return MLA_ERR_DTYPE;
+  if (s->o_dtype != MLA_BF16 && s->o_dtype != MLA_FP32) return MLA_ERR_DTYPE;
+  if (s->batch < 1 || s->num_heads < 16 || s->num_heads % 16 != 0 || s->num_blocks < 1 ||
+      s->max_blocks_per_seq < 1)
+    return MLA_ERR_SHAPE;
+  // byte counts of the biggest buffers must fit comfortably in 64 bits
+  const double kv_bytes = (double)s->num_blocks * s->page_size * s->head_size * 2.0;
+  const double q_bytes = (double)s->batch * s->num_heads * s->head_size * 2.0;
+  const double bt = (double)s->batch * s->max_blocks_per_seq;
+  if (kv_bytes > 4.0e18 || q_bytes > 4.0e18 || bt > 2.0e9) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
+static bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+extern "C" {
+
+int32_t mla_pages_split_count(int32_t max_seq_len, int32_t num_cus) {
+  if (num_cus < 1) return 0;
+  int64_t s = ((int64_t)max_seq_len + 511) / 512;
+  if (s < 1) s = 1;
+  if (s > 2 * (int64_t)num_cus) s = 2 * (int64_t)num_cus;
+  return (int32_t)s;
+}
+
+size_t mla_workspace_size(const mla_shape* shape, int32_t split_mode, int32_t num_kv_splits) {
+  if (check_shape(shape) != MLA_OK) return 0;
+  if (num_kv_splits < 1 || num_kv_splits > MLA_MAX_KV_SPLITS) return 0;
+  return workspace_layout(shape->batch, shape->num_heads, shape->kv_lora_rank, split_mode,
+                          num_kv_splits)
+      .total;
+}
+
+mla_status mla_plan(const mla_shape* shape, int32_t max_seq_len, int64_t total_seq_len,
+                    int32_t num_cus, int32_t deterministic, int32_t* split_mode,
+                    int32_t* num_kv_splits, size_t* workspace_bytes) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!split_mode || !num_kv_splits || !workspace_bytes) return MLA_ERR_NULL;
+  if (num_cus < 1 || max_seq_len < 0) return MLA_ERR_ARGUMENT;
+  if (deterministic) {
+    *split_mode = MLA_SPLIT_PER_SEQUENCE;
+    *num_kv_splits = 1;
+    *workspace_bytes = 0;
+    return MLA_OK;
+  }
+  const HeadTiling ht = head_tiling(shape->num_heads);
+  int64_t per_cu = (160 * 1024) / stage1_lds_bytes(*shape);
+  if (per_cu < 1) per_cu = 1;
+  if (per_cu > 4) per_cu = 4;
+  // one workgroup per resident slot, each head chunk counting as its own
+  int64_t units = num_cus * per_cu / ht.head_chunks;
+  if (units < 1) units = 1;
+  // keep at least 4 tiles (128 positions) per unit
+  int64_t total = total_seq_len > 0 ? total_seq_len : (int64_t)shape->batch * max_seq_len;
+  const int64_t tiles = total / kTile + shape->batch;
+  const int64_t cap = (tiles + 3) / 4;
+  if (units > cap) units = cap;
+  if (units < 1) units = 1;
+  if (units > MLA_MAX_KV_SPLITS) units = MLA_MAX_KV_SPLITS;
+  *split_mode = MLA_SPLIT_BALANCED;
+  *num_kv_splits = (int32_t)units;
+  *workspace_bytes = mla_workspace_size(shape, MLA_SPLIT_BALANCED, (int32_t)units);
+  return MLA_OK;
+}
+
+mla_status mla_decode(const mla_shape* shape, const void* q, const void* kv_cache,
+                      const int32_t* block_table, const int32_t* seq_lens, float scale,
+                      int32_t page_size, float k_scale, int32_t num_kv_splits,
+                      int32_t split_mode, void* o, float* lse, void* workspace,
+                      size_t workspace_bytes, void* hip_stream) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!q || !kv_cache || !block_table || !seq_lens || !o || !lse) return MLA_ERR_NULL;
+  if (page_size != shape->page_size) return MLA_ERR_PAGE_SIZE;
+  if (split_mode != MLA_SPLIT_PER_SEQUENCE && split_mode != MLA_SPLIT_BALANCED)
+    return MLA_ERR_SPLITS;
+  if (num_kv_splits < 1 || num_kv_splits > MLA_MAX_KV_SPLITS) return MLA_ERR_SPLITS;
+  if (split_mode == MLA_SPLIT_PER_SEQUENCE &&
+      (int64_t)shape->batch * num_kv_splits > (int64_t)1 << 27)
+    return MLA_ERR_SPLITS;
+  if (!(isfinite(scale) && scale > 0.f)) return MLA_ERR_ARGUMENT;
+  const bool fp8 = shape->kv_dtype == MLA_FP8_E4M3;
+  if (fp8 && !(isfinite(k_scale) && k_scale > 0.f)) return MLA_ERR_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4))
+    return MLA_ERR_ARGUMENT;
+  const WorkspaceLayout wl = workspace_layout(shape->batch, shape->num_heads,
+                                              shape->kv_lora_rank, split_mode, num_kv_splits);
+  if (wl.total > 0) {
+    if (!workspace || workspace_bytes < wl.total) return MLA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MLA_ERR_ARGUMENT;
+  }
+  if (fp8) return MLA_ERR_DTYPE;  // fp8 cache kernels are not part of this build yet
+
+  DecodeArgs a;
+  a.q = q;
+  a.kv = kv_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.o = o;
+  a.lse = lse;
+  a.ws_o = wl.total ? reinterpret_cast<float*>(workspace) : nullptr;
+  a.ws_lse = wl.total ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + wl.lse_offset)
+                      : nullptr;
+  a.batch = shape->batch;
+  a.heads = shape->num_heads;
+  a.head_size = shape->head_size;
+  a.d_v = shape->kv_lora_rank;
+  a.page_size = shape->page_size;
+  a.bt_stride = shape->max_blocks_per_seq;
+  a.kv_fp8 = fp8 ? 1 : 0;
+  a.o_f32 = shape->o_dtype == MLA_FP32 ? 1 : 0;
+  a.split_mode = split_mode;
+  a.num_splits = num_kv_splits;
+  a.scale = scale;
+  a.k_scale = k_scale;
+  return launch_decode(a, hip_stream) == 0 ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+const char* mla_status_string(int32_t status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
+    case MLA_ERR_HEAD_SIZE: return "MLA_ERR_HEAD_SIZE: head_size must be 576 or 320 with kv_lora_rank = head_size - 64";
+    case MLA_ERR_PAGE_SIZE: return "MLA_ERR_PAGE_SIZE: page_size must be a positive multiple of 16 and match the shape";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: q must be bf16, kv bf16 or fp8 e4m3fn, o bf16 or fp32";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: batch, heads (multiple of 16), num_blocks or table width out of range";
+    case MLA_ERR_SPLITS: return "MLA_ERR_SPLITS: num_kv_splits or split_mode out of range";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
+    case MLA_ERR_LAUNCH: return "MLA_ERR_LAUNCH: HIP kernel launch failed";
+    case MLA_ERR_ARGUMENT: return "MLA_ERR_ARGUMENT: non-finite/non-positive scale or k_scale, num_cus < 1, or a misaligned pointer";
+    default: return "unknown mla_status";
+  }
+}
+
+}  // extern "C"

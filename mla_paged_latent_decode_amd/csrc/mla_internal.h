@@ -1,0 +1,61 @@
+// Internal interface between the host ABI (mla_api.cpp) and the HIP kernels
+// (mla_kernels.hip).  Not installed; the public surface is include/mla.h.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kTile = 32;  // context positions per stage-1 tile
+
+// Workspace layout (both split modes): `slots` partial results, each
+//   ws_o   [slots][H][D_v]  float32, the segment's normalised output
+//   ws_lse [slots][H]       float32, the segment's natural-log lse
+// ws_lse starts at the first 256-byte boundary after ws_o.
+struct WorkspaceLayout {
+  int64_t slots = 0;
+  size_t o_bytes = 0;
+  size_t lse_offset = 0;
+  size_t total = 0;
+};
+
+WorkspaceLayout workspace_layout(int32_t batch, int32_t heads, int32_t d_v, int32_t split_mode,
+                                 int32_t num_splits);
+
+// How the heads of one sequence are spread over waves and workgroups.
+struct HeadTiling {
+  int heads_per_wave;   // 32 (32x32 MFMA tiles) or 16 (16x16 tiles)
+  int waves;            // waves per workgroup, each owning heads_per_wave heads
+  int head_chunks;      // workgroups per work unit along the head axis
+};
+
+HeadTiling head_tiling(int32_t heads);
+
+struct DecodeArgs {
+  const void* q;
+  const void* kv;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* o;
+  float* lse;
+  float* ws_o;
+  float* ws_lse;
+  int32_t batch;
+  int32_t heads;
+  int32_t head_size;
+  int32_t d_v;
+  int32_t page_size;
+  int32_t bt_stride;
+  int32_t kv_fp8;
+  int32_t o_f32;
+  int32_t split_mode;
+  int32_t num_splits;
+  float scale;
+  float k_scale;
+};
+
+// Enqueues stage 1 (and stage 2 when needed).  Returns 0 or a HIP error code.
+int launch_decode(const DecodeArgs& a, void* stream);
+
+}  // namespace mla

@@ -1,0 +1,773 @@
+// HIP kernels of libmla for gfx950 (MI355X): MLA paged latent decode.
+//
+// Stage 1 (split-KV attention over one segment of one sequence).
+//   One workgroup owns one work unit (a run of 32-position tiles of one or two
+//   sequences) and one chunk of heads; each wave owns 16 or 32 heads.  Per
+//   tile, the wave computes S^T[token, head] = K Q^T on bf16 MFMA (all heads
+//   share the one latent row stream, multi-query attention; "Triton と MLA"
+//   page, データフロー), updates the online softmax state (running max m,
+//   running sum l, rescaled accumulator; "vLLM 中 Attention Kernel 如何并行处理
+//   多个请求", section 七), and accumulates O^T[v, head] += V^T P^T on MFMA,
+//   where V is the leading D_v columns of the same tile.  Pages are reached
+//   through the block table (same article, section 十一).
+//
+//   Tiles stream HBM -> LDS with 16-byte global_load_lds (no register
+//   staging) into a ring of NBUF tiles, NBUF-1 tiles ahead of the compute.
+//   The LDS tile is stored as 1 KB blocks, each the exact operand footprint of
+//   one MFMA k-step, with an XOR swizzle so that both the QK^T read
+//   (ds_read_b128) and the transposed V read (ds_read_b64_tr_b16) hit
+//   distinct banks.
+//
+// Stage 2 (merge).  Partials (o_s, lse_s) of a sequence are combined with the
+//   log-sum-exp rule of the same article, section 十二:
+//   lse = M + ln sum_s e^(lse_s - M),  o = sum_s e^(lse_s - lse) o_s.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Lazy rescale: the running max used for the exponentials is only moved when
+// a tile's max exceeds it by more than kTau (log2 units), so p <= 2^kTau.
+// The final result does not depend on this choice; it only saves rescales.
+constexpr float kTau = 8.0f;
+
+// 4 KB of zeros in device memory: tail positions of a segment's last tile
+// load from here, so the LDS rows of positions past the sequence are zero and
+// never carry the (possibly NaN) contents of unreferenced cache slots.
+__device__ __attribute__((aligned(256))) const uint32_t g_zero_rows[1024] = {0};
+
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt is a 6-bit counter");
+  // simm16: vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8] (0), vmcnt[5:4] at [15:14]
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ float wave_max_xor(float x, int mask) {
+  return fmaxf(x, __shfl_xor(x, mask, 64));
+}
+
+// v_permlane32_swap with both operands x returns {x, partner} in some order
+// in every lane (partner = lane ^ 32), so max/sum of the pair is symmetric.
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Multiply an MFMA accumulator held in AGPRs by s in place.  The "+a"
+// constraints keep the accumulator in the AGPR file, so this (rare) rescale
+// costs no VGPRs beyond one temporary.
+__device__ __forceinline__ void scale_acc4(float& x0, float& x1, float& x2, float& x3, float s) {
+  float t;
+  asm volatile(
+      "v_accvgpr_read_b32 %4, %0\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %0, %4\n\t"
+      "v_accvgpr_read_b32 %4, %1\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %1, %4\n\t"
+      "v_accvgpr_read_b32 %4, %2\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %2, %4\n\t"
+      "v_accvgpr_read_b32 %4, %3\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %3, %4"
+      : "+a"(x0), "+a"(x1), "+a"(x2), "+a"(x3), "=&v"(t)
+      : "v"(s));
+}
+
+template <int N>
+__device__ __forceinline__ void scale_acc(float __attribute__((ext_vector_type(N))) & a, float s) {
+#pragma unroll
+  for (int i = 0; i < N; i += 4) {
+    float x0 = a[i], x1 = a[i + 1], x2 = a[i + 2], x3 = a[i + 3];
+    scale_acc4(x0, x1, x2, x3, s);
+    a[i] = x0;
+    a[i + 1] = x1;
+    a[i + 2] = x2;
+    a[i + 3] = x3;
+  }
+}
+
+__device__ __forceinline__ void store_out4(void* o, int o_f32, size_t idx, f32x4 v) {
+  if (o_f32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + idx) = v;
+  } else {
+    bf16x4 b = __builtin_convertvector(v, bf16x4);
+    *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(o) + idx) = b;
+  }
+}
+
+struct Stage1Params {
+  const __bf16* q;
+  const uint8_t* kv;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* o;
+  float* lse;
+  float* ws_o;
+  float* ws_lse;
+  int32_t batch, heads, page_size, bt_stride;
+  int32_t o_f32, split_mode, num_splits, head_chunks;
+  float score_log2;  // scale * log2(e) (* k_scale for fp8 caches)
+  float out_scale;   // 1, or k_scale for fp8 caches
+};
+
+// ---------------------------------------------------------------- work units
+
+// Split of sequence b in per-sequence mode: C_b = roundup(ceil(n / S), 32).
+__device__ __forceinline__ int per_seq_chunk(int n, int S) {
+  int c = (n + S - 1) / S;
+  return (c + kTile - 1) / kTile * kTile;
+}
+
+// Unit that holds global tile x when TT tiles are cut into U runs
+// [floor(u*TT/U), floor((u+1)*TT/U)).
+__device__ __forceinline__ int unit_of_tile(int64_t x, int64_t TT, int U) {
+  return (int)(((x + 1) * (int64_t)U - 1) / TT);
+}
+
+__device__ __forceinline__ int tiles_of(int n) { return (n + kTile - 1) / kTile; }
+
+// Inclusive wave prefix sum.
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int64_t total_tiles(const int32_t* seq_lens, int B, int lane) {
+  int64_t tot = 0;
+  for (int c0 = 0; c0 < B; c0 += 64) {
+    int b = c0 + lane;
+    int nt = b < B ? tiles_of(seq_lens[b]) : 0;
+    int s = wave_incl_scan(nt, lane);
+    tot += __shfl(s, 63, 64);
+  }
+  return tot;
+}
+
+// ---------------------------------------------------------------- stage 1
+
+template <int HPW, int W, int D, int DV, int NBUF>
+struct Cfg {
+  static constexpr int NKS = HPW == 32 ? D / 16 : D / 32;          // QK k-steps
+  static constexpr int NBLK = kTile * D * 2 / 1024;                  // 1 KB blocks per tile
+  static constexpr int LPW = NBLK / W;                               // DMA ops per wave per tile
+  static constexpr int TILE_BYTES = NBLK * 1024;
+  static constexpr int NVB = HPW == 32 ? DV / 32 : DV / 16;         // PV output blocks
+  static constexpr int HEADS_PER_WG = HPW * W;
+  static_assert(NBLK % W == 0, "each wave issues the same number of tile loads");
+  static_assert((NBUF - 1) * LPW <= 63, "outstanding loads must fit the vmcnt counter");
+  static_assert(HPW == 32 ? (D % 16 == 0 && DV % 32 == 0) : (D % 32 == 0 && DV % 16 == 0), "");
+  static_assert(HPW == 32 ? NBLK == NKS : NBLK == 2 * NKS, "tile block count");
+};
+
+template <int HPW, int W, int D, int DV, int NBUF>
+__global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
+  using C = Cfg<HPW, W, D, DV, NBUF>;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * C::TILE_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+
+  // XCD-aware decode of the workgroup id: consecutive ids go to different
+  // XCDs, so the head chunks of one unit share an XCD (and its L2).
+  const int id = blockIdx.x;
+  const int hc = (id >> 3) % p.head_chunks;
+  const int unit = ((id >> 3) / p.head_chunks) * 8 + (id & 7);
+  const int num_units = p.split_mode == 0 ? p.batch * p.num_splits : p.num_splits;
+  if (unit >= num_units) return;
+
+  const int h0 = hc * C::HEADS_PER_WG + wave * HPW;  // first head of this wave
+  const int H = p.heads;
+
+  // ---------------- per-lane constants of the LDS layout
+  // HPW == 32: block ks holds chunks (t, 2ks + h2) of the 32 tokens; logical
+  //   position t + 32*h2, stored at pos ^ (h2 << 2) ^ ((ks & 1) << 3).
+  // HPW == 16: block th*NKS + ks holds chunks (16th + t16, 4ks + c4); logical
+  //   position t16 + 16*c4, stored at pos ^ ((c4 & 1) << 3).
+  int qk_off_e, qk_off_o;  // LDS byte offset of this lane's K chunk (even / odd block)
+  int v_off0, v_off1;      // LDS byte offsets of this lane's V^T reads
+  int ld_tok_e, ld_tok_o, ld_chunk;  // what this lane loads (token for even/odd block, chunk byte)
+  if constexpr (HPW == 32) {
+    const int h2 = lane >> 5;
+    const int pe = lane ^ (h2 << 2);
+    const int po = pe ^ 8;
+    qk_off_e = pe * 16;
+    qk_off_o = po * 16;
+    ld_tok_e = pe & 31;
+    ld_tok_o = po & 31;
+    ld_chunk = h2 * 16;
+    const int g = lane >> 4, i = lane & 15, half = lane >> 5;
+    const int vh2 = (i >> 1) & 1;
+    const int t0 = 4 * half + (i >> 2);
+    const int base = ((t0 ^ (vh2 << 2)) + 32 * vh2) * 16 + 8 * (i & 1) + (g & 1) * 1024;
+    v_off0 = base + 8 * ((g & 1)) * 16;
+    v_off1 = base + 8 * ((g & 1) ^ 1) * 16;
+  } else {
+    const int pp = lane ^ (((lane >> 4) & 1) << 3);
+    qk_off_e = qk_off_o = pp * 16;
+    ld_tok_e = pp & 15;   // + 16 * th
+    ld_tok_o = pp & 15;
+    ld_chunk = (pp >> 4) * 16;
+    const int g = lane >> 4, i = lane & 15;
+    const int vc = (i >> 1) & 1;
+    const int t16 = 4 * g + (i >> 2);
+    v_off0 = ((t16 ^ (vc << 3)) + 16 * vc) * 16 + 8 * (i & 1);
+    v_off1 = v_off0;  // th = 1 adds NKS blocks
+  }
+
+  const uint8_t* zero_row = reinterpret_cast<const uint8_t*>(g_zero_rows);
+  const int64_t row_bytes = (int64_t)D * 2;
+  const int P = p.page_size;
+
+  // ---------------- one segment [ts, te) of sequence b
+  auto process = [&](int b, int ts, int te, bool final_out, int slot) __attribute__((always_inline)) {
+    const int n_tiles = (te - ts + kTile - 1) / kTile;
+    const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
+
+    // issue the DMA loads of tile i into ring slot i % NBUF
+    auto issue = [&](int i) __attribute__((always_inline)) {
+      const int tok0 = ts + i * kTile;
+      const int nvalid = min(kTile, te - tok0);
+      const int lb0 = tok0 / P;
+      const int off0 = tok0 - lb0 * P;
+      const int lb1 = (off0 + nvalid > P) ? lb0 + 1 : lb0;
+      const int64_t pg0 = bt[lb0];
+      const int64_t pg1 = bt[lb1];
+      uint8_t* dst = ring + (i % NBUF) * C::TILE_BYTES;
+      auto row_ptr = [&](int t) __attribute__((always_inline)) -> const uint8_t* {
+        if (t >= nvalid) return zero_row;
+        const int x = off0 + t;
+        const int64_t page = x < P ? pg0 : pg1;
+        const int r = x < P ? x : x - P;
+        return p.kv + (page * P + r) * row_bytes + ld_chunk;
+      };
+      if constexpr (HPW == 32) {
+        const uint8_t* src_e = row_ptr(ld_tok_e);
+        const uint8_t* src_o = row_ptr(ld_tok_o);
+#pragma unroll
+        for (int k = 0; k < C::LPW; ++k) {
+          const int j = wave + k * W;  // block index
+          const uint8_t* src = (j & 1) ? src_o : src_e;
+          __builtin_amdgcn_global_load_lds(src + j * 32, (LDS_AS void*)(dst + j * 1024), 16, 0, 0);
+        }
+      } else {
+        const uint8_t* src0 = row_ptr(ld_tok_e);
+        const uint8_t* src1 = row_ptr(ld_tok_e + 16);
+#pragma unroll
+        for (int k = 0; k < C::LPW; ++k) {
+          const int j = wave + k * W;
+          const int th = j / C::NKS, ks = j % C::NKS;
+          const uint8_t* src = th ? src1 : src0;
+          __builtin_amdgcn_global_load_lds(src + ks * 64, (LDS_AS void*)(dst + j * 1024), 16, 0, 0);
+        }
+      }
+    };
+
+    // Q fragments of this wave's heads (B operand of S^T = K Q^T)
+    bf16x8 qf[C::NKS];
+    {
+      const __bf16* qb = p.q + ((int64_t)b * H + h0) * D;
+      if constexpr (HPW == 32) {
+        const __bf16* qr = qb + (int64_t)(lane & 31) * D + 8 * (lane >> 5);
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qr + 16 * ks);
+      } else {
+        const __bf16* qr = qb + (int64_t)(lane & 15) * D + 8 * (lane >> 4);
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qr + 32 * ks);
+      }
+    }
+
+    float m_run = -INFINITY;  // running max (log2 units) used for the exponentials
+    float l_part = 0.f;       // this lane's share of sum_t p_t (fp32 weights): for lse
+    float lr_part = 0.f;      // the same over the bf16-rounded weights: normalises o
+    typedef typename std::conditional<HPW == 32, f32x16, f32x4>::type acc_t;
+    acc_t oacc[C::NVB];
+#pragma unroll
+    for (int vb = 0; vb < C::NVB; ++vb) oacc[vb] = acc_t{};
+
+    __builtin_amdgcn_s_barrier();  // every wave is done with the ring of a previous segment
+    const int pre = min(NBUF - 1, n_tiles);
+    for (int i = 0; i < pre; ++i) issue(i);
+
+    for (int i = 0; i < n_tiles; ++i) {
+      const int ahead = min(NBUF - 2, n_tiles - 1 - i);
+      if (ahead >= 2) wait_vmcnt<(NBUF >= 4 ? 2 : 0) * C::LPW>();
+      else if (ahead == 1) wait_vmcnt<(NBUF >= 3 ? 1 : 0) * C::LPW>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (i + NBUF - 1 < n_tiles) issue(i + NBUF - 1);
+
+      const uint8_t* tile = ring + (i % NBUF) * C::TILE_BYTES;
+      const int nvalid = min(kTile, te - (ts + i * kTile));
+
+      if constexpr (HPW == 32) {
+        // ---- S^T[32 tokens, 32 heads] over D
+        f32x16 s = {};
+        {
+          auto kread = [&](int ks) __attribute__((always_inline)) {
+            return *reinterpret_cast<const LDS_AS bf16x8*>(
+                (const LDS_AS uint8_t*)tile + ks * 1024 + ((ks & 1) ? qk_off_o : qk_off_e));
+          };
+          // software pipeline: the K chunk of step ks+2 is in flight while
+          // step ks runs on the matrix core
+          bf16x8 k0 = kread(0), k1 = kread(1);
+#pragma unroll
+          for (int ks = 0; ks < C::NKS; ++ks) {
+            bf16x8 k2 = k1;
+            if (ks + 2 < C::NKS) k2 = kread(ks + 2);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            k0 = k1;
+            k1 = k2;
+          }
+        }
+        // token of s[r] is 8*(r/4) + 4*(lane/32) + r%4; mask positions past the segment
+        if (nvalid < kTile) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int t = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (t >= nvalid) s[r] = -INFINITY;
+          }
+        }
+        float mt = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+        mt = max_halves(mt) * p.score_log2;
+        const float m_new = fmaxf(m_run, mt);
+        if (i == 0) {
+          m_run = m_new;  // nothing accumulated yet: no rescale
+        } else if (__builtin_amdgcn_ballot_w64(m_new > m_run + kTau)) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_part *= alpha;
+          lr_part *= alpha;
+#pragma unroll
+          for (int vb = 0; vb < C::NVB; ++vb) scale_acc(oacc[vb], alpha);
+        }
+        f32x16 pr;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.score_log2, -m_run));
+        {
+          const f32x8 a = (f32x8){pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]} +
+                          (f32x8){pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]};
+          l_part += ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+        }
+        const bf16x8 p0 = __builtin_convertvector(
+            (f32x8){pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]}, bf16x8);
+        const bf16x8 p1 = __builtin_convertvector(
+            (f32x8){pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]}, bf16x8);
+        // the running sum adds the bf16 weights the MFMA uses, so that o stays
+        // an exact convex combination of V rows with those weights
+        {
+          const f32x8 r0 = __builtin_convertvector(p0, f32x8);
+          const f32x8 r1 = __builtin_convertvector(p1, f32x8);
+          const f32x8 r01 = r0 + r1;
+          lr_part += ((r01[0] + r01[1]) + (r01[2] + r01[3])) + ((r01[4] + r01[5]) + (r01[6] + r01[7]));
+        }
+        // ---- O^T[v, head] += V^T P^T, V = leading DV columns of the tile
+        {
+          auto vread = [&](int st) __attribute__((always_inline)) {
+            const int vb = st >> 1, kk = st & 1;
+            const LDS_AS uint8_t* vt = (const LDS_AS uint8_t*)tile + vb * 2048 + kk * 256;
+            const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (LDS_AS bf16x4*)(vt + v_off0));
+            const bf16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (LDS_AS bf16x4*)(vt + v_off1));
+            return bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          };
+          constexpr int NST = 2 * C::NVB;
+          bf16x8 a0 = vread(0), a1 = vread(1);
+#pragma unroll
+          for (int st = 0; st < NST; ++st) {
+            bf16x8 a2 = a1;
+            if (st + 2 < NST) a2 = vread(st + 2);
+            oacc[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, (st & 1) ? p1 : p0,
+                                                                  oacc[st >> 1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            a0 = a1;
+            a1 = a2;
+          }
+        }
+      } else {
+        // ---- S^T over two 16-token halves x 16 heads
+        f32x4 s0 = {}, s1 = {};
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+          const bf16x8 k0 = *reinterpret_cast<const LDS_AS bf16x8*>(
+              (const LDS_AS uint8_t*)tile + ks * 1024 + qk_off_e);
+          const bf16x8 k1 = *reinterpret_cast<const LDS_AS bf16x8*>(
+              (const LDS_AS uint8_t*)tile + (C::NKS + ks) * 1024 + qk_off_e);
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks], s1, 0, 0, 0);
+        }
+        // token of s_th[r] is 16*th + 4*(lane/16) + r
+        if (nvalid < kTile) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 4 * (lane >> 4) + r;
+            if (t >= nvalid) s0[r] = -INFINITY;
+            if (t + 16 >= nvalid) s1[r] = -INFINITY;
+          }
+        }
+        float mt = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                         fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+        mt = wave_max_xor(mt, 16);
+        mt = max_halves(mt) * p.score_log2;
+        const float m_new = fmaxf(m_run, mt);
+        if (i == 0) {
+          m_run = m_new;  // nothing accumulated yet: no rescale
+        } else if (__builtin_amdgcn_ballot_w64(m_new > m_run + kTau)) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_part *= alpha;
+          lr_part *= alpha;
+#pragma unroll
+          for (int vb = 0; vb < C::NVB; ++vb) scale_acc(oacc[vb], alpha);
+        }
+        f32x8 pr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], p.score_log2, -m_run));
+          pr[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.score_log2, -m_run));
+        }
+        const bf16x8 pb = __builtin_convertvector(pr, bf16x8);
+        l_part += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+        {
+          const f32x8 r = __builtin_convertvector(pb, f32x8);
+          lr_part += ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
+        }
+#pragma unroll
+        for (int vb = 0; vb < C::NVB; ++vb) {
+          const LDS_AS uint8_t* vt =
+              (const LDS_AS uint8_t*)tile + (vb >> 1) * 1024 + (vb & 1) * 512;
+          const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vt + v_off0));
+          const bf16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (LDS_AS bf16x4*)(vt + C::NKS * 1024 + v_off1));
+          const bf16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          oacc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, oacc[vb], 0, 0, 0);
+        }
+      }
+    }
+
+    // ---- epilogue: o = O / l, lse = ln(2) * (m + log2 l)
+    float l_tot, lr_tot;
+    if constexpr (HPW == 32) {
+      l_tot = sum_halves(l_part);
+      lr_tot = sum_halves(lr_part);
+    } else {
+      l_tot = sum_halves(l_part + __shfl_xor(l_part, 16, 64));
+      lr_tot = sum_halves(lr_part + __shfl_xor(lr_part, 16, 64));
+    }
+    const float inv = p.out_scale / lr_tot;
+    const float lse_v = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    const int hl = HPW == 32 ? (lane & 31) : (lane & 15);
+    const int h = h0 + hl;
+    const bool lse_writer = HPW == 32 ? (lane < 32) : (lane < 16);
+    if (final_out) {
+      const size_t obase = ((size_t)b * H + h) * DV;
+#pragma unroll
+      for (int vb = 0; vb < C::NVB; ++vb) {
+        if constexpr (HPW == 32) {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int v = 32 * vb + 8 * g4 + 4 * (lane >> 5);
+            f32x4 val = {oacc[vb][4 * g4] * inv, oacc[vb][4 * g4 + 1] * inv,
+                         oacc[vb][4 * g4 + 2] * inv, oacc[vb][4 * g4 + 3] * inv};
+            store_out4(p.o, p.o_f32, obase + v, val);
+          }
+        } else {
+          const int v = 16 * vb + 4 * (lane >> 4);
+          f32x4 val = oacc[vb] * inv;
+          store_out4(p.o, p.o_f32, obase + v, val);
+        }
+      }
+      if (lse_writer) p.lse[(size_t)b * H + h] = lse_v;
+    } else {
+      float* wo = p.ws_o + ((size_t)slot * H + h) * DV;
+#pragma unroll
+      for (int vb = 0; vb < C::NVB; ++vb) {
+        if constexpr (HPW == 32) {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int v = 32 * vb + 8 * g4 + 4 * (lane >> 5);
+            f32x4 val = {oacc[vb][4 * g4] * inv, oacc[vb][4 * g4 + 1] * inv,
+                         oacc[vb][4 * g4 + 2] * inv, oacc[vb][4 * g4 + 3] * inv};
+            *reinterpret_cast<f32x4*>(wo + v) = val;
+          }
+        } else {
+          const int v = 16 * vb + 4 * (lane >> 4);
+          *reinterpret_cast<f32x4*>(wo + v) = oacc[vb] * inv;
+        }
+      }
+      if (lse_writer) p.ws_lse[(size_t)slot * H + h] = lse_v;
+    }
+  };
+
+  // ---------------- enumerate this unit's segments (one call site of process)
+  int b, ts, te, slot;
+  bool fin;
+  if (p.split_mode == 0) {
+    const int S = p.num_splits;
+    b = unit / S;
+    const int s = unit % S;
+    const int n = p.seq_lens[b];
+    if (n <= 0) {
+      if (s == 0) {  // empty sequence: o = 0, lse = -inf
+        const int hl = HPW == 32 ? (lane & 31) : (lane & 15);
+        const int h = h0 + hl;
+        const size_t obase = ((size_t)b * H + h) * DV;
+        constexpr int per_lane = DV * HPW / 64;
+        const int part = HPW == 32 ? (lane >> 5) : (lane >> 4);
+        for (int k = 0; k < per_lane; k += 4)
+          store_out4(p.o, p.o_f32, obase + part * per_lane + k, f32x4{0.f, 0.f, 0.f, 0.f});
+        if (HPW == 32 ? lane < 32 : lane < 16) p.lse[(size_t)b * H + h] = -INFINITY;
+      }
+      return;
+    }
+    const int Cb = per_seq_chunk(n, S);
+    ts = s * Cb;
+    if (ts >= n) return;
+    te = min(ts + Cb, n);
+    fin = (n + Cb - 1) / Cb == 1;
+    slot = b * S + s;
+    process(b, ts, te, fin, slot);
+    return;
+  }
+
+  // balanced: the unit covers global tiles [a0, a1) of the batch's tile stream
+  const int U = p.num_splits;
+  const int64_t TT = total_tiles(p.seq_lens, p.batch, lane);
+  if (TT == 0) return;
+  const int64_t a0 = (int64_t)unit * TT / U;
+  const int64_t a1 = (int64_t)(unit + 1) * TT / U;
+  if (a0 >= a1) return;
+  // first sequence whose tiles reach past a0, and its first global tile
+  int64_t st = 0;
+  b = 0;
+  for (int c0 = 0; c0 < p.batch; c0 += 64) {
+    const int bl = c0 + lane;
+    const int ntl = bl < p.batch ? tiles_of(p.seq_lens[bl]) : 0;
+    const int incl = wave_incl_scan(ntl, lane);
+    const uint64_t past = __builtin_amdgcn_ballot_w64(bl < p.batch && st + incl > a0);
+    if (past) {
+      const int k = __builtin_ctzll(past);
+      b = c0 + k;
+      st += __shfl(incl - ntl, k, 64);
+      break;
+    }
+    st += __shfl(incl, 63, 64);
+  }
+  b = uniform(b);
+  for (;;) {
+    const int n = p.seq_lens[b];
+    const int nt = tiles_of(n);
+    const int64_t lo = (a0 > st ? a0 : st) - st;
+    const int64_t hi = (a1 < st + nt ? a1 : st + nt) - st;
+    if (hi > lo) process(b, (int)lo * kTile, min((int)hi * kTile, n), lo == 0 && hi == nt, unit + b);
+    st += nt;
+    ++b;
+    if (b >= p.batch || st >= a1) break;
+  }
+}
+
+// ---------------------------------------------------------------- stage 2
+
+struct Stage2Params {
+  const int32_t* seq_lens;
+  const float* ws_o;
+  const float* ws_lse;
+  void* o;
+  float* lse;
+  int32_t batch, heads, o_f32, split_mode, num_splits, head_groups;
+};
+
+// One workgroup per (sequence, 16 heads); 16 threads per head, 4 floats each
+// per step.
+template <int DV>
+__global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
+  const int b = blockIdx.x / p.head_groups;
+  const int hg = blockIdx.x % p.head_groups;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int H = p.heads;
+  const int h = hg * 16 + (t >> 4);
+  const int j = t & 15;
+  const int n = p.seq_lens[b];
+
+  int first, count, unit0 = 0, units = 1;
+  int64_t tiles_total = 1;
+  if (p.split_mode == 0) {
+    const int S = p.num_splits;
+    if (n <= 0) return;  // stage 1 wrote o = 0, lse = -inf
+    const int Cb = per_seq_chunk(n, S);
+    const int nseg = (n + Cb - 1) / Cb;
+    if (nseg <= 1) return;  // stage 1 wrote the final result
+    first = b * S;
+    count = nseg;
+  } else {
+    const int U = p.num_splits;
+    // tiles before sequence b, and in total
+    int64_t before = 0, TT = 0;
+    for (int c0 = 0; c0 < p.batch; c0 += 64) {
+      const int bl = c0 + lane;
+      const int nt = bl < p.batch ? tiles_of(p.seq_lens[bl]) : 0;
+      const int incl = wave_incl_scan(nt, lane);
+      const int tot = __shfl(incl, 63, 64);
+      if (b >= c0 + 64) before += tot;
+      else if (b >= c0) before += __shfl(incl - nt, b - c0, 64);
+      TT += tot;
+    }
+    const int nt = tiles_of(n);
+    if (nt == 0) {
+      if (h < H) {
+        for (int v = 4 * j; v < DV; v += 64)
+          store_out4(p.o, p.o_f32, ((size_t)b * H + h) * DV + v, f32x4{0.f, 0.f, 0.f, 0.f});
+        if (j == 0) p.lse[(size_t)b * H + h] = -INFINITY;
+      }
+      return;
+    }
+    const int uf = unit_of_tile(before, TT, U);
+    const int ul = unit_of_tile(before + nt - 1, TT, U);
+    if (uf == ul) return;  // stage 1 wrote the final result
+    first = uf + b;
+    count = ul - uf + 1;
+    // with more units than tiles some units in [uf, ul] own no tile and wrote
+    // no partial; they are skipped below
+    tiles_total = TT;
+    units = U;
+    unit0 = uf;
+  }
+  if (h >= H) return;
+  auto live = [&](int k) {
+    if (p.split_mode == 0) return true;
+    const int64_t u = unit0 + k;
+    return (u + 1) * tiles_total / units > u * tiles_total / units;
+  };
+
+  float M = -INFINITY;
+  for (int k = 0; k < count; ++k)
+    if (live(k)) M = fmaxf(M, p.ws_lse[(size_t)(first + k) * H + h]);
+  float tot = 0.f;
+  f32x4 acc[DV / 64];
+#pragma unroll
+  for (int c = 0; c < DV / 64; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < count; ++k) {
+    if (!live(k)) continue;
+    const size_t slot = (size_t)(first + k);
+    const float w = __expf(p.ws_lse[slot * H + h] - M);
+    tot += w;
+    const float* src = p.ws_o + (slot * H + h) * DV + 4 * j;
+#pragma unroll
+    for (int c = 0; c < DV / 64; ++c) acc[c] += w * *reinterpret_cast<const f32x4*>(src + 64 * c);
+  }
+  const float inv = 1.f / tot;
+#pragma unroll
+  for (int c = 0; c < DV / 64; ++c)
+    store_out4(p.o, p.o_f32, ((size_t)b * H + h) * DV + 4 * j + 64 * c, acc[c] * inv);
+  if (j == 0) p.lse[(size_t)b * H + h] = M + __logf(tot);
+}
+
+// ---------------------------------------------------------------- dispatch
+
+typedef void (*Stage1Fn)(Stage1Params);
+
+template <int HPW, int W, int D, int DV, int NBUF>
+int launch_stage1(const Stage1Params& sp, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((mla_stage1<HPW, W, D, DV, NBUF>), dim3(grid), dim3(64 * W), 0, st, sp);
+  return (int)hipGetLastError();
+}
+
+template <int D, int DV>
+int launch_stage1_for(const HeadTiling& ht, const Stage1Params& sp, int grid, hipStream_t st) {
+  // ring depth: as deep as LDS and the 6-bit vmcnt allow
+  if (ht.heads_per_wave == 32) {
+    switch (ht.waves) {
+      case 4: return launch_stage1<32, 4, D, DV, 4>(sp, grid, st);
+      case 2: return launch_stage1<32, 2, D, DV, (D == 576 ? 2 : 4)>(sp, grid, st);
+      default: return launch_stage1<32, 1, D, DV, (D == 576 ? 2 : 4)>(sp, grid, st);
+    }
+  } else {
+    switch (ht.waves) {
+      case 4: return launch_stage1<16, 4, D, DV, 4>(sp, grid, st);
+      case 2: return launch_stage1<16, 2, D, DV, (D == 576 ? 2 : 4)>(sp, grid, st);
+      default: return launch_stage1<16, 1, D, DV, (D == 576 ? 2 : 4)>(sp, grid, st);
+    }
+  }
+}
+
+}  // namespace
+
+int launch_decode(const DecodeArgs& a, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const HeadTiling ht = head_tiling(a.heads);
+
+  Stage1Params sp;
+  sp.q = reinterpret_cast<const __bf16*>(a.q);
+  sp.kv = reinterpret_cast<const uint8_t*>(a.kv);
+  sp.block_table = a.block_table;
+  sp.seq_lens = a.seq_lens;
+  sp.o = a.o;
+  sp.lse = a.lse;
+  sp.ws_o = a.ws_o;
+  sp.ws_lse = a.ws_lse;
+  sp.batch = a.batch;
+  sp.heads = a.heads;
+  sp.page_size = a.page_size;
+  sp.bt_stride = a.bt_stride;
+  sp.o_f32 = a.o_f32;
+  sp.split_mode = a.split_mode;
+  sp.num_splits = a.num_splits;
+  sp.head_chunks = ht.head_chunks;
+  sp.score_log2 = a.scale * kLog2e * (a.kv_fp8 ? a.k_scale : 1.f);
+  sp.out_scale = a.kv_fp8 ? a.k_scale : 1.f;
+
+  const int units = a.split_mode == 0 ? a.batch * a.num_splits : a.num_splits;
+  const int grid1 = (units + 7) / 8 * 8 * ht.head_chunks;
+  int err;
+  if (a.kv_fp8) return (int)hipErrorInvalidValue;  // fp8 kernels: not built yet
+  if (a.head_size == 576) err = launch_stage1_for<576, 512>(ht, sp, grid1, st);
+  else err = launch_stage1_for<320, 256>(ht, sp, grid1, st);
+  if (err) return err;
+
+  const bool merge = a.split_mode == 1 || a.num_splits > 1;
+  if (!merge) return 0;
+  Stage2Params s2;
+  s2.seq_lens = a.seq_lens;
+  s2.ws_o = a.ws_o;
+  s2.ws_lse = a.ws_lse;
+  s2.o = a.o;
+  s2.lse = a.lse;
+  s2.batch = a.batch;
+  s2.heads = a.heads;
+  s2.o_f32 = a.o_f32;
+  s2.split_mode = a.split_mode;
+  s2.num_splits = a.num_splits;
+  s2.head_groups = (a.heads + 15) / 16;
+  const int grid2 = a.batch * s2.head_groups;
+  if (a.d_v == 512) hipLaunchKernelGGL(mla_stage2<512>, dim3(grid2), dim3(256), 0, st, s2);
+  else hipLaunchKernelGGL(mla_stage2<256>, dim3(grid2), dim3(256), 0, st, s2);
+  return (int)hipGetLastError();
+}
+
+}  // namespace mla

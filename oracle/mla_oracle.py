@@ -97,7 +97,8 @@ def physical_slot(block_table_row: np.ndarray, pos: int, block_size: int) -> int
 def gather_rows(kv_rows: np.ndarray, block_table_row: np.ndarray, n: int,
                 block_size: int) -> np.ndarray:
     """Rows of positions 0..n-1 of one sequence, read through its table.
-    ``kv_rows`` is the pool flattened to [num_blocks * block_size, D]."""
+    ``kv_rows`` is the pool flattened to [num_blocks * block_size, D] (raw
+    bits or decoded values)."""
     slots = [physical_slot(block_table_row, t, block_size) for t in range(n)]
     return kv_rows[np.asarray(slots, dtype=np.int64)] if n else kv_rows[:0]
 
@@ -138,13 +139,14 @@ def decode(q_bits: np.ndarray, kv_bits: np.ndarray, block_table: np.ndarray,
     NB, P, D2 = kv_bits.shape
     if D2 != D:
         raise ValueError("q and cache head sizes differ")
-    rows = decode_kv(kv_bits, kv_dtype, k_scale).reshape(NB * P, D)
+    bits = kv_bits.reshape(NB * P, D)
     sc = float(np.float32(scale))
     idx = range(B) if batches is None else batches
     outs, lses = [], []
     for b in idx:
         q = bf16_bits_to_f64(q_bits[b])
-        K = gather_rows(rows, block_table[b], int(seq_lens[b]), P)
+        # gather the sequence's rows as stored, then decode only those
+        K = decode_kv(gather_rows(bits, block_table[b], int(seq_lens[b]), P), kv_dtype, k_scale)
         o, lse = attend(q, K, kv_lora_rank, sc)
         outs.append(o)
         lses.append(lse)
@@ -215,13 +217,13 @@ def decode_split(q_bits: np.ndarray, kv_bits: np.ndarray, block_table: np.ndarra
     by section 12's formula (or its (o_s, lse_s) form when ``normalised``)."""
     B, H, D = q_bits.shape
     NB, P, _ = kv_bits.shape
-    rows = decode_kv(kv_bits, kv_dtype, k_scale).reshape(NB * P, D)
+    bits = kv_bits.reshape(NB * P, D)
     sc = float(np.float32(scale))
     outs, lses = [], []
     for b in range(B):
         n = int(seq_lens[b])
         q = bf16_bits_to_f64(q_bits[b])
-        K = gather_rows(rows, block_table[b], n, P)
+        K = decode_kv(gather_rows(bits, block_table[b], n, P), kv_dtype, k_scale)
         segs = list(bounds_of(b, n)) or [(0, 0)]
         if normalised:
             parts = [attend(q, K[s:e], kv_lora_rank, sc) for (s, e) in segs]

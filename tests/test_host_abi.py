@@ -1,0 +1,134 @@
+"""CPU tests of libmla's host side: the library loads, exports every function
+include/mla.h declares, and its planner, workspace sizing and argument checks
+behave as documented.  No GPU work is enqueued: every mla_decode call here is
+rejected by the host checks before anything reaches HIP."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import mla_paged_latent_decode_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "pages_worked_examples.json")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = mla.load_library()
+    names = header_functions()
+    assert {"mla_decode", "mla_plan", "mla_workspace_size", "mla_status_string",
+            "mla_pages_split_count"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in range(10):
+        s = mla.mla_status_string(code)
+        assert s and "unknown" not in s
+    assert "unknown" in mla.mla_status_string(99)
+
+
+def test_pages_split_count_matches_worked_cases():
+    g = json.load(open(GOLDEN))["split_count_rule"]
+    for c in g["cases"]:
+        assert mla.mla_pages_split_count(c["max_seq_len"], c["sm_count"]) == c["splits"]
+    assert mla.mla_pages_split_count(100, 0) == 0
+
+
+def shape(**kw):
+    d = dict(batch=64, num_heads=128, head_size=576, page_size=64, num_blocks=8192,
+             max_blocks_per_seq=128)
+    d.update(kw)
+    return mla.make_shape(**d)
+
+
+def test_workspace_sizes():
+    s = shape()
+    assert mla.mla_workspace_size(s, mla.SPLIT_PER_SEQUENCE, 1) == 0
+    per = 64 * 16 * 128 * 512 * 4
+    got = mla.mla_workspace_size(s, mla.SPLIT_PER_SEQUENCE, 16)
+    lse_bytes = 64 * 16 * 128 * 4
+    assert got == per + lse_bytes  # both parts are 256-byte multiples here
+    bal = mla.mla_workspace_size(s, mla.SPLIT_BALANCED, 256)
+    assert bal == (256 + 64) * 128 * (512 + 1) * 4
+    assert mla.mla_workspace_size(s, 7, 4) == 0
+    assert mla.mla_workspace_size(s, mla.SPLIT_BALANCED, 0) == 0
+    assert mla.mla_workspace_size(shape(head_size=400), mla.SPLIT_BALANCED, 4) == 0
+
+
+def test_plan_deterministic_and_balanced():
+    s = shape()
+    assert mla.mla_plan(s, 8192, 0, 256, deterministic=True) == (mla.SPLIT_PER_SEQUENCE, 1, 0)
+    mode, units, ws = mla.mla_plan(s, 8192, 64 * 4608, 256)
+    assert mode == mla.SPLIT_BALANCED and units == 256
+    assert ws == mla.mla_workspace_size(s, mode, units)
+    # tiny batches get few units (at least 4 tiles each)
+    t = shape(batch=2, num_heads=16, page_size=16, num_blocks=16, max_blocks_per_seq=7)
+    mode, units, ws = mla.mla_plan(t, 100, 137, 256)
+    assert mode == mla.SPLIT_BALANCED and 1 <= units <= 2
+    # more head chunks -> fewer units per chunk
+    big = shape(num_heads=256)
+    assert mla.mla_plan(big, 8192, 64 * 4608, 256)[1] == 128
+
+
+@pytest.mark.parametrize("kw,exc", [
+    (dict(head_size=400), ValueError),
+    (dict(head_size=576, kv_lora_rank=448), ValueError),
+    (dict(page_size=24), ValueError),
+    (dict(page_size=0), ValueError),
+    (dict(q_dtype=mla.MLA_FP8_E4M3), NotImplementedError),
+    (dict(o_dtype=mla.MLA_FP8_E4M3), NotImplementedError),
+    (dict(num_heads=24), mla.MlaError),
+    (dict(batch=0), mla.MlaError),
+    (dict(num_blocks=0), mla.MlaError),
+])
+def test_plan_rejects_bad_shapes(kw, exc):
+    with pytest.raises(exc):
+        mla.mla_plan(shape(**kw), 1024, 0, 256)
+
+
+def _decode_raw(s, *, q=256, kv=256, bt=256, sl=256, scale=0.07, page=None, k_scale=1.0,
+                splits=1, mode=0, o=256, lse=256, ws=None, ws_bytes=0):
+    lib = mla.load_library()
+    return lib.mla_decode(ctypes.byref(s), q, kv, bt, sl, scale,
+                          s.page_size if page is None else page, k_scale, splits, mode, o, lse,
+                          ws, ws_bytes, None)
+
+
+def test_decode_argument_checks_fail_before_launch():
+    s = shape()
+    assert _decode_raw(s, q=None) == mla.MLA_ERR_NULL
+    assert _decode_raw(s, lse=None) == mla.MLA_ERR_NULL
+    assert _decode_raw(s, page=16) == mla.MLA_ERR_PAGE_SIZE
+    assert _decode_raw(shape(head_size=320, kv_lora_rank=512)) == mla.MLA_ERR_HEAD_SIZE
+    assert _decode_raw(s, splits=0) == mla.MLA_ERR_SPLITS
+    assert _decode_raw(s, mode=5) == mla.MLA_ERR_SPLITS
+    assert _decode_raw(s, splits=mla.MLA_MAX_KV_SPLITS + 1) == mla.MLA_ERR_SPLITS
+    assert _decode_raw(s, scale=float("nan")) == mla.MLA_ERR_ARGUMENT
+    assert _decode_raw(s, scale=-1.0) == mla.MLA_ERR_ARGUMENT
+    fp8 = shape(kv_dtype=mla.MLA_FP8_E4M3)
+    assert _decode_raw(fp8, k_scale=0.0) == mla.MLA_ERR_ARGUMENT
+    assert _decode_raw(fp8, k_scale=float("inf")) == mla.MLA_ERR_ARGUMENT
+    assert _decode_raw(s, q=258) == mla.MLA_ERR_ARGUMENT  # misaligned
+    # split layouts that need a workspace refuse a missing or short one
+    need = mla.mla_workspace_size(s, 0, 16)
+    assert _decode_raw(s, splits=16) == mla.MLA_ERR_WORKSPACE
+    assert _decode_raw(s, splits=16, ws=256, ws_bytes=need - 1) == mla.MLA_ERR_WORKSPACE
+    assert _decode_raw(s, splits=16, mode=1, ws=256, ws_bytes=10) == mla.MLA_ERR_WORKSPACE
+    assert _decode_raw(s, splits=16, ws=264, ws_bytes=need) == mla.MLA_ERR_ARGUMENT
+
+
+def test_fp8_query_is_refused():
+    with pytest.raises(NotImplementedError):
+        mla.mla_plan(shape(q_dtype=mla.MLA_FP8_E4M3), 100, 0, 256)
+    assert _decode_raw(shape(q_dtype=mla.MLA_FP8_E4M3)) == mla.MLA_ERR_DTYPE
