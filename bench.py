@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Benchmark of MLA paged latent decode on one MI355X.
+
+One step = one decode of the whole batch (stage 1 split-KV attention, then
+the stage-2 log-sum-exp merge) on synthetic seeded inputs already resident in
+HBM.  Default workload: B=64 sequences, H=128 heads, D=576 (kv_lora_rank 512
++ rope 64), bf16 q and cache, page 64, pool of 8192 pages, lengths uniform in
+[1024, 8192], shuffled block table, scale 192^-0.5.
+
+Two copies of the cache (the second with every page moved to another
+physical slot) alternate step by step, so consecutive steps never find the
+previous step's rows in the 256 MB Infinity Cache.
+
+Prints ONE JSON line: value = algorithmic HBM GB/s of the whole decode
+(bytes the method must move / time per step), plus TFLOP/s, the roofline of
+the stage-1 kernel timed with HIP events on its own stream, and the float64
+CPU oracle timed on the host as a baseline.
+
+Extra modes:
+  --copy-calibration   also runs a plain 1 GiB device copy (for scaling
+                       rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
+  --ingest-pmc F W     turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE,
+                       WRITE_SIZE runs of this script with --copy-calibration)
+                       into profiles/<kernel>_<workload>_traffic.json
+"""
+import argparse
+import csv
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode HBM GB/s + MFMA TFLOP/s (% of peak), B=64 H=128 D=576 ctx 1k-8k"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, public spec
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, public spec
+KERNEL_SRC = os.path.join(ROOT, "mla_paged_latent_decode_amd", "csrc", "mla_kernels.hip")
+COPY_BYTES = 1 << 30
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic(inp):
+    """Bytes and FLOPs the method itself must move / compute (no workspace,
+    no padding): the cache rows read once, q, o, lse, the table entries and
+    seq_lens; FLOPs = 2 H sum(n) (D + D_v)."""
+    import numpy as np
+    w = inp.workload
+    n = np.asarray(inp.seq_lens, dtype=np.int64)
+    e_kv = 2 if w.kv_dtype == "bf16" else 1
+    B, H, D, DV, P = w.batch, w.num_heads, w.head_size, w.kv_lora_rank, w.page_size
+    kv = int(n.sum()) * D * e_kv
+    table = int(((n + P - 1) // P).sum()) * 4
+    stage1 = kv + B * H * D * 2 + table + 4 * B
+    total = stage1 + B * H * DV * 2 + B * H * 4
+    flops = 2 * H * int(n.sum()) * (D + DV)
+    return {"kv_bytes": kv, "stage1_bytes": stage1, "total_bytes": total, "flops": flops,
+            "tokens": int(n.sum())}
+
+
+def cpu_baseline(inp, alg, budget_s=25.0):
+    """The float64 oracle on the host cores, over whole sequences of the same
+    batch until the batch is done or the time budget is spent."""
+    import numpy as np
+    import oracle
+    w = inp.workload
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = None
+    done, tok = 0, 0
+    t0 = time.perf_counter()
+    for b in range(w.batch):
+        oracle.decode(inp.q_bits, inp.kv_bits, inp.block_table, inp.seq_lens, scale=w.scale,
+                      k_scale=w.k_scale, kv_dtype=w.kv_dtype, kv_lora_rank=w.kv_lora_rank,
+                      batches=[b])
+        done += 1
+        tok += int(inp.seq_lens[b])
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    per_token = alg["total_bytes"] / alg["tokens"]
+    return {"value": round(tok * per_token / dt / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {w.batch} sequences ({tok} tokens) of the same batch, "
+                      f"{dt:.1f} s, numpy float64 with BLAS on the host",
+            "tokens_heads_per_s": round(tok * w.num_heads / dt, 1)}
+
+
+def load_traffic(workload):
+    path = os.path.join(ROOT, "profiles", f"mla_stage1_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_sha256_16") != kernel_hash():
+        return None  # counters were taken on another version of the kernel
+    return t.get("bytes_per_launch")
+
+
+def ingest_pmc(fetch_csv, write_csv, workload):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the stage-1
+    kernel, scaled by what the same counters read for the 1 GiB copy."""
+    def per_kernel(path, counter):
+        acc = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row["Kernel_Name"]
+                acc.setdefault(name, []).append(float(row["Counter_Value"]))
+        return acc
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(d, key):
+        ks = [k for k in d if key in k]
+        vals = [v for k in ks for v in d[k]]
+        return sum(vals) / len(vals) if vals else None
+
+    def copy_of(d):
+        ks = [k for k in d if "copy" in k.lower() or "elementwise" in k.lower()]
+        vals = [v for k in ks for v in d[k]]
+        return max(vals) if vals else None
+    f1, w1 = pick(fetch, "mla_stage1"), pick(write, "mla_stage1")
+    fc, wc = copy_of(fetch), copy_of(write)
+    ffac = COPY_BYTES / (fc * 1024) if fc else 1.0
+    wfac = COPY_BYTES / (wc * 1024) if wc else 1.0
+    out = {"workload": workload, "kernel_sha256_16": kernel_hash(),
+           "fetch_kib_per_dispatch": f1, "write_kib_per_dispatch": w1,
+           "copy_fetch_kib": fc, "copy_write_kib": wc, "fetch_scale": ffac, "write_scale": wfac,
+           "bytes_per_launch": (f1 * 1024 * ffac + w1 * 1024 * wfac) if f1 and w1 else None,
+           "sources": [os.path.basename(fetch_csv), os.path.basename(write_csv)]}
+    path = os.path.join(ROOT, "profiles", f"mla_stage1_{workload}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--split", default="plan", choices=["plan", "pages", "single"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    args = ap.parse_args()
+
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world}): this "
+              "library has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import mla_paged_latent_decode_amd as mla
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    inp = W.generate(args.workload)
+    w = inp.workload
+    alg = algorithmic(inp)
+    print(f"[bench] generated {args.workload} in {time.perf_counter() - t_gen:.1f}s: "
+          f"{alg['tokens']} tokens", file=sys.stderr, flush=True)
+
+    q = torch.from_numpy(inp.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    if w.kv_dtype == "bf16":
+        kv = torch.from_numpy(inp.kv_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        kv = torch.from_numpy(inp.kv_bits).view(torch.float8_e4m3fn).to(dev)
+    bt = torch.from_numpy(inp.block_table).to(dev)
+    sl = torch.from_numpy(inp.seq_lens).to(dev)
+    # second copy of the cache with its pages moved (input preparation only)
+    g = torch.Generator(device="cpu").manual_seed(1234)
+    new_of_old = torch.randperm(kv.shape[0], generator=g).to(dev)
+    kv2 = torch.empty_like(kv)
+    kv2[new_of_old] = kv
+    bt2 = new_of_old.to(torch.int32)[bt.long()].contiguous()
+    sets = [(kv, bt), (kv2, bt2)]
+
+    shape = mla.shape_of(q, kv, bt)
+    max_len, tot = int(inp.seq_lens.max()), int(inp.seq_lens.sum())
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    if args.split == "plan":
+        mode, splits, ws_bytes = mla.mla_plan(shape, max_len, tot, cus)
+    elif args.split == "pages":
+        mode, splits = mla.SPLIT_PER_SEQUENCE, mla.mla_pages_split_count(max_len, cus)
+        ws_bytes = mla.mla_workspace_size(shape, mode, splits)
+    else:
+        mode, splits, ws_bytes = mla.SPLIT_PER_SEQUENCE, 1, 0
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    o = torch.empty((w.batch, w.num_heads, w.kv_lora_rank), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, w.num_heads), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    calls = [mla.PreparedDecode(q, k, b, sl, w.scale, w.page_size, w.k_scale, splits, mode, o,
+                                lse, ws, stream=stream.cuda_stream) for (k, b) in sets]
+
+    for i in range(args.warmup):
+        calls[i % 2]("stage1")
+        calls[i % 2]("stage2")
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        c = calls[i % 2]
+        evs[i][0].record(stream)
+        c("stage1")
+        evs[i][1].record(stream)
+        c("stage2")
+        evs[i][2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / K
+    s1 = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    s2 = np.array([e[1].elapsed_time(e[2]) for e in evs])
+
+    if args.copy_calibration:
+        a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        bcopy = torch.empty_like(a)
+        for _ in range(3):
+            bcopy.copy_(a)
+        torch.cuda.synchronize()
+
+    gbs = alg["total_bytes"] / (ms_step * 1e-3) / 1e9
+    tflops = alg["flops"] / (ms_step * 1e-3) / 1e12
+    s1_ms = float(s1.mean())
+    t_hbm = alg["stage1_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = alg["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        ach = alg["stage1_bytes"] / (s1_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    else:
+        ach = alg["flops"] / (s1_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
+    roof["traffic"] = load_traffic(args.workload)
+    roof["kernel"] = "mla_stage1"
+    roof["avg_launch_ms"] = round(s1_ms, 5)
+    roof["mfma_tflops"] = round(alg["flops"] / (s1_ms * 1e-3) / 1e12, 1)
+    roof["mfma_frac"] = round(roof["mfma_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
+    roof["hbm_gbs"] = round(alg["stage1_bytes"] / (s1_ms * 1e-3) / 1e9, 1)
+    roof["hbm_frac"] = round(roof["hbm_gbs"] / HBM_PEAK_GBS, 4)
+    roof["roofline_frac"] = round(max(t_hbm, t_mfma) / (s1_ms * 1e-3), 4)
+
+    out = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.kv_dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.description}", "batch": w.batch,
+                   "heads": w.num_heads, "head_size": w.head_size,
+                   "kv_lora_rank": w.kv_lora_rank, "page_size": w.page_size,
+                   "total_tokens": alg["tokens"], "split_mode": int(mode),
+                   "num_kv_splits": int(splits), "seed": w.seed},
+        "tflops": round(tflops, 1),
+        "tokens_heads_per_s": round(alg["tokens"] * w.num_heads / (ms_step * 1e-3), 1),
+        "roofline_frac_total": round(max(alg["total_bytes"] / (HBM_PEAK_GBS * 1e9), t_mfma)
+                                     / (ms_step * 1e-3), 4),
+        "stage2_avg_ms": round(float(s2.mean()), 5),
+        "wall_s": round(wall, 4),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, alg)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

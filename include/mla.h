@@ -182,6 +182,28 @@ mla_status mla_decode(const mla_shape* shape, const void* q, const void* kv_cach
                       int32_t split_mode, void* o, float* lse, void* workspace,
                       size_t workspace_bytes, void* hip_stream);
 
+/* The two halves of mla_decode, for callers that time or schedule them
+ * apart.  Same arguments, checks and ownership as mla_decode; issuing
+ * mla_decode_stage1 then mla_decode_stage2 on one stream with the same
+ * arguments is exactly mla_decode.
+ *   stage1  the split-KV attention over every segment ("vLLM 中 Attention
+ *           Kernel 如何并行处理多个请求", section 十二, the parallel segments):
+ *           sequences covered by one segment get their final o/lse, the others
+ *           leave (o_s, lse_s) partials in the workspace.
+ *   stage2  the log-sum-exp merge of those partials into o/lse (same section,
+ *           the second reduction kernel); enqueues nothing when the split
+ *           layout produced no partials (per-sequence mode with one split). */
+mla_status mla_decode_stage1(const mla_shape* shape, const void* q, const void* kv_cache,
+                             const int32_t* block_table, const int32_t* seq_lens, float scale,
+                             int32_t page_size, float k_scale, int32_t num_kv_splits,
+                             int32_t split_mode, void* o, float* lse, void* workspace,
+                             size_t workspace_bytes, void* hip_stream);
+mla_status mla_decode_stage2(const mla_shape* shape, const void* q, const void* kv_cache,
+                             const int32_t* block_table, const int32_t* seq_lens, float scale,
+                             int32_t page_size, float k_scale, int32_t num_kv_splits,
+                             int32_t split_mode, void* o, float* lse, void* workspace,
+                             size_t workspace_bytes, void* hip_stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char* mla_status_string(int32_t status);
 

@@ -71,9 +71,10 @@ def load_library():
         lib.mla_plan.restype = i32
         lib.mla_workspace_size.argtypes = [shp, i32, i32]
         lib.mla_workspace_size.restype = sz
-        lib.mla_decode.argtypes = [shp, vp, vp, vp, vp, ctypes.c_float, i32, ctypes.c_float, i32,
-                                   i32, vp, vp, vp, sz, vp]
-        lib.mla_decode.restype = i32
+        for fn in (lib.mla_decode, lib.mla_decode_stage1, lib.mla_decode_stage2):
+            fn.argtypes = [shp, vp, vp, vp, vp, ctypes.c_float, i32, ctypes.c_float, i32, i32,
+                           vp, vp, vp, sz, vp]
+            fn.restype = i32
         lib.mla_status_string.argtypes = [i32]
         lib.mla_status_string.restype = ctypes.c_char_p
         _LIB = lib
@@ -161,14 +162,15 @@ def mla_decode(q, kv_cache, block_table, seq_lens, scale: float, page_size: int,
                split_mode: Optional[int] = None, workspace=None, kv_dtype=None,
                o_dtype=None, max_seq_len: Optional[int] = None,
                total_seq_len: Optional[int] = None, num_cus: Optional[int] = None,
-               deterministic: bool = False, stream=None):
+               deterministic: bool = False, stream=None, stages: str = "both"):
     """Enqueue one MLA decode step on the current (or given) stream.
 
     When ``num_kv_splits`` is None the split plan comes from ``mla_plan``
     (which needs ``max_seq_len``; it is read from ``seq_lens`` when not
     given).  When ``num_kv_splits`` is given without ``split_mode``, the
     per-sequence split layout is used.  Missing ``o``/``lse``/``workspace``
-    are allocated with torch.  Returns (o, lse)."""
+    are allocated with torch.  ``stages`` = "stage1" / "stage2" enqueues only
+    that half (mla_decode_stage1 / mla_decode_stage2).  Returns (o, lse)."""
     torch = _torch()
     lib = load_library()
     if not (q.is_cuda and kv_cache.is_cuda and block_table.is_cuda and seq_lens.is_cuda):
@@ -211,10 +213,44 @@ def mla_decode(q, kv_cache, block_table, seq_lens, scale: float, page_size: int,
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
-    st = lib.mla_decode(ctypes.byref(shape), q.data_ptr(), kv_cache.data_ptr(),
+    fn = {"both": lib.mla_decode, "stage1": lib.mla_decode_stage1,
+          "stage2": lib.mla_decode_stage2}[stages]
+    st = fn(ctypes.byref(shape), q.data_ptr(), kv_cache.data_ptr(),
                         block_table.data_ptr(), seq_lens.data_ptr(), float(scale),
                         int(page_size), float(k_scale), int(num_kv_splits), int(split_mode),
                         o.data_ptr(), lse.data_ptr(), ws_ptr, int(ws_bytes), stream)
     if st != MLA_OK:
         _raise(st, "mla_decode")
     return o, lse
+
+
+class PreparedDecode:
+    """A decode call with every argument marshalled once, for loops that
+    launch the same step repeatedly (benchmarks, graph capture).  Calling it
+    enqueues the chosen stages through the C ABI; torch tensors are kept
+    alive by this object."""
+
+    def __init__(self, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
+                 num_kv_splits, split_mode, o, lse, workspace=None, kv_dtype=None, stream=None):
+        torch = _torch()
+        self.lib = load_library()
+        self.keep = (q, kv_cache, block_table, seq_lens, o, lse, workspace)
+        self.shape = shape_of(q, kv_cache, block_table, kv_dtype=kv_dtype, o_dtype=o.dtype)
+        need = mla_workspace_size(self.shape, split_mode, num_kv_splits)
+        if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+            raise MlaError(MLA_ERR_WORKSPACE, "workspace too small")
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        self.args = (ctypes.byref(self.shape), q.data_ptr(), kv_cache.data_ptr(),
+                     block_table.data_ptr(), seq_lens.data_ptr(), float(scale), int(page_size),
+                     float(k_scale), int(num_kv_splits), int(split_mode), o.data_ptr(),
+                     lse.data_ptr(), workspace.data_ptr() if workspace is not None else None,
+                     workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                     stream)
+        self.fns = {"both": self.lib.mla_decode, "stage1": self.lib.mla_decode_stage1,
+                    "stage2": self.lib.mla_decode_stage2}
+
+    def __call__(self, stages: str = "both"):
+        st = self.fns[stages](*self.args)
+        if st != MLA_OK:
+            _raise(st, "mla_decode")

@@ -49,8 +49,9 @@ static int64_t stage1_lds_bytes(const mla_shape& s) {
   const HeadTiling t = head_tiling(s.num_heads);
   const int64_t tile = (int64_t)kTile * s.head_size * 2;
   int nbuf = 4;
-  if (t.waves < 4 && s.head_size == 576) nbuf = 2;
-  return nbuf * tile;
+  if (s.head_size == 576) nbuf = t.waves < 4 ? 2 : (t.heads_per_wave == 32 ? 3 : 4);
+  const int64_t qlds = (t.heads_per_wave == 32 && s.head_size == 576) ? t.waves * 12 * 1024 : 0;
+  return nbuf * tile + qlds;
 }
 
 }  // namespace mla
@@ -130,11 +131,12 @@ mla_status mla_plan(const mla_shape* shape, int32_t max_seq_len, int64_t total_s
   return MLA_OK;
 }
 
-mla_status mla_decode(const mla_shape* shape, const void* q, const void* kv_cache,
-                      const int32_t* block_table, const int32_t* seq_lens, float scale,
-                      int32_t page_size, float k_scale, int32_t num_kv_splits,
-                      int32_t split_mode, void* o, float* lse, void* workspace,
-                      size_t workspace_bytes, void* hip_stream) {
+static mla_status decode_stages(const mla_shape* shape, const void* q, const void* kv_cache,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                float scale, int32_t page_size, float k_scale,
+                                int32_t num_kv_splits, int32_t split_mode, void* o, float* lse,
+                                void* workspace, size_t workspace_bytes, void* hip_stream,
+                                int stages) {
   mla_status st = check_shape(shape);
   if (st != MLA_OK) return st;
   if (!q || !kv_cache || !block_table || !seq_lens || !o || !lse) return MLA_ERR_NULL;
@@ -181,7 +183,37 @@ mla_status mla_decode(const mla_shape* shape, const void* q, const void* kv_cach
   a.num_splits = num_kv_splits;
   a.scale = scale;
   a.k_scale = k_scale;
-  return launch_decode(a, hip_stream) == 0 ? MLA_OK : MLA_ERR_LAUNCH;
+  return launch_decode(a, hip_stream, stages) == 0 ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+mla_status mla_decode(const mla_shape* shape, const void* q, const void* kv_cache,
+                      const int32_t* block_table, const int32_t* seq_lens, float scale,
+                      int32_t page_size, float k_scale, int32_t num_kv_splits,
+                      int32_t split_mode, void* o, float* lse, void* workspace,
+                      size_t workspace_bytes, void* hip_stream) {
+  return decode_stages(shape, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
+                       num_kv_splits, split_mode, o, lse, workspace, workspace_bytes, hip_stream,
+                       kBothStages);
+}
+
+mla_status mla_decode_stage1(const mla_shape* shape, const void* q, const void* kv_cache,
+                             const int32_t* block_table, const int32_t* seq_lens, float scale,
+                             int32_t page_size, float k_scale, int32_t num_kv_splits,
+                             int32_t split_mode, void* o, float* lse, void* workspace,
+                             size_t workspace_bytes, void* hip_stream) {
+  return decode_stages(shape, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
+                       num_kv_splits, split_mode, o, lse, workspace, workspace_bytes, hip_stream,
+                       kStage1);
+}
+
+mla_status mla_decode_stage2(const mla_shape* shape, const void* q, const void* kv_cache,
+                             const int32_t* block_table, const int32_t* seq_lens, float scale,
+                             int32_t page_size, float k_scale, int32_t num_kv_splits,
+                             int32_t split_mode, void* o, float* lse, void* workspace,
+                             size_t workspace_bytes, void* hip_stream) {
+  return decode_stages(shape, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
+                       num_kv_splits, split_mode, o, lse, workspace, workspace_bytes, hip_stream,
+                       kStage2);
 }
 
 const char* mla_status_string(int32_t status) {

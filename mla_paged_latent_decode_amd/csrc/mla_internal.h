@@ -55,7 +55,10 @@ struct DecodeArgs {
   float k_scale;
 };
 
-// Enqueues stage 1 (and stage 2 when needed).  Returns 0 or a HIP error code.
-int launch_decode(const DecodeArgs& a, void* stream);
+enum Stages { kStage1 = 1, kStage2 = 2, kBothStages = 3 };
+
+// Enqueues stage 1 and/or stage 2 (stage 2 only when the split layout needs
+// a merge).  Returns 0 or a HIP error code.
+int launch_decode(const DecodeArgs& a, void* stream, int stages);
 
 }  // namespace mla

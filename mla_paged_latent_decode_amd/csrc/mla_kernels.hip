@@ -11,12 +11,11 @@
 //   where V is the leading D_v columns of the same tile.  Pages are reached
 //   through the block table (same article, section 十一).
 //
-//   Tiles stream HBM -> LDS with 16-byte global_load_lds (no register
+//   Tiles stream HBM -> LDS with 16-byte buffer_load ... lds (no register
 //   staging) into a ring of NBUF tiles, NBUF-1 tiles ahead of the compute.
-//   The LDS tile is stored as 1 KB blocks, each the exact operand footprint of
-//   one MFMA k-step, with an XOR swizzle so that both the QK^T read
-//   (ds_read_b128) and the transposed V read (ds_read_b64_tr_b16) hit
-//   distinct banks.
+//   The LDS tile is stored as 1 KB blocks of 16 positions x 64 bytes with an
+//   XOR swizzle, so that both the QK^T read (ds_read_b128) and the
+//   transposed V read (ds_read_b64_tr_b16) hit distinct banks.
 //
 // Stage 2 (merge).  Partials (o_s, lse_s) of a sequence are combined with the
 //   log-sum-exp rule of the same article, section 十二:
@@ -30,6 +29,21 @@
 
 namespace mla {
 namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Scalar (SMEM) read of one int32 at byte `offset` of the buffer `rsrc`,
+// waited for in place.  The block-table reads go through the scalar cache and
+// lgkmcnt: issued as a compiler intrinsic, the compiler would first drain
+// every in-flight tile load (vmcnt(0)) in case the load alias them, which
+// serialises the HBM->LDS ring; the asm form has no such wait.  (A read
+// only; nothing here writes through the scalar cache.)
+__device__ __forceinline__ int sload_i32(i32x4 rsrc, int offset) {
+  int v;
+  asm volatile("s_buffer_load_dword %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
+               : "=s"(v) : "s"(rsrc), "s"(offset));
+  return v;
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -46,10 +60,18 @@ constexpr float kLn2 = 0.6931471805599453f;
 // The final result does not depend on this choice; it only saves rescales.
 constexpr float kTau = 8.0f;
 
-// 4 KB of zeros in device memory: tail positions of a segment's last tile
-// load from here, so the LDS rows of positions past the sequence are zero and
-// never carry the (possibly NaN) contents of unreferenced cache slots.
-__device__ __attribute__((aligned(256))) const uint32_t g_zero_rows[1024] = {0};
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<0, N>(f);
+}
 
 template <int VM>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -59,6 +81,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 __device__ __forceinline__ float wave_max_xor(float x, int mask) {
   return fmaxf(x, __shfl_xor(x, mask, 64));
@@ -73,6 +100,29 @@ __device__ __forceinline__ float max_halves(float x) {
 __device__ __forceinline__ float sum_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Transposed LDS read (ds_read_b64_tr_b16) issued from inline asm.  Issued
+// through the builtin, the compiler conservatively drains every in-flight
+// tile load (vmcnt(0)) before it, which would serialise the HBM->LDS ring;
+// from asm it does not, and the ring's own explicit waits + barrier already
+// order these reads after the tile's loads.  The result may only be used
+// after lds_wait<N>() on it (asm reads are invisible to the compiler's
+// lgkmcnt tracking).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr16_asm(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field is 16 bits");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+// Wait until at most N LDS/SMEM operations are outstanding, then hand x
+// back: the dependence makes every use of x come after the wait.
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4& x) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt is a 4-bit counter");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
 }
 
 // Multiply an MFMA accumulator held in AGPRs by s in place.  The "+a"
@@ -167,22 +217,42 @@ __device__ __forceinline__ int64_t total_tiles(const int32_t* seq_lens, int B, i
 
 template <int HPW, int W, int D, int DV, int NBUF>
 struct Cfg {
-  static constexpr int NKS = HPW == 32 ? D / 16 : D / 32;          // QK k-steps
-  static constexpr int NBLK = kTile * D * 2 / 1024;                  // 1 KB blocks per tile
-  static constexpr int LPW = NBLK / W;                               // DMA ops per wave per tile
+  static constexpr int NKQ = D / 32;                       // 32-wide d groups per row
+  static constexpr int NBLK = 2 * NKQ;                     // 1 KB LDS blocks per tile
+  static constexpr int NKS = HPW == 32 ? D / 16 : D / 32;  // QK k-steps
+  // With 32 heads per wave and D = 576, the O accumulators (256 registers)
+  // and all 36 Q fragments (144) leave too few registers for the rest of the
+  // loop; the last QLDS k-steps of Q then live in LDS (1 KB per step/wave).
+  static constexpr int QLDS = (HPW == 32 && D == 576) ? 12 : 0;
+  static constexpr int NQR = NKS - QLDS;                   // Q k-steps held in VGPRs
+  static constexpr int QLDS_BYTES = W * QLDS * 1024;
+  static constexpr int LPW = NBLK / W;                     // DMA ops per wave per tile
   static constexpr int TILE_BYTES = NBLK * 1024;
-  static constexpr int NVB = HPW == 32 ? DV / 32 : DV / 16;         // PV output blocks
+  static constexpr int NVB = HPW == 32 ? DV / 32 : DV / 16;  // PV output blocks
   static constexpr int HEADS_PER_WG = HPW * W;
+  static constexpr int ROW_BYTES = D * 2;
+  static_assert(NBLK * 1024 == kTile * D * 2, "tile bytes");
   static_assert(NBLK % W == 0, "each wave issues the same number of tile loads");
   static_assert((NBUF - 1) * LPW <= 63, "outstanding loads must fit the vmcnt counter");
-  static_assert(HPW == 32 ? (D % 16 == 0 && DV % 32 == 0) : (D % 32 == 0 && DV % 16 == 0), "");
-  static_assert(HPW == 32 ? NBLK == NKS : NBLK == 2 * NKS, "tile block count");
+  static_assert(NBUF * TILE_BYTES + QLDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(D % 32 == 0 && DV % 32 == 0, "");
 };
+
+// LDS layout of a 32-position tile.  Block (th, kq), at (th * NKQ + kq) KB,
+// holds positions 16*th .. 16*th+15 and the four 16-byte chunks c4 of d-group
+// kq (d = 32*kq + 8*c4 + e).  Chunk (t16, c4) sits at 16-byte slot
+// (t16 ^ f(c4)) + 16*c4 with f(c4) = 8*(c4 & 1) + 4*(c4 >> 1): a 16-lane
+// quarter of a QK^T read (fixed c4, t16 = 0..15) and each half-wave of a
+// transposed V read (4 or 8 positions x 4 chunks) touch 16 distinct 16-byte
+// bank groups.
+__device__ __forceinline__ int tile_slot(int t16, int c4) {
+  return (t16 ^ (8 * (c4 & 1) + 4 * (c4 >> 1))) + 16 * c4;
+}
 
 template <int HPW, int W, int D, int DV, int NBUF>
 __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   using C = Cfg<HPW, W, D, DV, NBUF>;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * C::TILE_BYTES + C::QLDS_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -199,97 +269,102 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   const int H = p.heads;
 
   // ---------------- per-lane constants of the LDS layout
-  // HPW == 32: block ks holds chunks (t, 2ks + h2) of the 32 tokens; logical
-  //   position t + 32*h2, stored at pos ^ (h2 << 2) ^ ((ks & 1) << 3).
-  // HPW == 16: block th*NKS + ks holds chunks (16th + t16, 4ks + c4); logical
-  //   position t16 + 16*c4, stored at pos ^ ((c4 & 1) << 3).
-  int qk_off_e, qk_off_o;  // LDS byte offset of this lane's K chunk (even / odd block)
-  int v_off0, v_off1;      // LDS byte offsets of this lane's V^T reads
-  int ld_tok_e, ld_tok_o, ld_chunk;  // what this lane loads (token for even/odd block, chunk byte)
+  // DMA: lane l writes slot l of a block: chunk c4 = l / 16 of position
+  // t16 = (l % 16) ^ f(c4); its source offset within the 16-row page run.
+  const int dma_c4 = lane >> 4;
+  const int dma_voff =
+      ((lane & 15) ^ (8 * (dma_c4 & 1) + 4 * (dma_c4 >> 1))) * C::ROW_BYTES + 16 * dma_c4;
+  int qk_off_e, qk_off_o, v_off0, v_off1;
   if constexpr (HPW == 32) {
-    const int h2 = lane >> 5;
-    const int pe = lane ^ (h2 << 2);
-    const int po = pe ^ 8;
-    qk_off_e = pe * 16;
-    qk_off_o = po * 16;
-    ld_tok_e = pe & 31;
-    ld_tok_o = po & 31;
-    ld_chunk = h2 * 16;
+    // QK A operand: position t = lane % 32, chunk 2*ks + lane / 32
+    const int t = lane & 31, h2 = lane >> 5;
+    const int thb = (t >> 4) * C::NKQ * 1024;
+    qk_off_e = thb + tile_slot(t & 15, h2) * 16;      // ks even: c4 = h2
+    qk_off_o = thb + tile_slot(t & 15, 2 + h2) * 16;  // ks odd:  c4 = 2 + h2
+    // V^T A operand (transposed read): 4 positions x 16 v per 16-lane group
     const int g = lane >> 4, i = lane & 15, half = lane >> 5;
-    const int vh2 = (i >> 1) & 1;
-    const int t0 = 4 * half + (i >> 2);
-    const int base = ((t0 ^ (vh2 << 2)) + 32 * vh2) * 16 + 8 * (i & 1) + (g & 1) * 1024;
-    v_off0 = base + 8 * ((g & 1)) * 16;
-    v_off1 = base + 8 * ((g & 1) ^ 1) * 16;
+    const int c4 = 2 * (g & 1) + ((i >> 1) & 1);
+    v_off0 = tile_slot(4 * half + (i >> 2), c4) * 16 + 8 * (i & 1);
+    v_off1 = tile_slot(4 * half + (i >> 2) + 8, c4) * 16 + 8 * (i & 1);
   } else {
-    const int pp = lane ^ (((lane >> 4) & 1) << 3);
-    qk_off_e = qk_off_o = pp * 16;
-    ld_tok_e = pp & 15;   // + 16 * th
-    ld_tok_o = pp & 15;
-    ld_chunk = (pp >> 4) * 16;
+    qk_off_e = qk_off_o = tile_slot(lane & 15, lane >> 4) * 16;
     const int g = lane >> 4, i = lane & 15;
-    const int vc = (i >> 1) & 1;
     const int t16 = 4 * g + (i >> 2);
-    v_off0 = ((t16 ^ (vc << 3)) + 16 * vc) * 16 + 8 * (i & 1);
-    v_off1 = v_off0;  // th = 1 adds NKS blocks
+    v_off0 = tile_slot(t16, (i >> 1) & 1) * 16 + 8 * (i & 1);      // even v-block
+    v_off1 = tile_slot(t16, 2 + ((i >> 1) & 1)) * 16 + 8 * (i & 1);  // odd v-block
   }
 
-  const uint8_t* zero_row = reinterpret_cast<const uint8_t*>(g_zero_rows);
-  const int64_t row_bytes = (int64_t)D * 2;
   const int P = p.page_size;
 
   // ---------------- one segment [ts, te) of sequence b
   auto process = [&](int b, int ts, int te, bool final_out, int slot) __attribute__((always_inline)) {
     const int n_tiles = (te - ts + kTile - 1) / kTile;
-    const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
+    i32x4 bt_rsrc;  // the sequence's block-table row
+    {
+      const uint64_t a = reinterpret_cast<uint64_t>(p.block_table + (int64_t)b * p.bt_stride);
+      bt_rsrc[0] = uniform((int)(uint32_t)a);
+      bt_rsrc[1] = uniform((int)(uint32_t)(a >> 32));
+      bt_rsrc[2] = p.bt_stride * 4;
+      bt_rsrc[3] = 0x00020000;
+    }
+    // page cursor of the next 16-position half to load
+    int cur_lb = ts / P;
+    int cur_off = ts - cur_lb * P;
+    int cur_tok = ts;
 
-    // issue the DMA loads of tile i into ring slot i % NBUF
+    // Issue the loads of the next tile (ring slot i % NBUF).  Each 16-row
+    // half lies in one page (P and 16-position boundaries are multiples of
+    // 16); a buffer resource sized to the valid rows makes the loads of
+    // positions past the segment return zeros, so those LDS rows hold zeros
+    // and never the (possibly NaN) contents of unreferenced slots.
     auto issue = [&](int i) __attribute__((always_inline)) {
-      const int tok0 = ts + i * kTile;
-      const int nvalid = min(kTile, te - tok0);
-      const int lb0 = tok0 / P;
-      const int off0 = tok0 - lb0 * P;
-      const int lb1 = (off0 + nvalid > P) ? lb0 + 1 : lb0;
-      const int64_t pg0 = bt[lb0];
-      const int64_t pg1 = bt[lb1];
       uint8_t* dst = ring + (i % NBUF) * C::TILE_BYTES;
-      auto row_ptr = [&](int t) __attribute__((always_inline)) -> const uint8_t* {
-        if (t >= nvalid) return zero_row;
-        const int x = off0 + t;
-        const int64_t page = x < P ? pg0 : pg1;
-        const int r = x < P ? x : x - P;
-        return p.kv + (page * P + r) * row_bytes + ld_chunk;
-      };
-      if constexpr (HPW == 32) {
-        const uint8_t* src_e = row_ptr(ld_tok_e);
-        const uint8_t* src_o = row_ptr(ld_tok_o);
+      __amdgpu_buffer_rsrc_t rs[2];
 #pragma unroll
-        for (int k = 0; k < C::LPW; ++k) {
-          const int j = wave + k * W;  // block index
-          const uint8_t* src = (j & 1) ? src_o : src_e;
-          __builtin_amdgcn_global_load_lds(src + j * 32, (LDS_AS void*)(dst + j * 1024), 16, 0, 0);
+      for (int th = 0; th < 2; ++th) {
+        const int nv = uniform(max(0, min(16, te - cur_tok)));
+        uint64_t base = reinterpret_cast<uint64_t>(p.kv);
+        if (nv > 0) {
+          const int64_t page = sload_i32(bt_rsrc, cur_lb * 4);
+          base += (uint64_t)((page * P + cur_off) * (int64_t)C::ROW_BYTES);
         }
-      } else {
-        const uint8_t* src0 = row_ptr(ld_tok_e);
-        const uint8_t* src1 = row_ptr(ld_tok_e + 16);
+        // every field wave-uniform, so the resource lives in SGPRs
+        base = ((uint64_t)(uint32_t)uniform((int)(base >> 32)) << 32) |
+               (uint32_t)uniform((int)(uint32_t)base);
+        rs[th] = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nv * C::ROW_BYTES,
+                                                   0x00020000);
+        cur_tok += 16;
+        cur_off += 16;
+        if (cur_off == P) {
+          cur_off = 0;
+          ++cur_lb;
+        }
+      }
 #pragma unroll
-        for (int k = 0; k < C::LPW; ++k) {
-          const int j = wave + k * W;
-          const int th = j / C::NKS, ks = j % C::NKS;
-          const uint8_t* src = th ? src1 : src0;
-          __builtin_amdgcn_global_load_lds(src + ks * 64, (LDS_AS void*)(dst + j * 1024), 16, 0, 0);
-        }
+      for (int k = 0; k < C::LPW; ++k) {
+        const int j = wave + k * W;  // block index
+        const int th = j >= C::NKQ ? 1 : 0;
+        const int kq = j - th * C::NKQ;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(th ? rs[1] : rs[0],
+                                                 (LDS_AS void*)(dst + j * 1024), 16,
+                                                 dma_voff + 64 * kq, 0, 0, 0);
       }
     };
 
-    // Q fragments of this wave's heads (B operand of S^T = K Q^T)
-    bf16x8 qf[C::NKS];
+    // Q fragments of this wave's heads (B operand of S^T = K Q^T): the first
+    // NQR k-steps in VGPRs, the rest in this wave's LDS region (lane-linear)
+    bf16x8 qf[C::NQR];
+    LDS_AS uint8_t* qlds = (LDS_AS uint8_t*)ring + NBUF * C::TILE_BYTES + wave * C::QLDS * 1024;
     {
       const __bf16* qb = p.q + ((int64_t)b * H + h0) * D;
       if constexpr (HPW == 32) {
         const __bf16* qr = qb + (int64_t)(lane & 31) * D + 8 * (lane >> 5);
 #pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qr + 16 * ks);
+        for (int ks = 0; ks < C::NQR; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qr + 16 * ks);
+#pragma unroll
+        for (int ks = C::NQR; ks < C::NKS; ++ks)
+          *reinterpret_cast<LDS_AS bf16x8*>(qlds + (ks - C::NQR) * 1024 + lane * 16) =
+              *reinterpret_cast<const bf16x8*>(qr + 16 * ks);
       } else {
         const __bf16* qr = qb + (int64_t)(lane & 15) * D + 8 * (lane >> 4);
 #pragma unroll
@@ -305,9 +380,14 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
 #pragma unroll
     for (int vb = 0; vb < C::NVB; ++vb) oacc[vb] = acc_t{};
 
-    __builtin_amdgcn_s_barrier();  // every wave is done with the ring of a previous segment
-    const int pre = min(NBUF - 1, n_tiles);
-    for (int i = 0; i < pre; ++i) issue(i);
+    // Drain this wave's earlier stores and loads once, so that no wait for
+    // them lands between the ring loads below, then make sure every wave is
+    // done with the ring of a previous segment.
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i)
+      if (i < n_tiles) issue(i);
 
     for (int i = 0; i < n_tiles; ++i) {
       const int ahead = min(NBUF - 2, n_tiles - 1 - i);
@@ -317,31 +397,44 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       __builtin_amdgcn_s_barrier();
       if (i + NBUF - 1 < n_tiles) issue(i + NBUF - 1);
 
-      const uint8_t* tile = ring + (i % NBUF) * C::TILE_BYTES;
+      const LDS_AS uint8_t* tile = (const LDS_AS uint8_t*)ring + (i % NBUF) * C::TILE_BYTES;
       const int nvalid = min(kTile, te - (ts + i * kTile));
 
       if constexpr (HPW == 32) {
-        // ---- S^T[32 tokens, 32 heads] over D
+        // ---- S^T[32 positions, 32 heads] over D
         f32x16 s = {};
         {
           auto kread = [&](int ks) __attribute__((always_inline)) {
             return *reinterpret_cast<const LDS_AS bf16x8*>(
-                (const LDS_AS uint8_t*)tile + ks * 1024 + ((ks & 1) ? qk_off_o : qk_off_e));
+                tile + (ks >> 1) * 1024 + ((ks & 1) ? qk_off_o : qk_off_e));
           };
-          // software pipeline: the K chunk of step ks+2 is in flight while
-          // step ks runs on the matrix core
+          auto qread = [&](int ks) __attribute__((always_inline)) {
+            return *reinterpret_cast<const LDS_AS bf16x8*>(qlds + (ks - C::NQR) * 1024 +
+                                                           lane * 16);
+          };
+          // software pipeline: the K chunk (and LDS Q fragment) of step ks+2
+          // is in flight while step ks runs on the matrix core
           bf16x8 k0 = kread(0), k1 = kread(1);
+          bf16x8 q0 = {}, q1 = {};
+          if (C::NQR == 0) q0 = qread(0);
+          if (C::NQR <= 1) q1 = qread(1);
 #pragma unroll
           for (int ks = 0; ks < C::NKS; ++ks) {
-            bf16x8 k2 = k1;
-            if (ks + 2 < C::NKS) k2 = kread(ks + 2);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s, 0, 0, 0);
+            bf16x8 k2 = k1, q2 = q1;
+            if (ks + 2 < C::NKS) {
+              k2 = kread(ks + 2);
+              if (ks + 2 >= C::NQR) q2 = qread(ks + 2);
+            }
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ks < C::NQR ? qf[ks < C::NQR ? ks : 0] : q0,
+                                                        s, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             k0 = k1;
             k1 = k2;
+            q0 = q1;
+            q1 = q2;
           }
         }
-        // token of s[r] is 8*(r/4) + 4*(lane/32) + r%4; mask positions past the segment
+        // position of s[r] is 8*(r/4) + 4*(lane/32) + r%4; mask past the segment
         if (nvalid < kTile) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -377,51 +470,53 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
             (f32x8){pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]}, bf16x8);
         const bf16x8 p1 = __builtin_convertvector(
             (f32x8){pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]}, bf16x8);
-        // the running sum adds the bf16 weights the MFMA uses, so that o stays
-        // an exact convex combination of V rows with those weights
+        // the running sum that normalises o adds the bf16 weights the MFMA
+        // uses, so o is an exact convex combination of V rows with them
         {
-          const f32x8 r0 = __builtin_convertvector(p0, f32x8);
-          const f32x8 r1 = __builtin_convertvector(p1, f32x8);
-          const f32x8 r01 = r0 + r1;
+          const f32x8 r01 = __builtin_convertvector(p0, f32x8) + __builtin_convertvector(p1, f32x8);
           lr_part += ((r01[0] + r01[1]) + (r01[2] + r01[3])) + ((r01[4] + r01[5]) + (r01[6] + r01[7]));
         }
         // ---- O^T[v, head] += V^T P^T, V = leading DV columns of the tile
         {
-          auto vread = [&](int st) __attribute__((always_inline)) {
-            const int vb = st >> 1, kk = st & 1;
-            const LDS_AS uint8_t* vt = (const LDS_AS uint8_t*)tile + vb * 2048 + kk * 256;
-            const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (LDS_AS bf16x4*)(vt + v_off0));
-            const bf16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (LDS_AS bf16x4*)(vt + v_off1));
-            return bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-          };
+          const uint32_t vbase0 = (uint32_t)(uintptr_t)tile + v_off0;
+          const uint32_t vbase1 = (uint32_t)(uintptr_t)tile + v_off1;
           constexpr int NST = 2 * C::NVB;
-          bf16x8 a0 = vread(0), a1 = vread(1);
-#pragma unroll
-          for (int st = 0; st < NST; ++st) {
-            bf16x8 a2 = a1;
-            if (st + 2 < NST) a2 = vread(st + 2);
-            oacc[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, (st & 1) ? p1 : p0,
-                                                                  oacc[st >> 1], 0, 0, 0);
+          // fragment of step st: v-block st/2, positions 16*(st%2) .. +15
+          auto vread = [&](auto stc) __attribute__((always_inline)) {
+            constexpr int st = decltype(stc)::value;
+            constexpr int off = ((st & 1) * C::NKQ + (st >> 1)) * 1024;
+            const u32x2 lo = ds_read_tr16_asm<off>(vbase0);
+            const u32x2 hi = ds_read_tr16_asm<off>(vbase1);
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+          };
+          u32x4 a0 = vread(std::integral_constant<int, 0>{});
+          u32x4 a1 = vread(std::integral_constant<int, 1>{});
+          static_for<NST>([&](auto stc) __attribute__((always_inline)) {
+            constexpr int st = decltype(stc)::value;
+            u32x4 a2 = a1;
+            if constexpr (st + 2 < NST) a2 = vread(std::integral_constant<int, st + 2>{});
+            // reads issued after step st's pair: those of st+1 and st+2
+            constexpr int later = 2 * ((st + 2 < NST ? st + 2 : NST - 1) - st);
+            lds_wait<later>(a0);
+            oacc[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, a0), (st & 1) ? p1 : p0, oacc[st >> 1], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             a0 = a1;
             a1 = a2;
-          }
+          });
         }
       } else {
-        // ---- S^T over two 16-token halves x 16 heads
+        // ---- S^T over two 16-position halves x 16 heads
         f32x4 s0 = {}, s1 = {};
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
-          const bf16x8 k0 = *reinterpret_cast<const LDS_AS bf16x8*>(
-              (const LDS_AS uint8_t*)tile + ks * 1024 + qk_off_e);
+          const bf16x8 k0 = *reinterpret_cast<const LDS_AS bf16x8*>(tile + ks * 1024 + qk_off_e);
           const bf16x8 k1 = *reinterpret_cast<const LDS_AS bf16x8*>(
-              (const LDS_AS uint8_t*)tile + (C::NKS + ks) * 1024 + qk_off_e);
+              tile + (C::NKQ + ks) * 1024 + qk_off_e);
           s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], s0, 0, 0, 0);
           s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks], s1, 0, 0, 0);
         }
-        // token of s_th[r] is 16*th + 4*(lane/16) + r
+        // position of s_th[r] is 16*th + 4*(lane/16) + r
         if (nvalid < kTile) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -436,7 +531,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
         mt = max_halves(mt) * p.score_log2;
         const float m_new = fmaxf(m_run, mt);
         if (i == 0) {
-          m_run = m_new;  // nothing accumulated yet: no rescale
+          m_run = m_new;
         } else if (__builtin_amdgcn_ballot_w64(m_new > m_run + kTau)) {
           const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
           m_run = m_new;
@@ -457,15 +552,31 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           const f32x8 r = __builtin_convertvector(pb, f32x8);
           lr_part += ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
         }
-#pragma unroll
-        for (int vb = 0; vb < C::NVB; ++vb) {
-          const LDS_AS uint8_t* vt =
-              (const LDS_AS uint8_t*)tile + (vb >> 1) * 1024 + (vb & 1) * 512;
-          const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vt + v_off0));
-          const bf16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (LDS_AS bf16x4*)(vt + C::NKS * 1024 + v_off1));
-          const bf16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-          oacc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, oacc[vb], 0, 0, 0);
+        {
+          const uint32_t vbase0 = (uint32_t)(uintptr_t)tile + v_off0;
+          const uint32_t vbase1 = (uint32_t)(uintptr_t)tile + v_off1;
+          auto vread = [&](auto vbc) __attribute__((always_inline)) {
+            constexpr int vb = decltype(vbc)::value;
+            constexpr int off = (vb >> 1) * 1024;
+            const uint32_t base = (vb & 1) ? vbase1 : vbase0;
+            const u32x2 lo = ds_read_tr16_asm<off>(base);
+            const u32x2 hi = ds_read_tr16_asm<off + C::NKQ * 1024>(base);
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+          };
+          u32x4 a0 = vread(std::integral_constant<int, 0>{});
+          u32x4 a1 = vread(std::integral_constant<int, 1>{});
+          static_for<C::NVB>([&](auto vbc) __attribute__((always_inline)) {
+            constexpr int vb = decltype(vbc)::value;
+            u32x4 a2 = a1;
+            if constexpr (vb + 2 < C::NVB) a2 = vread(std::integral_constant<int, vb + 2>{});
+            constexpr int later = 2 * ((vb + 2 < C::NVB ? vb + 2 : C::NVB - 1) - vb);
+            lds_wait<later>(a0);
+            oacc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), pb,
+                                                               oacc[vb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            a0 = a1;
+            a1 = a2;
+          });
         }
       }
     }
@@ -483,50 +594,38 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     const float lse_v = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
     const int hl = HPW == 32 ? (lane & 31) : (lane & 15);
     const int h = h0 + hl;
-    const bool lse_writer = HPW == 32 ? (lane < 32) : (lane < 16);
-    if (final_out) {
-      const size_t obase = ((size_t)b * H + h) * DV;
+    // final results go to o (bf16 or fp32), partials to the fp32 workspace
+    const bool out16 = final_out && !p.o_f32;
+    float* dst32 = final_out ? reinterpret_cast<float*>(p.o) : p.ws_o;
+    const size_t row = final_out ? (size_t)b * H + h : (size_t)slot * H + h;
 #pragma unroll
-      for (int vb = 0; vb < C::NVB; ++vb) {
+    for (int vb = 0; vb < C::NVB; ++vb) {
+#pragma unroll
+      for (int g4 = 0; g4 < (HPW == 32 ? 4 : 1); ++g4) {
+        int v;
+        f32x4 val;
         if constexpr (HPW == 32) {
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int v = 32 * vb + 8 * g4 + 4 * (lane >> 5);
-            f32x4 val = {oacc[vb][4 * g4] * inv, oacc[vb][4 * g4 + 1] * inv,
-                         oacc[vb][4 * g4 + 2] * inv, oacc[vb][4 * g4 + 3] * inv};
-            store_out4(p.o, p.o_f32, obase + v, val);
-          }
+          v = 32 * vb + 8 * g4 + 4 * (lane >> 5);
+          val = f32x4{oacc[vb][4 * g4], oacc[vb][4 * g4 + 1], oacc[vb][4 * g4 + 2],
+                      oacc[vb][4 * g4 + 3]} * inv;
         } else {
-          const int v = 16 * vb + 4 * (lane >> 4);
-          f32x4 val = oacc[vb] * inv;
-          store_out4(p.o, p.o_f32, obase + v, val);
+          v = 16 * vb + 4 * (lane >> 4);
+          val = oacc[vb] * inv;
         }
+        if (out16)
+          *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(p.o) + row * DV + v) =
+              __builtin_convertvector(val, bf16x4);
+        else
+          *reinterpret_cast<f32x4*>(dst32 + row * DV + v) = val;
       }
-      if (lse_writer) p.lse[(size_t)b * H + h] = lse_v;
-    } else {
-      float* wo = p.ws_o + ((size_t)slot * H + h) * DV;
-#pragma unroll
-      for (int vb = 0; vb < C::NVB; ++vb) {
-        if constexpr (HPW == 32) {
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int v = 32 * vb + 8 * g4 + 4 * (lane >> 5);
-            f32x4 val = {oacc[vb][4 * g4] * inv, oacc[vb][4 * g4 + 1] * inv,
-                         oacc[vb][4 * g4 + 2] * inv, oacc[vb][4 * g4 + 3] * inv};
-            *reinterpret_cast<f32x4*>(wo + v) = val;
-          }
-        } else {
-          const int v = 16 * vb + 4 * (lane >> 4);
-          *reinterpret_cast<f32x4*>(wo + v) = oacc[vb] * inv;
-        }
-      }
-      if (lse_writer) p.ws_lse[(size_t)slot * H + h] = lse_v;
     }
+    if (HPW == 32 ? (lane < 32) : (lane < 16)) (final_out ? p.lse : p.ws_lse)[row] = lse_v;
   };
 
-  // ---------------- enumerate this unit's segments (one call site of process)
-  int b, ts, te, slot;
-  bool fin;
+  // ---------------- enumerate this unit's segments; process has one call site
+  int b = 0, ts = 0, te = 0, slot = 0;
+  bool fin = false;
+  int64_t st = 0, a0 = 0, a1 = 0;  // balanced mode: tile cursor and unit range
   if (p.split_mode == 0) {
     const int S = p.num_splits;
     b = unit / S;
@@ -534,8 +633,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     const int n = p.seq_lens[b];
     if (n <= 0) {
       if (s == 0) {  // empty sequence: o = 0, lse = -inf
-        const int hl = HPW == 32 ? (lane & 31) : (lane & 15);
-        const int h = h0 + hl;
+        const int h = h0 + (HPW == 32 ? (lane & 31) : (lane & 15));
         const size_t obase = ((size_t)b * H + h) * DV;
         constexpr int per_lane = DV * HPW / 64;
         const int part = HPW == 32 ? (lane >> 5) : (lane >> 4);
@@ -551,41 +649,45 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     te = min(ts + Cb, n);
     fin = (n + Cb - 1) / Cb == 1;
     slot = b * S + s;
-    process(b, ts, te, fin, slot);
-    return;
-  }
-
-  // balanced: the unit covers global tiles [a0, a1) of the batch's tile stream
-  const int U = p.num_splits;
-  const int64_t TT = total_tiles(p.seq_lens, p.batch, lane);
-  if (TT == 0) return;
-  const int64_t a0 = (int64_t)unit * TT / U;
-  const int64_t a1 = (int64_t)(unit + 1) * TT / U;
-  if (a0 >= a1) return;
-  // first sequence whose tiles reach past a0, and its first global tile
-  int64_t st = 0;
-  b = 0;
-  for (int c0 = 0; c0 < p.batch; c0 += 64) {
-    const int bl = c0 + lane;
-    const int ntl = bl < p.batch ? tiles_of(p.seq_lens[bl]) : 0;
-    const int incl = wave_incl_scan(ntl, lane);
-    const uint64_t past = __builtin_amdgcn_ballot_w64(bl < p.batch && st + incl > a0);
-    if (past) {
-      const int k = __builtin_ctzll(past);
-      b = c0 + k;
-      st += __shfl(incl - ntl, k, 64);
-      break;
+  } else {
+    // the unit covers global tiles [a0, a1) of the batch's tile stream
+    const int U = p.num_splits;
+    const int64_t TT = uniform64(total_tiles(p.seq_lens, p.batch, lane));
+    if (TT == 0) return;
+    a0 = (int64_t)unit * TT / U;
+    a1 = (int64_t)(unit + 1) * TT / U;
+    if (a0 >= a1) return;
+    // first sequence whose tiles reach past a0, and its first global tile
+    for (int c0 = 0; c0 < p.batch; c0 += 64) {
+      const int bl = c0 + lane;
+      const int ntl = bl < p.batch ? tiles_of(p.seq_lens[bl]) : 0;
+      const int incl = wave_incl_scan(ntl, lane);
+      const uint64_t past = __builtin_amdgcn_ballot_w64(bl < p.batch && st + incl > a0);
+      if (past) {
+        const int k = __builtin_ctzll(past);
+        b = c0 + k;
+        st += __shfl(incl - ntl, k, 64);
+        break;
+      }
+      st += __shfl(incl, 63, 64);
     }
-    st += __shfl(incl, 63, 64);
+    b = uniform(b);
+    st = uniform64(st);
   }
-  b = uniform(b);
   for (;;) {
-    const int n = p.seq_lens[b];
-    const int nt = tiles_of(n);
-    const int64_t lo = (a0 > st ? a0 : st) - st;
-    const int64_t hi = (a1 < st + nt ? a1 : st + nt) - st;
-    if (hi > lo) process(b, (int)lo * kTile, min((int)hi * kTile, n), lo == 0 && hi == nt, unit + b);
-    st += nt;
+    if (p.split_mode != 0) {
+      const int n = p.seq_lens[b];
+      const int nt = tiles_of(n);
+      const int64_t lo = (a0 > st ? a0 : st) - st;
+      const int64_t hi = (a1 < st + nt ? a1 : st + nt) - st;
+      ts = (int)lo * kTile;
+      te = hi > lo ? min((int)hi * kTile, n) : ts;
+      fin = lo == 0 && hi == nt;
+      slot = unit + b;
+      st += nt;
+    }
+    if (te > ts) process(b, ts, te, fin, slot);
+    if (p.split_mode == 0) break;
     ++b;
     if (b >= p.batch || st >= a1) break;
   }
@@ -703,7 +805,7 @@ int launch_stage1_for(const HeadTiling& ht, const Stage1Params& sp, int grid, hi
   // ring depth: as deep as LDS and the 6-bit vmcnt allow
   if (ht.heads_per_wave == 32) {
     switch (ht.waves) {
-      case 4: return launch_stage1<32, 4, D, DV, 4>(sp, grid, st);
+      case 4: return launch_stage1<32, 4, D, DV, (D == 576 ? 3 : 4)>(sp, grid, st);
       case 2: return launch_stage1<32, 2, D, DV, (D == 576 ? 2 : 4)>(sp, grid, st);
       default: return launch_stage1<32, 1, D, DV, (D == 576 ? 2 : 4)>(sp, grid, st);
     }
@@ -718,7 +820,7 @@ int launch_stage1_for(const HeadTiling& ht, const Stage1Params& sp, int grid, hi
 
 }  // namespace
 
-int launch_decode(const DecodeArgs& a, void* stream) {
+int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const HeadTiling ht = head_tiling(a.heads);
 
@@ -744,14 +846,14 @@ int launch_decode(const DecodeArgs& a, void* stream) {
 
   const int units = a.split_mode == 0 ? a.batch * a.num_splits : a.num_splits;
   const int grid1 = (units + 7) / 8 * 8 * ht.head_chunks;
-  int err;
   if (a.kv_fp8) return (int)hipErrorInvalidValue;  // fp8 kernels: not built yet
-  if (a.head_size == 576) err = launch_stage1_for<576, 512>(ht, sp, grid1, st);
-  else err = launch_stage1_for<320, 256>(ht, sp, grid1, st);
-  if (err) return err;
-
+  if (stages & kStage1) {
+    const int err = a.head_size == 576 ? launch_stage1_for<576, 512>(ht, sp, grid1, st)
+                                       : launch_stage1_for<320, 256>(ht, sp, grid1, st);
+    if (err) return err;
+  }
   const bool merge = a.split_mode == 1 || a.num_splits > 1;
-  if (!merge) return 0;
+  if (!merge || !(stages & kStage2)) return 0;
   Stage2Params s2;
   s2.seq_lens = a.seq_lens;
   s2.ws_o = a.ws_o;
