@@ -33,7 +33,7 @@ def compile_command(out: str = LIB_PATH) -> list:
         f"-I{INCLUDE}", f"-I{CSRC}",
         # packed fp32 VALU ops stay disabled in every HIP translation unit
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wno-unused-command-line-argument",
+        "-Wno-unused-command-line-argument", "-Wl,--no-undefined",
         *SOURCES, "-o", out,
     ]
 

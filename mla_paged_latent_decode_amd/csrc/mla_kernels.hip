@@ -32,23 +32,13 @@ namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// Scalar (SMEM) read of one int32 at byte `offset` of the buffer `rsrc`,
-// waited for in place.  The block-table reads go through the scalar cache and
-// lgkmcnt: issued as a compiler intrinsic, the compiler would first drain
-// every in-flight tile load (vmcnt(0)) in case the load alias them, which
-// serialises the HBM->LDS ring; the asm form has no such wait.  (A read
-// only; nothing here writes through the scalar cache.)
-__device__ __forceinline__ int sload_i32(i32x4 rsrc, int offset) {
-  int v;
-  asm volatile("s_buffer_load_dword %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
-               : "=s"(v) : "s"(rsrc), "s"(offset));
-  return v;
-}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
@@ -223,7 +213,7 @@ struct Cfg {
   // With 32 heads per wave and D = 576, the O accumulators (256 registers)
   // and all 36 Q fragments (144) leave too few registers for the rest of the
   // loop; the last QLDS k-steps of Q then live in LDS (1 KB per step/wave).
-  static constexpr int QLDS = (HPW == 32 && D == 576) ? 12 : 0;
+  static constexpr int QLDS = (HPW == 32 && D == 576) ? (NBUF >= 4 ? 4 : 12) : 0;
   static constexpr int NQR = NKS - QLDS;                   // Q k-steps held in VGPRs
   static constexpr int QLDS_BYTES = W * QLDS * 1024;
   static constexpr int LPW = NBLK / W;                     // DMA ops per wave per tile
@@ -299,40 +289,58 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   // ---------------- one segment [ts, te) of sequence b
   auto process = [&](int b, int ts, int te, bool final_out, int slot) __attribute__((always_inline)) {
     const int n_tiles = (te - ts + kTile - 1) / kTile;
-    i32x4 bt_rsrc;  // the sequence's block-table row
-    {
-      const uint64_t a = reinterpret_cast<uint64_t>(p.block_table + (int64_t)b * p.bt_stride);
-      bt_rsrc[0] = uniform((int)(uint32_t)a);
-      bt_rsrc[1] = uniform((int)(uint32_t)(a >> 32));
-      bt_rsrc[2] = p.bt_stride * 4;
-      bt_rsrc[3] = 0x00020000;
-    }
     // page cursor of the next 16-position half to load
     int cur_lb = ts / P;
     int cur_off = ts - cur_lb * P;
     int cur_tok = ts;
+    // Block-table window: lane k holds the page of logical block win_lb + k.
+    // One vector load per 64 pages; a page is then read with v_readlane.
+    const int32_t* bt_row = p.block_table + (int64_t)b * p.bt_stride;
+    const int lb_end = (te - 1) / P + 1;  // blocks this segment reads
+    int win_lb = cur_lb;
+    int win = 0;
+    auto load_window = [&]() __attribute__((always_inline)) {
+      const int k = win_lb + lane;
+      win = k < lb_end ? bt_row[k] : 0;
+    };
+    load_window();
 
     // Issue the loads of the next tile (ring slot i % NBUF).  Each 16-row
     // half lies in one page (P and 16-position boundaries are multiples of
     // 16); a buffer resource sized to the valid rows makes the loads of
     // positions past the segment return zeros, so those LDS rows hold zeros
     // and never the (possibly NaN) contents of unreferenced slots.
-    auto issue = [&](int i) __attribute__((always_inline)) {
-      uint8_t* dst = ring + (i % NBUF) * C::TILE_BYTES;
-      __amdgpu_buffer_rsrc_t rs[2];
+    struct TileLoad {  // plain fields: the buffer resources are built at each use
+      uint64_t base[2];
+      int bytes[2];
+      uint8_t* dst;
+    };
+    // Resources of the next tile to load (ring slot i % NBUF); advances the cursor.
+    auto prepare = [&](int i) __attribute__((always_inline)) {
+      TileLoad tl;
+      tl.dst = ring + (i % NBUF) * C::TILE_BYTES;
 #pragma unroll
       for (int th = 0; th < 2; ++th) {
         const int nv = uniform(max(0, min(16, te - cur_tok)));
         uint64_t base = reinterpret_cast<uint64_t>(p.kv);
         if (nv > 0) {
-          const int64_t page = sload_i32(bt_rsrc, cur_lb * 4);
+          // The window load is read inside its own branch, so that the wait
+          // for it stays there: a wait at the join would drain the ring.
+          int64_t page;
+          if (cur_lb - win_lb >= 64) {  // uniform: move the window (once per 64 pages)
+            win_lb = cur_lb;
+            load_window();
+            page = __builtin_amdgcn_readlane(win, 0);
+          } else {
+            page = __builtin_amdgcn_readlane(win, cur_lb - win_lb);
+          }
           base += (uint64_t)((page * P + cur_off) * (int64_t)C::ROW_BYTES);
         }
         // every field wave-uniform, so the resource lives in SGPRs
         base = ((uint64_t)(uint32_t)uniform((int)(base >> 32)) << 32) |
                (uint32_t)uniform((int)(uint32_t)base);
-        rs[th] = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nv * C::ROW_BYTES,
-                                                   0x00020000);
+        tl.base[th] = base;
+        tl.bytes[th] = nv * C::ROW_BYTES;
         cur_tok += 16;
         cur_off += 16;
         if (cur_off == P) {
@@ -340,15 +348,23 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           ++cur_lb;
         }
       }
+      return tl;
+    };
+    // The k-th of this wave's LPW block loads of a prepared tile.
+    auto dma = [&](const TileLoad& tl, int k) __attribute__((always_inline)) {
+      const int j = wave + k * W;  // block index
+      const int th = j >= C::NKQ ? 1 : 0;
+      const int kq = j - th * C::NKQ;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(th ? tl.base[1] : tl.base[0]), (short)0, th ? tl.bytes[1] : tl.bytes[0],
+          0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(tl.dst + j * 1024), 16,
+                                               dma_voff + 64 * kq, 0, 0, 0);
+    };
+    auto issue = [&](int i) __attribute__((always_inline)) {
+      const TileLoad tl = prepare(i);
 #pragma unroll
-      for (int k = 0; k < C::LPW; ++k) {
-        const int j = wave + k * W;  // block index
-        const int th = j >= C::NKQ ? 1 : 0;
-        const int kq = j - th * C::NKQ;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(th ? rs[1] : rs[0],
-                                                 (LDS_AS void*)(dst + j * 1024), 16,
-                                                 dma_voff + 64 * kq, 0, 0, 0);
-      }
+      for (int k = 0; k < C::LPW; ++k) dma(tl, k);
     };
 
     // Q fragments of this wave's heads (B operand of S^T = K Q^T): the first
@@ -380,6 +396,199 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
 #pragma unroll
     for (int vb = 0; vb < C::NVB; ++vb) oacc[vb] = acc_t{};
 
+    if constexpr (HPW == 32 && NBUF >= 3) {
+      // ---- software-pipelined loop (32-head waves).  Iteration j runs the
+      // softmax of tile j interleaved with the QK^T MFMAs of tile j+1, then
+      // the PV MFMAs of tile j; the loads of tile j+NBUF-1 are spread over
+      // the QK^T steps.  The ring holds tiles j (V), j+1 (K) and NBUF-2
+      // tiles in flight.  Past the segment, loads are issued with an empty
+      // resource (they write zeros into a free slot), so every iteration
+      // issues the same number of loads and the waits are constants.
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int i = 0; i < NBUF - 1; ++i) issue(i);
+      wait_vmcnt<(NBUF - 2) * C::LPW>();
+      __builtin_amdgcn_s_barrier();
+
+      auto kread = [&](const LDS_AS uint8_t* t, int ks) __attribute__((always_inline)) {
+        return *reinterpret_cast<const LDS_AS bf16x8*>(t + (ks >> 1) * 1024 +
+                                                       ((ks & 1) ? qk_off_o : qk_off_e));
+      };
+      auto qread = [&](int ks) __attribute__((always_inline)) {
+        return *reinterpret_cast<const LDS_AS bf16x8*>(qlds + (ks - C::NQR) * 1024 + lane * 16);
+      };
+      // S^T of one tile on two accumulator chains (even / odd k-steps, summed
+      // by the softmax); hook(k-step) runs right after each MFMA is issued.
+      struct S2 {
+        f32x16 e, o;
+      };
+      auto qk = [&](const LDS_AS uint8_t* t, auto&& hook) __attribute__((always_inline)) {
+        f32x16 se = {}, so = {};
+        bf16x8 k0 = kread(t, 0), k1 = kread(t, 1);
+        bf16x8 q0 = {}, q1 = {};
+        if constexpr (C::NQR == 0) q0 = qread(0);
+        if constexpr (C::NQR <= 1) q1 = qread(1);
+        static_for<C::NKS>([&](auto ksc) __attribute__((always_inline)) {
+          constexpr int ks = decltype(ksc)::value;
+          bf16x8 k2 = k1, q2 = q1;
+          if constexpr (ks + 2 < C::NKS) {
+            k2 = kread(t, ks + 2);
+            if constexpr (ks + 2 >= C::NQR) q2 = qread(ks + 2);
+          }
+          bf16x8 qv;
+          if constexpr (ks < C::NQR) qv = qf[ks];
+          else qv = q0;
+          if constexpr (ks & 1) so = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qv, so, 0, 0, 0);
+          else se = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qv, se, 0, 0, 0);
+          hook(ksc);
+          __builtin_amdgcn_sched_barrier(0);
+          k0 = k1;
+          k1 = k2;
+          q0 = q1;
+          q1 = q2;
+        });
+        return S2{se, so};
+      };
+      auto no_hook = [&](auto) __attribute__((always_inline)) {};
+
+      f32x16 s_cur;  // scores of the tile whose softmax runs next
+      {
+        const S2 s0 = qk((const LDS_AS uint8_t*)ring, no_hook);  // S^T of tile 0
+        s_cur = s0.e + s0.o;
+      }
+      for (int j = 0; j < n_tiles; ++j) {
+        wait_vmcnt<(NBUF - 3) * C::LPW>();  // tile j+1 is in LDS
+        __builtin_amdgcn_s_barrier();       // ... for every wave; tile j-1's slot is free
+        const LDS_AS uint8_t* tcur = (const LDS_AS uint8_t*)ring + (j % NBUF) * C::TILE_BYTES;
+        const LDS_AS uint8_t* tnext =
+            (const LDS_AS uint8_t*)ring + ((j + 1) % NBUF) * C::TILE_BYTES;
+        const int nvalid = min(kTile, te - (ts + j * kTile));
+        const TileLoad tl = prepare(j + NBUF - 1);
+
+        float mt = -INFINITY, alpha = 1.f;
+        bool rescale = false;
+        bf16x8 p0, p1;
+        f32x16& sv = s_cur;  // scores of tile j, turned into weights in place
+        // Softmax of tile j, spread over the QK^T steps of tile j+1 at a few
+        // VALU instructions per MFMA, so that the matrix core stays fed:
+        //   0-3        running row max
+        //   4          mask past the segment (last tile only)
+        //   5          max across the two half-waves, new running max, rescale test
+        //   6 .. 6+E   the 16 weights: exp2, sums, bf16 packing of each pair
+        //   .. +L      sum of the bf16 weights (normalises o)
+        constexpr int E = C::NKS - 8 < 16 ? C::NKS - 8 : 16;
+        constexpr int L = C::NKS - 6 - E < 8 ? C::NKS - 6 - E : 8;
+        static_assert(E >= 1 && L >= 1, "too few QK^T steps to hide the softmax");
+        auto hook = [&](auto ksc) __attribute__((always_inline)) {
+          constexpr int ks = decltype(ksc)::value;
+          if constexpr (ks < 4) {
+            mt = fmaxf(mt, fmaxf(fmaxf(sv[4 * ks], sv[4 * ks + 1]), fmaxf(sv[4 * ks + 2], sv[4 * ks + 3])));
+          } else if constexpr (ks == 4) {
+            // position of sv[r] is 8*(r/4) + 4*(lane/32) + r%4
+            if (nvalid < kTile) {
+              mt = -INFINITY;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int t = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (t >= nvalid) sv[r] = -INFINITY;
+                mt = fmaxf(mt, sv[r]);
+              }
+            }
+          } else if constexpr (ks == 5) {
+            mt = max_halves(mt) * p.score_log2;
+            const float m_new = fmaxf(m_run, mt);
+            // the accumulator rescale itself waits until after the QK^T
+            // stream (PV of this tile comes after it)
+            if (j == 0) {
+              m_run = m_new;  // nothing accumulated yet: no rescale
+            } else if (__builtin_amdgcn_ballot_w64(m_new > m_run + kTau)) {
+              alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+              rescale = true;
+              m_run = m_new;
+              l_part *= alpha;
+              lr_part *= alpha;
+            }
+          } else {
+            static_for<16>([&](auto rc) __attribute__((always_inline)) {
+              constexpr int r = decltype(rc)::value;
+              if constexpr (6 + r * E / 16 == ks) {
+                sv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], p.score_log2, -m_run));
+                l_part += sv[r];
+                if constexpr (r & 1) {
+                  const bf16x2 pk = __builtin_convertvector((f32x2){sv[r - 1], sv[r]}, bf16x2);
+                  if constexpr (r < 8) {
+                    p0[r - 1] = pk[0];
+                    p0[r] = pk[1];
+                  } else {
+                    p1[r - 9] = pk[0];
+                    p1[r - 8] = pk[1];
+                  }
+                }
+              }
+            });
+            // the sum that normalises o adds the bf16 weights the MFMA uses,
+            // so o is an exact convex combination of V rows with them
+            static_for<8>([&](auto qc) __attribute__((always_inline)) {
+              constexpr int q = decltype(qc)::value;
+              if constexpr (6 + E + q * L / 8 == ks) {
+                const bf16x8& pp = q < 4 ? p0 : p1;
+                lr_part += (float)pp[(2 * q) & 7] + (float)pp[((2 * q) & 7) + 1];
+              }
+            });
+          }
+        };
+        S2 s_next = {};
+        if (j + 1 < n_tiles) s_next = qk(tnext, hook);
+        else static_for<C::NKS>(hook);
+        if (rescale) {  // uniform, rare: the running max moved by more than kTau
+#pragma unroll
+          for (int vb = 0; vb < C::NVB; ++vb) scale_acc(oacc[vb], alpha);
+        }
+
+        // ---- O^T[v, head] += V^T P^T of tile j; k-half outer so that
+        // consecutive MFMAs accumulate into different blocks
+        {
+          const uint32_t vbase0 = (uint32_t)(uintptr_t)tcur + v_off0;
+          const uint32_t vbase1 = (uint32_t)(uintptr_t)tcur + v_off1;
+          constexpr int NST = 2 * C::NVB;
+          auto vread = [&](auto stc) __attribute__((always_inline)) {
+            constexpr int st = decltype(stc)::value;
+            constexpr int kk = st / C::NVB, vb = st % C::NVB;
+            constexpr int off = (kk * C::NKQ + vb) * 1024;
+            const u32x2 lo = ds_read_tr16_asm<off>(vbase0);
+            const u32x2 hi = ds_read_tr16_asm<off>(vbase1);
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+          };
+          u32x4 a0 = vread(std::integral_constant<int, 0>{});
+          u32x4 a1 = vread(std::integral_constant<int, 1>{});
+          u32x4 a2 = vread(std::integral_constant<int, 2>{});
+          static_for<NST>([&](auto stc) __attribute__((always_inline)) {
+            constexpr int st = decltype(stc)::value;
+            constexpr int kk = st / C::NVB, vb = st % C::NVB;
+            u32x4 a3 = a2;
+            if constexpr (st + 3 < NST) a3 = vread(std::integral_constant<int, st + 3>{});
+            constexpr int later = 2 * ((st + 3 < NST ? st + 3 : NST - 1) - st);
+            lds_wait<later>(a0);
+            oacc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0),
+                                                              kk ? p1 : p0, oacc[vb], 0, 0, 0);
+            // scores of tile j+1: sum of its two QK^T chains
+            if constexpr (st < 4) {
+#pragma unroll
+              for (int r = 4 * st; r < 4 * st + 4; ++r) s_cur[r] = s_next.e[r] + s_next.o[r];
+            }
+            // loads of tile j+NBUF-1, spread over the PV MFMAs
+#pragma unroll
+            for (int k = 0; k < C::LPW; ++k)
+              if ((k + 1) * NST / C::LPW - 1 == st) dma(tl, k);
+            __builtin_amdgcn_sched_barrier(0);
+            a0 = a1;
+            a1 = a2;
+            a2 = a3;
+          });
+        }
+      }
+    } else {
     // Drain this wave's earlier stores and loads once, so that no wait for
     // them lands between the ring loads below, then make sure every wave is
     // done with the ring of a previous segment.
@@ -395,7 +604,18 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       else if (ahead == 1) wait_vmcnt<(NBUF >= 3 ? 1 : 0) * C::LPW>();
       else wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
-      if (i + NBUF - 1 < n_tiles) issue(i + NBUF - 1);
+      // The next tile's loads are spread over this tile's QK^T MFMAs: each
+      // load instruction can hold the wave at issue while the vector-memory
+      // queue drains, which the matrix core then overlaps.
+      const bool more = i + NBUF - 1 < n_tiles;
+      TileLoad tl;
+      if (more) tl = prepare(i + NBUF - 1);
+      auto dma_at = [&](int ks) __attribute__((always_inline)) {
+        // load k goes after k-step floor(k * NKS / LPW)
+#pragma unroll
+        for (int k = 0; k < C::LPW; ++k)
+          if ((k * C::NKS) / C::LPW == ks && more) dma(tl, k);
+      };
 
       const LDS_AS uint8_t* tile = (const LDS_AS uint8_t*)ring + (i % NBUF) * C::TILE_BYTES;
       const int nvalid = min(kTile, te - (ts + i * kTile));
@@ -427,6 +647,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
             }
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ks < C::NQR ? qf[ks < C::NQR ? ks : 0] : q0,
                                                         s, 0, 0, 0);
+            dma_at(ks);
             __builtin_amdgcn_sched_barrier(0);
             k0 = k1;
             k1 = k2;
@@ -515,6 +736,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
               tile + (C::NKQ + ks) * 1024 + qk_off_e);
           s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], s0, 0, 0, 0);
           s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks], s1, 0, 0, 0);
+          dma_at(ks);
         }
         // position of s_th[r] is 16*th + 4*(lane/16) + r
         if (nvalid < kTile) {
@@ -579,6 +801,8 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           });
         }
       }
+    }
+
     }
 
     // ---- epilogue: o = O / l, lse = ln(2) * (m + log2 l)
@@ -805,8 +1029,8 @@ int launch_stage1_for(const HeadTiling& ht, const Stage1Params& sp, int grid, hi
   // ring depth: as deep as LDS and the 6-bit vmcnt allow
   if (ht.heads_per_wave == 32) {
     switch (ht.waves) {
-      case 4: return launch_stage1<32, 4, D, DV, (D == 576 ? 3 : 4)>(sp, grid, st);
-      case 2: return launch_stage1<32, 2, D, DV, (D == 576 ? 2 : 4)>(sp, grid, st);
+      case 4: return launch_stage1<32, 4, D, DV, 4>(sp, grid, st);
+      case 2: return launch_stage1<32, 2, D, DV, (D == 576 ? 3 : 4)>(sp, grid, st);
       default: return launch_stage1<32, 1, D, DV, (D == 576 ? 2 : 4)>(sp, grid, st);
     }
   } else {
