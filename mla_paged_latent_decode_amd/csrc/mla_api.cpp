@@ -44,14 +44,11 @@ HeadTiling head_tiling(int32_t heads) {
   return t;
 }
 
-// LDS bytes of one stage-1 workgroup (ring depth chosen in mla_kernels.hip).
-static int64_t stage1_lds_bytes(const mla_shape& s) {
+// LDS bytes of one stage-1 workgroup (the same plan the kernel dispatch uses).
+static int64_t stage1_lds(const mla_shape& s) {
   const HeadTiling t = head_tiling(s.num_heads);
-  const int64_t tile = (int64_t)kTile * s.head_size * 2;
-  int nbuf = 4;
-  if (s.head_size == 576) nbuf = t.waves < 4 ? 2 : (t.heads_per_wave == 32 ? 3 : 4);
-  const int64_t qlds = (t.heads_per_wave == 32 && s.head_size == 576) ? t.waves * 12 * 1024 : 0;
-  return nbuf * tile + qlds;
+  return stage1_lds_bytes(t.heads_per_wave, t.waves, s.head_size,
+                          s.kv_dtype == MLA_FP8_E4M3);
 }
 
 }  // namespace mla
@@ -112,7 +109,7 @@ mla_status mla_plan(const mla_shape* shape, int32_t max_seq_len, int64_t total_s
     return MLA_OK;
   }
   const HeadTiling ht = head_tiling(shape->num_heads);
-  int64_t per_cu = (160 * 1024) / stage1_lds_bytes(*shape);
+  int64_t per_cu = kLdsBytes / stage1_lds(*shape);
   if (per_cu < 1) per_cu = 1;
   if (per_cu > 4) per_cu = 4;
   // one workgroup per resident slot, each head chunk counting as its own
@@ -159,7 +156,6 @@ static mla_status decode_stages(const mla_shape* shape, const void* q, const voi
     if (!workspace || workspace_bytes < wl.total) return MLA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return MLA_ERR_ARGUMENT;
   }
-  if (fp8) return MLA_ERR_DTYPE;  // fp8 cache kernels are not part of this build yet
 
   DecodeArgs a;
   a.q = q;

@@ -32,6 +32,33 @@ struct HeadTiling {
 
 HeadTiling head_tiling(int32_t heads);
 
+// LDS plan of one stage-1 workgroup, shared by the planner (mla_api.cpp) and
+// the kernel dispatch (mla_kernels.hip).  A bf16 cache streams straight into
+// a ring of `ring_depth` bf16 tiles (32 positions x D).  An fp8 cache streams
+// into two fp8 staging tiles and is widened to bf16 into a ring of 3 (32-head
+// waves, 4 waves: software-pipelined loop) or 2 tiles.  With 32 heads per
+// wave at D = 576 the last `qlds_steps` 16-wide k-steps of Q live in LDS
+// (1 KB per step and wave), as many as the remaining LDS holds, up to 12.
+constexpr int kLdsBytes = 160 * 1024;
+
+constexpr int stage1_ring_depth(int hpw, int waves, int d, bool fp8) {
+  if (fp8) return (hpw == 32 && waves == 4) ? 3 : 2;
+  if (d != 576) return 4;
+  if (hpw == 32) return waves == 4 ? 4 : (waves == 2 ? 3 : 2);
+  return waves == 4 ? 4 : 2;
+}
+constexpr int stage1_staging_bytes(int d, bool fp8) { return fp8 ? 2 * kTile * d : 0; }
+constexpr int stage1_qlds_steps(int hpw, int waves, int d, bool fp8) {
+  if (!(hpw == 32 && d == 576)) return 0;
+  const int room = (kLdsBytes - stage1_ring_depth(hpw, waves, d, fp8) * kTile * d * 2 -
+                    stage1_staging_bytes(d, fp8)) / (waves * 1024);
+  return room < 12 ? room : 12;
+}
+constexpr int stage1_lds_bytes(int hpw, int waves, int d, bool fp8) {
+  return stage1_ring_depth(hpw, waves, d, fp8) * kTile * d * 2 + stage1_staging_bytes(d, fp8) +
+         stage1_qlds_steps(hpw, waves, d, fp8) * waves * 1024;
+}
+
 struct DecodeArgs {
   const void* q;
   const void* kv;

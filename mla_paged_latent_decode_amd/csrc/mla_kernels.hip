@@ -77,6 +77,14 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// A wave-uniform value the compiler must materialise in an SGPR at this
+// point: per-lane addresses built from it are then formed right before
+// their use instead of being hoisted out of the loop into long-lived VGPRs.
+__device__ __forceinline__ int sgpr_here(int x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
 __device__ __forceinline__ float wave_max_xor(float x, int mask) {
   return fmaxf(x, __shfl_xor(x, mask, 64));
 }
@@ -114,6 +122,66 @@ __device__ __forceinline__ void lds_wait(u32x4& x) {
   static_assert(N >= 0 && N < 16, "lgkmcnt is a 4-bit counter");
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
 }
+
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x2& x) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt is a 4-bit counter");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
+}
+// Plain LDS read / write from asm, for the fp8 widening step: the compiler
+// would otherwise order them after every in-flight tile load (the loads
+// write LDS), and it does not count them, so every use of a read comes after
+// an explicit lds_wait.  The write clobbers memory so that no compiler LDS
+// access moves across it.
+__device__ __forceinline__ u32x2 ds_read_b64_asm(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+__device__ __forceinline__ void ds_write_b128_asm(uint32_t addr, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+// Eight OCP e4m3fn values (one per byte, lowest byte first) to eight bf16.
+// Every e4m3fn value is exactly representable in bf16, so the conversion
+// (scale 1) is exact.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 v) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, true));
+  return r;
+}
+
+// LDS operation schedule of one P V^T pass: step s issues the two
+// transposed V reads of step s+3, then (fp8 caches) the staging read of
+// widened block k at s = 3k, or the write of block k at s = 3k+2, then waits
+// for its own V reads and runs its MFMA.  The functions give how many LDS
+// operations were issued after the one a wait is for, which is the lgkmcnt
+// to wait for (LDS operations complete in order).
+template <int NST, int NCV>
+struct PvSched {
+  static constexpr bool has_r(int s) { return s >= 0 && s % 3 == 0 && s / 3 < NCV; }
+  static constexpr bool has_w(int s) { return s >= 0 && s % 3 == 2 && s / 3 < NCV; }
+  static constexpr int nv(int s) { return s + 3 < NST ? 2 : 0; }
+  static constexpr int ops(int s) { return nv(s) + (has_r(s) ? 1 : 0) + (has_w(s) ? 1 : 0); }
+  // after the V reads of step st (issued in step st-3, or before step 0)
+  static constexpr int after_v(int st) {
+    int n = 0;
+    if (st >= 3) {
+      n += (has_r(st - 3) ? 1 : 0) + (has_w(st - 3) ? 1 : 0);
+      for (int s = st - 2; s <= st; ++s) n += ops(s);
+    } else {
+      n += 2 * (2 - st);
+      for (int s = 0; s <= st; ++s) n += ops(s);
+    }
+    return n;
+  }
+  // after the staging read of block k, at the write of step 3k+2
+  static constexpr int after_r(int k) { return nv(3 * k + 1) + nv(3 * k + 2); }
+  static_assert(NCV == 0 || 3 * NCV - 1 < NST, "widening must end inside the pass");
+};
 
 // Multiply an MFMA accumulator held in AGPRs by s in place.  The "+a"
 // constraints keep the accumulator in the AGPR file, so this (rare) rescale
@@ -205,7 +273,7 @@ __device__ __forceinline__ int64_t total_tiles(const int32_t* seq_lens, int B, i
 
 // ---------------------------------------------------------------- stage 1
 
-template <int HPW, int W, int D, int DV, int NBUF>
+template <int HPW, int W, int D, int DV, int NBUF, bool F8>
 struct Cfg {
   static constexpr int NKQ = D / 32;                       // 32-wide d groups per row
   static constexpr int NBLK = 2 * NKQ;                     // 1 KB LDS blocks per tile
@@ -213,18 +281,33 @@ struct Cfg {
   // With 32 heads per wave and D = 576, the O accumulators (256 registers)
   // and all 36 Q fragments (144) leave too few registers for the rest of the
   // loop; the last QLDS k-steps of Q then live in LDS (1 KB per step/wave).
-  static constexpr int QLDS = (HPW == 32 && D == 576) ? (NBUF >= 4 ? 4 : 12) : 0;
+  static constexpr int QLDS = stage1_qlds_steps(HPW, W, D, F8);
   static constexpr int NQR = NKS - QLDS;                   // Q k-steps held in VGPRs
   static constexpr int QLDS_BYTES = W * QLDS * 1024;
-  static constexpr int LPW = NBLK / W;                     // DMA ops per wave per tile
+  static constexpr int LPW = NBLK / W;                     // bf16 blocks per wave per tile
   static constexpr int TILE_BYTES = NBLK * 1024;
   static constexpr int NVB = HPW == 32 ? DV / 32 : DV / 16;  // PV output blocks
   static constexpr int HEADS_PER_WG = HPW * W;
-  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int SRC_ROW = F8 ? D : 2 * D;           // bytes of one cache row
+  // fp8: a 16-row half tile (16*D contiguous bytes of one page) is copied to
+  // a staging tile with G-byte LDS DMA per lane (consecutive lanes write
+  // consecutive G bytes), G = 16 when every wave then issues the same number
+  // of copies, else 4; bf16: one 16-byte copy per lane and block.
+  static constexpr int G =
+      !F8 ? 16 : ((16 * D) % 1024 == 0 && (2 * 16 * D / 1024) % W == 0) ? 16 : 4;
+  static constexpr int NIH = F8 ? 16 * D / (64 * G) : NKQ;  // DMA copies per half tile
+  static constexpr int NIW = 2 * NIH / W;                   // DMA copies per wave per tile
+  static constexpr int STG_TILE = F8 ? kTile * D : 0;       // fp8 staging tile bytes
+  static constexpr int STG_BYTES = 2 * STG_TILE;
+  // software-pipelined loop (softmax of tile j behind the QK^T of tile j+1)
+  static constexpr bool PIPE = HPW == 32 && (F8 ? W == 4 : NBUF >= 3);
+  static_assert(NBUF == stage1_ring_depth(HPW, W, D, F8), "ring depth");
   static_assert(NBLK * 1024 == kTile * D * 2, "tile bytes");
-  static_assert(NBLK % W == 0, "each wave issues the same number of tile loads");
-  static_assert((NBUF - 1) * LPW <= 63, "outstanding loads must fit the vmcnt counter");
-  static_assert(NBUF * TILE_BYTES + QLDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(NBLK % W == 0, "each wave loads or widens the same number of blocks");
+  static_assert(!F8 || ((16 * D) % (64 * G) == 0 && (2 * NIH) % W == 0), "fp8 copy split");
+  static_assert(F8 ? NIW <= 63 : (NBUF - 1) * LPW <= 63,
+                "outstanding loads must fit the vmcnt counter");
+  static_assert(NBUF * TILE_BYTES + STG_BYTES + QLDS_BYTES <= kLdsBytes, "LDS budget");
   static_assert(D % 32 == 0 && DV % 32 == 0, "");
 };
 
@@ -239,10 +322,13 @@ __device__ __forceinline__ int tile_slot(int t16, int c4) {
   return (t16 ^ (8 * (c4 & 1) + 4 * (c4 >> 1))) + 16 * c4;
 }
 
-template <int HPW, int W, int D, int DV, int NBUF>
+template <int HPW, int W, int D, int DV, int NBUF, bool F8>
 __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
-  using C = Cfg<HPW, W, D, DV, NBUF>;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * C::TILE_BYTES + C::QLDS_BYTES];
+  using C = Cfg<HPW, W, D, DV, NBUF, F8>;
+  // [bf16 ring: NBUF tiles][fp8 staging: 2 tiles][Q k-steps of each wave]
+  __shared__ __attribute__((aligned(1024)))
+  uint8_t ring[NBUF * C::TILE_BYTES + C::STG_BYTES + C::QLDS_BYTES];
+  uint8_t* const stg = ring + NBUF * C::TILE_BYTES;
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -263,7 +349,12 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   // t16 = (l % 16) ^ f(c4); its source offset within the 16-row page run.
   const int dma_c4 = lane >> 4;
   const int dma_voff =
-      ((lane & 15) ^ (8 * (dma_c4 & 1) + 4 * (dma_c4 >> 1))) * C::ROW_BYTES + 16 * dma_c4;
+      ((lane & 15) ^ (8 * (dma_c4 & 1) + 4 * (dma_c4 >> 1))) * C::SRC_ROW + 16 * dma_c4;
+  // fp8 widening: lane l converts chunk c4 = l % 4 of position t16 = l / 4
+  // of a block, read from the row-major staging tile and written to the
+  // chunk's slot of the bf16 tile layout
+  const uint32_t cv_src = (uint32_t)((lane >> 2) * D + 8 * (lane & 3));
+  const uint32_t cv_dst = (uint32_t)(tile_slot(lane >> 2, lane & 3) * 16);
   int qk_off_e, qk_off_o, v_off0, v_off1;
   if constexpr (HPW == 32) {
     // QK A operand: position t = lane % 32, chunk 2*ks + lane / 32
@@ -318,7 +409,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     // Resources of the next tile to load (ring slot i % NBUF); advances the cursor.
     auto prepare = [&](int i) __attribute__((always_inline)) {
       TileLoad tl;
-      tl.dst = ring + (i % NBUF) * C::TILE_BYTES;
+      tl.dst = F8 ? stg + (i & 1) * C::STG_TILE : ring + (i % NBUF) * C::TILE_BYTES;
 #pragma unroll
       for (int th = 0; th < 2; ++th) {
         const int nv = uniform(max(0, min(16, te - cur_tok)));
@@ -334,13 +425,13 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           } else {
             page = __builtin_amdgcn_readlane(win, cur_lb - win_lb);
           }
-          base += (uint64_t)((page * P + cur_off) * (int64_t)C::ROW_BYTES);
+          base += (uint64_t)((page * P + cur_off) * (int64_t)C::SRC_ROW);
         }
         // every field wave-uniform, so the resource lives in SGPRs
         base = ((uint64_t)(uint32_t)uniform((int)(base >> 32)) << 32) |
                (uint32_t)uniform((int)(uint32_t)base);
         tl.base[th] = base;
-        tl.bytes[th] = nv * C::ROW_BYTES;
+        tl.bytes[th] = nv * C::SRC_ROW;
         cur_tok += 16;
         cur_off += 16;
         if (cur_off == P) {
@@ -350,27 +441,67 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       }
       return tl;
     };
-    // The k-th of this wave's LPW block loads of a prepared tile.
+    // The k-th of this wave's NIW copies of a prepared tile.  bf16: block j
+    // of the tile layout, one 16-byte chunk per lane.  fp8: the r-th 64*G
+    // bytes of a half tile into the row-major staging tile.
     auto dma = [&](const TileLoad& tl, int k) __attribute__((always_inline)) {
-      const int j = wave + k * W;  // block index
-      const int th = j >= C::NKQ ? 1 : 0;
-      const int kq = j - th * C::NKQ;
+      const int j = wave + k * W;  // copy index
+      const int th = j >= C::NIH ? 1 : 0;
+      const int r = j - th * C::NIH;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(th ? tl.base[1] : tl.base[0]), (short)0, th ? tl.bytes[1] : tl.bytes[0],
           0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(tl.dst + j * 1024), 16,
-                                               dma_voff + 64 * kq, 0, 0, 0);
+      if constexpr (F8) {
+        LDS_AS void* dst = (LDS_AS void*)(tl.dst + th * 16 * D + r * 64 * C::G);
+        const int voff = C::G * lane + sgpr_here(r * 64 * C::G);
+        // the size operand is spelled as a literal: given as a template
+        // constant, the host pass drops the kernel's launch stub
+        if constexpr (C::G == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, 0, 0, 0);
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, voff, 0, 0, 0);
+      } else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(tl.dst + j * 1024), 16,
+                                                 dma_voff + sgpr_here(64 * r), 0, 0, 0);
     };
     auto issue = [&](int i) __attribute__((always_inline)) {
       const TileLoad tl = prepare(i);
 #pragma unroll
-      for (int k = 0; k < C::LPW; ++k) dma(tl, k);
+      for (int k = 0; k < C::NIW; ++k) dma(tl, k);
+    };
+    // fp8: LDS addresses of the k-th of this wave's LPW widened blocks of
+    // tile x (staging slot x % 2 -> ring slot x % NBUF)
+    auto widen_src = [&](int x, int k) __attribute__((always_inline)) {
+      const int j = wave + k * W;
+      const int th = j >= C::NKQ ? 1 : 0;
+      return cv_src + (uint32_t)sgpr_here((int)(uint32_t)(uintptr_t)stg + (x & 1) * C::STG_TILE +
+                                          th * 16 * D + 32 * (j - th * C::NKQ));
+    };
+    auto widen_dst = [&](int x, int k) __attribute__((always_inline)) {
+      return cv_dst + (uint32_t)sgpr_here((int)(uint32_t)(uintptr_t)ring +
+                                          (x % NBUF) * C::TILE_BYTES + (wave + k * W) * 1024);
+    };
+    // widen all of this wave's blocks of tile x, four reads in flight
+    auto widen_tile = [&](int x) __attribute__((always_inline)) {
+      static_for<(C::LPW + 3) / 4>([&](auto bc) __attribute__((always_inline)) {
+        constexpr int k0 = 4 * decltype(bc)::value;
+        constexpr int nb = C::LPW - k0 < 4 ? C::LPW - k0 : 4;
+        u32x2 v[nb];
+        static_for<nb>([&](auto ic) __attribute__((always_inline)) {
+          v[decltype(ic)::value] = ds_read_b64_asm(widen_src(x, k0 + decltype(ic)::value));
+        });
+        static_for<nb>([&](auto ic) __attribute__((always_inline)) {
+          constexpr int i = decltype(ic)::value;
+          // issued after read i: the other nb-1-i reads and i writes
+          lds_wait<nb - 1>(v[i]);
+          ds_write_b128_asm(widen_dst(x, k0 + i), e4m3x8_to_bf16x8(v[i]));
+        });
+      });
     };
 
     // Q fragments of this wave's heads (B operand of S^T = K Q^T): the first
     // NQR k-steps in VGPRs, the rest in this wave's LDS region (lane-linear)
     bf16x8 qf[C::NQR];
-    LDS_AS uint8_t* qlds = (LDS_AS uint8_t*)ring + NBUF * C::TILE_BYTES + wave * C::QLDS * 1024;
+    LDS_AS uint8_t* qlds =
+        (LDS_AS uint8_t*)ring + NBUF * C::TILE_BYTES + C::STG_BYTES + wave * C::QLDS * 1024;
     {
       const __bf16* qb = p.q + ((int64_t)b * H + h0) * D;
       if constexpr (HPW == 32) {
@@ -396,20 +527,37 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
 #pragma unroll
     for (int vb = 0; vb < C::NVB; ++vb) oacc[vb] = acc_t{};
 
-    if constexpr (HPW == 32 && NBUF >= 3) {
+    if constexpr (C::PIPE) {
       // ---- software-pipelined loop (32-head waves).  Iteration j runs the
       // softmax of tile j interleaved with the QK^T MFMAs of tile j+1, then
-      // the PV MFMAs of tile j; the loads of tile j+NBUF-1 are spread over
-      // the QK^T steps.  The ring holds tiles j (V), j+1 (K) and NBUF-2
-      // tiles in flight.  Past the segment, loads are issued with an empty
-      // resource (they write zeros into a free slot), so every iteration
-      // issues the same number of loads and the waits are constants.
+      // the PV MFMAs of tile j.  The ring holds tiles j (V) and j+1 (K).
+      // bf16: the loads of tile j+NBUF-1 go straight into the ring, spread
+      // over the PV MFMAs, with NBUF-2 tiles in flight.  fp8: the loads of
+      // tile j+3 go to staging slot (j+3) % 2 early in the iteration (over
+      // the QK^T MFMAs); tile j+2, loaded during the previous iteration, is
+      // widened into ring slot (j+2) % 3 over the PV MFMAs.  Past the
+      // segment, loads are issued with an empty resource (they write zeros
+      // into a free slot), so every iteration issues the same number of
+      // loads and the waits are constants.
+      constexpr int AHEAD = F8 ? 3 : NBUF - 1;  // tile whose loads iteration j issues: j + AHEAD
       wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
+      if constexpr (F8) {
+        issue(0);
+        issue(1);
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();  // staging tiles 0 and 1 complete
+        widen_tile(0);
+        widen_tile(1);
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();  // ring tiles 0, 1 written; staging slot 0 free
+        issue(2);
+      } else {
 #pragma unroll
-      for (int i = 0; i < NBUF - 1; ++i) issue(i);
-      wait_vmcnt<(NBUF - 2) * C::LPW>();
-      __builtin_amdgcn_s_barrier();
+        for (int i = 0; i < NBUF - 1; ++i) issue(i);
+        wait_vmcnt<(NBUF - 2) * C::LPW>();
+        __builtin_amdgcn_s_barrier();
+      }
 
       auto kread = [&](const LDS_AS uint8_t* t, int ks) __attribute__((always_inline)) {
         return *reinterpret_cast<const LDS_AS bf16x8*>(t + (ks >> 1) * 1024 +
@@ -458,13 +606,16 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
         s_cur = s0.e + s0.o;
       }
       for (int j = 0; j < n_tiles; ++j) {
-        wait_vmcnt<(NBUF - 3) * C::LPW>();  // tile j+1 is in LDS
-        __builtin_amdgcn_s_barrier();       // ... for every wave; tile j-1's slot is free
+        // tile j+1 is in the ring (fp8: its widening is written and tile
+        // j+2's staging copy complete) for every wave; tile j-1's slot is free
+        if constexpr (F8) wait_vmcnt<0>();
+        else wait_vmcnt<(NBUF - 3) * C::LPW>();
+        __builtin_amdgcn_s_barrier();
         const LDS_AS uint8_t* tcur = (const LDS_AS uint8_t*)ring + (j % NBUF) * C::TILE_BYTES;
         const LDS_AS uint8_t* tnext =
             (const LDS_AS uint8_t*)ring + ((j + 1) % NBUF) * C::TILE_BYTES;
         const int nvalid = min(kTile, te - (ts + j * kTile));
-        const TileLoad tl = prepare(j + NBUF - 1);
+        const TileLoad tl = prepare(j + AHEAD);
 
         float mt = -INFINITY, alpha = 1.f;
         bool rescale = false;
@@ -482,6 +633,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
         static_assert(E >= 1 && L >= 1, "too few QK^T steps to hide the softmax");
         auto hook = [&](auto ksc) __attribute__((always_inline)) {
           constexpr int ks = decltype(ksc)::value;
+          if constexpr (F8 && ks < C::NIW) dma(tl, ks);  // fp8: staging loads of tile j+3
           if constexpr (ks < 4) {
             mt = fmaxf(mt, fmaxf(fmaxf(sv[4 * ks], sv[4 * ks + 1]), fmaxf(sv[4 * ks + 2], sv[4 * ks + 3])));
           } else if constexpr (ks == 4) {
@@ -552,6 +704,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           const uint32_t vbase0 = (uint32_t)(uintptr_t)tcur + v_off0;
           const uint32_t vbase1 = (uint32_t)(uintptr_t)tcur + v_off1;
           constexpr int NST = 2 * C::NVB;
+          using Sched = PvSched<NST, F8 ? C::LPW : 0>;
           auto vread = [&](auto stc) __attribute__((always_inline)) {
             constexpr int st = decltype(stc)::value;
             constexpr int kk = st / C::NVB, vb = st % C::NVB;
@@ -563,13 +716,20 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           u32x4 a0 = vread(std::integral_constant<int, 0>{});
           u32x4 a1 = vread(std::integral_constant<int, 1>{});
           u32x4 a2 = vread(std::integral_constant<int, 2>{});
+          u32x2 wv = {};  // fp8: staging chunk being widened
           static_for<NST>([&](auto stc) __attribute__((always_inline)) {
             constexpr int st = decltype(stc)::value;
             constexpr int kk = st / C::NVB, vb = st % C::NVB;
             u32x4 a3 = a2;
             if constexpr (st + 3 < NST) a3 = vread(std::integral_constant<int, st + 3>{});
-            constexpr int later = 2 * ((st + 3 < NST ? st + 3 : NST - 1) - st);
-            lds_wait<later>(a0);
+            if constexpr (F8) {  // widen block st/3 of tile j+2
+              if constexpr (Sched::has_r(st)) wv = ds_read_b64_asm(widen_src(j + 2, st / 3));
+              if constexpr (Sched::has_w(st)) {
+                lds_wait<Sched::after_r(st / 3)>(wv);
+                ds_write_b128_asm(widen_dst(j + 2, st / 3), e4m3x8_to_bf16x8(wv));
+              }
+            }
+            lds_wait<Sched::after_v(st)>(a0);
             oacc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0),
                                                               kk ? p1 : p0, oacc[vb], 0, 0, 0);
             // scores of tile j+1: sum of its two QK^T chains
@@ -577,10 +737,12 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
 #pragma unroll
               for (int r = 4 * st; r < 4 * st + 4; ++r) s_cur[r] = s_next.e[r] + s_next.o[r];
             }
-            // loads of tile j+NBUF-1, spread over the PV MFMAs
+            // bf16: loads of tile j+NBUF-1, spread over the PV MFMAs
+            if constexpr (!F8) {
 #pragma unroll
-            for (int k = 0; k < C::LPW; ++k)
-              if ((k + 1) * NST / C::LPW - 1 == st) dma(tl, k);
+              for (int k = 0; k < C::NIW; ++k)
+                if ((k + 1) * NST / C::NIW - 1 == st) dma(tl, k);
+            }
             __builtin_amdgcn_sched_barrier(0);
             a0 = a1;
             a1 = a2;
@@ -592,29 +754,44 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     // Drain this wave's earlier stores and loads once, so that no wait for
     // them lands between the ring loads below, then make sure every wave is
     // done with the ring of a previous segment.
+    // fp8 (ring of 2): iteration i loads tile i+2 into staging slot i % 2
+    // over its QK^T MFMAs and widens tile i+1 into ring slot (i+1) % 2 at
+    // its end; the barrier at the top of iteration i+1 publishes both.
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
+    if constexpr (F8) {
+      issue(0);
+      issue(1);
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();  // staging tiles 0 and 1 complete
+      widen_tile(0);
+    } else {
 #pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i)
-      if (i < n_tiles) issue(i);
+      for (int i = 0; i < NBUF - 1; ++i)
+        if (i < n_tiles) issue(i);
+    }
 
     for (int i = 0; i < n_tiles; ++i) {
-      const int ahead = min(NBUF - 2, n_tiles - 1 - i);
-      if (ahead >= 2) wait_vmcnt<(NBUF >= 4 ? 2 : 0) * C::LPW>();
-      else if (ahead == 1) wait_vmcnt<(NBUF >= 3 ? 1 : 0) * C::LPW>();
-      else wait_vmcnt<0>();
+      if constexpr (F8) {
+        wait_vmcnt<0>();
+      } else {
+        const int ahead = min(NBUF - 2, n_tiles - 1 - i);
+        if (ahead >= 2) wait_vmcnt<(NBUF >= 4 ? 2 : 0) * C::LPW>();
+        else if (ahead == 1) wait_vmcnt<(NBUF >= 3 ? 1 : 0) * C::LPW>();
+        else wait_vmcnt<0>();
+      }
       __builtin_amdgcn_s_barrier();
       // The next tile's loads are spread over this tile's QK^T MFMAs: each
       // load instruction can hold the wave at issue while the vector-memory
       // queue drains, which the matrix core then overlaps.
-      const bool more = i + NBUF - 1 < n_tiles;
+      const bool more = F8 || i + NBUF - 1 < n_tiles;
       TileLoad tl;
-      if (more) tl = prepare(i + NBUF - 1);
+      if (more) tl = prepare(F8 ? i + 2 : i + NBUF - 1);
       auto dma_at = [&](int ks) __attribute__((always_inline)) {
-        // load k goes after k-step floor(k * NKS / LPW)
+        // load k goes after k-step floor(k * NKS / NIW)
 #pragma unroll
-        for (int k = 0; k < C::LPW; ++k)
-          if ((k * C::NKS) / C::LPW == ks && more) dma(tl, k);
+        for (int k = 0; k < C::NIW; ++k)
+          if ((k * C::NKS) / C::NIW == ks && more) dma(tl, k);
       };
 
       const LDS_AS uint8_t* tile = (const LDS_AS uint8_t*)ring + (i % NBUF) * C::TILE_BYTES;
@@ -638,22 +815,25 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           bf16x8 q0 = {}, q1 = {};
           if (C::NQR == 0) q0 = qread(0);
           if (C::NQR <= 1) q1 = qread(1);
-#pragma unroll
-          for (int ks = 0; ks < C::NKS; ++ks) {
+          // (compile-time k-steps: Q fragments stay in registers)
+          static_for<C::NKS>([&](auto ksc) __attribute__((always_inline)) {
+            constexpr int ks = decltype(ksc)::value;
             bf16x8 k2 = k1, q2 = q1;
-            if (ks + 2 < C::NKS) {
+            if constexpr (ks + 2 < C::NKS) {
               k2 = kread(ks + 2);
-              if (ks + 2 >= C::NQR) q2 = qread(ks + 2);
+              if constexpr (ks + 2 >= C::NQR) q2 = qread(ks + 2);
             }
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ks < C::NQR ? qf[ks < C::NQR ? ks : 0] : q0,
-                                                        s, 0, 0, 0);
+            bf16x8 qv;
+            if constexpr (ks < C::NQR) qv = qf[ks];
+            else qv = q0;
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qv, s, 0, 0, 0);
             dma_at(ks);
             __builtin_amdgcn_sched_barrier(0);
             k0 = k1;
             k1 = k2;
             q0 = q1;
             q1 = q2;
-          }
+          });
         }
         // position of s[r] is 8*(r/4) + 4*(lane/32) + r%4; mask past the segment
         if (nvalid < kTile) {
@@ -729,15 +909,15 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       } else {
         // ---- S^T over two 16-position halves x 16 heads
         f32x4 s0 = {}, s1 = {};
-#pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) {
+        static_for<C::NKS>([&](auto ksc) __attribute__((always_inline)) {
+          constexpr int ks = decltype(ksc)::value;
           const bf16x8 k0 = *reinterpret_cast<const LDS_AS bf16x8*>(tile + ks * 1024 + qk_off_e);
           const bf16x8 k1 = *reinterpret_cast<const LDS_AS bf16x8*>(
               tile + (C::NKQ + ks) * 1024 + qk_off_e);
           s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], s0, 0, 0, 0);
           s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks], s1, 0, 0, 0);
           dma_at(ks);
-        }
+        });
         // position of s_th[r] is 16*th + 4*(lane/16) + r
         if (nvalid < kTile) {
 #pragma unroll
@@ -801,6 +981,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           });
         }
       }
+      if constexpr (F8) widen_tile(i + 1);
     }
 
     }
@@ -1016,30 +1197,25 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
 
 // ---------------------------------------------------------------- dispatch
 
-typedef void (*Stage1Fn)(Stage1Params);
-
-template <int HPW, int W, int D, int DV, int NBUF>
+template <int HPW, int W, int D, int DV, bool F8>
 int launch_stage1(const Stage1Params& sp, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((mla_stage1<HPW, W, D, DV, NBUF>), dim3(grid), dim3(64 * W), 0, st, sp);
+  constexpr int NBUF = stage1_ring_depth(HPW, W, D, F8);
+  hipLaunchKernelGGL((mla_stage1<HPW, W, D, DV, NBUF, F8>), dim3(grid), dim3(64 * W), 0, st, sp);
   return (int)hipGetLastError();
 }
 
-template <int D, int DV>
+template <int D, int DV, bool F8>
 int launch_stage1_for(const HeadTiling& ht, const Stage1Params& sp, int grid, hipStream_t st) {
-  // ring depth: as deep as LDS and the 6-bit vmcnt allow
   if (ht.heads_per_wave == 32) {
     switch (ht.waves) {
-      case 4: return launch_stage1<32, 4, D, DV, 4>(sp, grid, st);
-      case 2: return launch_stage1<32, 2, D, DV, (D == 576 ? 3 : 4)>(sp, grid, st);
-      default: return launch_stage1<32, 1, D, DV, (D == 576 ? 2 : 4)>(sp, grid, st);
-    }
-  } else {
-    switch (ht.waves) {
-      case 4: return launch_stage1<16, 4, D, DV, 4>(sp, grid, st);
-      case 2: return launch_stage1<16, 2, D, DV, (D == 576 ? 2 : 4)>(sp, grid, st);
-      default: return launch_stage1<16, 1, D, DV, (D == 576 ? 2 : 4)>(sp, grid, st);
+      case 4: return launch_stage1<32, 4, D, DV, F8>(sp, grid, st);
+      case 2: return launch_stage1<32, 2, D, DV, F8>(sp, grid, st);
+      default: return launch_stage1<32, 1, D, DV, F8>(sp, grid, st);
     }
   }
+  // 16-head waves only arise for an odd number of 16-head groups (H % 32 != 0),
+  // which always gives one wave per workgroup
+  return launch_stage1<16, 1, D, DV, F8>(sp, grid, st);
 }
 
 }  // namespace
@@ -1070,10 +1246,14 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
 
   const int units = a.split_mode == 0 ? a.batch * a.num_splits : a.num_splits;
   const int grid1 = (units + 7) / 8 * 8 * ht.head_chunks;
-  if (a.kv_fp8) return (int)hipErrorInvalidValue;  // fp8 kernels: not built yet
   if (stages & kStage1) {
-    const int err = a.head_size == 576 ? launch_stage1_for<576, 512>(ht, sp, grid1, st)
-                                       : launch_stage1_for<320, 256>(ht, sp, grid1, st);
+    int err;
+    if (a.kv_fp8)
+      err = a.head_size == 576 ? launch_stage1_for<576, 512, true>(ht, sp, grid1, st)
+                               : launch_stage1_for<320, 256, true>(ht, sp, grid1, st);
+    else
+      err = a.head_size == 576 ? launch_stage1_for<576, 512, false>(ht, sp, grid1, st)
+                               : launch_stage1_for<320, 256, false>(ht, sp, grid1, st);
     if (err) return err;
   }
   const bool merge = a.split_mode == 1 || a.num_splits > 1;

@@ -124,6 +124,58 @@ def test_ragged_cases(mla, case, mode, splits):
     assert_close(inp, o, lse, ro, rl, label + " o=bf16", rounding_slack=True)
 
 
+FP8_SCALE = float(np.float32(0.05))
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("mode,splits", [(0, 1), (0, 3), (1, 4), (1, 37)])
+def test_ragged_cases_fp8(mla, case, mode, splits):
+    H, D, P, sl = CASES[case]
+    inp = W.small_case(seed=200 + case, batch=len(sl), num_heads=H, head_size=D,
+                       kv_lora_rank=D - 64, page_size=P, seq_lens=sl, table_pad=1,
+                       kv_dtype=W.FP8_E4M3, k_scale=FP8_SCALE)
+    ro, rl = ref(inp)
+    label = f"fp8 case{case} H={H} D={D} P={P} mode={mode} S={splits}"
+    o, lse = run_gpu(mla, inp, splits, mode, o_dtype=torch.float32)
+    assert_close(inp, o, lse, ro, rl, label + " o=f32")
+    o, lse = run_gpu(mla, inp, splits, mode)
+    assert_close(inp, o, lse, ro, rl, label + " o=bf16", rounding_slack=True)
+
+
+FINITE_E4M3 = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+
+
+@pytest.mark.parametrize("H,D", [(16, 576), (32, 576), (64, 576), (128, 576), (48, 320),
+                                 (128, 320)])
+@pytest.mark.parametrize("mode,splits", [(0, 1), (1, 2)])
+def test_fp8_one_position_returns_the_widened_row(mla, H, D, mode, splits):
+    """With a single position the softmax weight is 1, so o is that row's
+    kv_c part times k_scale.  Each sequence's row runs through all 254 finite
+    e4m3fn codes (both signs, subnormals, +-448), so every code must come
+    back as its exact value: with k_scale = 0.375 the product has at most 6
+    significant bits and is exact in bf16 as well as in fp32."""
+    Dv, P, B = D - 64, 16, 3
+    k_scale = 0.375
+    rng = np.random.default_rng(21)
+    nb = B + 2
+    kv = rng.choice(FINITE_E4M3, size=(nb, P, D)).astype(np.uint8)
+    for b in range(B):
+        kv[b + 1, 0, :FINITE_E4M3.size] = np.roll(FINITE_E4M3, 37 * b)
+    table = np.array([[b + 1, 0] for b in range(B)], dtype=np.int32)
+    q = W.f32_to_bf16_bits(rng.standard_normal((B, H, D), dtype=np.float32) * 0.1)
+    w = W.Workload(name="fp8-codes", seed=21, batch=B, num_heads=H, head_size=D,
+                   kv_lora_rank=Dv, page_size=P, num_blocks=nb, kv_dtype=W.FP8_E4M3,
+                   k_scale=k_scale, scale=W.DSV3_SCALE, seq_lens_fixed=(1,) * B)
+    inp = W.DecodeInputs(workload=w, q_bits=q, kv_bits=kv, block_table=table,
+                         seq_lens=np.ones(B, dtype=np.int32))
+    ro, rl = ref(inp)
+    o32, l32 = run_gpu(mla, inp, splits, mode, o_dtype=torch.float32)
+    o16, _ = run_gpu(mla, inp, splits, mode)
+    assert np.array_equal(o32, ro), np.abs(o32 - ro).max()
+    assert np.array_equal(o16, ro), np.abs(o16 - ro).max()
+    assert np.abs(l32 - rl).max() <= 1e-4 * max(1.0, np.abs(rl).max())
+
+
 def test_fp32_output(mla):
     inp = W.small_case(seed=7, batch=3, num_heads=128, head_size=576, kv_lora_rank=512,
                        page_size=64, seq_lens=(100, 1000, 5))
@@ -144,20 +196,24 @@ def test_empty_sequences(mla, mode, splits):
 
 # ---------------------------------------------------------------- bit-exact indexing
 
+@pytest.mark.parametrize("kv_dtype", [W.BF16, W.FP8_E4M3])
 @pytest.mark.parametrize("mode,splits", [(0, 1), (0, 4), (1, 6)])
-def test_page_permutation_is_bitwise_invariant(mla, mode, splits):
+def test_page_permutation_is_bitwise_invariant(mla, mode, splits, kv_dtype):
     inp = W.small_case(seed=11, batch=4, num_heads=128, head_size=576, kv_lora_rank=512,
-                       page_size=16, seq_lens=(37, 100, 64, 257), extra_pages=9)
+                       page_size=16, seq_lens=(37, 100, 64, 257), extra_pages=9,
+                       kv_dtype=kv_dtype, k_scale=FP8_SCALE if kv_dtype == W.FP8_E4M3 else 1.0)
     o, lse = run_gpu(mla, inp, splits, mode)
     o2, lse2 = run_gpu(mla, W.permute_pages(inp, seed=5), splits, mode)
     assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
 
 
+@pytest.mark.parametrize("kv_dtype", [W.BF16, W.FP8_E4M3])
 @pytest.mark.parametrize("mode,splits", [(0, 1), (1, 3)])
 @pytest.mark.parametrize("H,P", [(128, 64), (16, 16)])
-def test_poisoned_unreferenced_slots(mla, mode, splits, H, P):
+def test_poisoned_unreferenced_slots(mla, mode, splits, H, P, kv_dtype):
     inp = W.small_case(seed=13, batch=3, num_heads=H, head_size=576, kv_lora_rank=512,
-                       page_size=P, seq_lens=(37, 100, 5), extra_pages=4, table_pad=3)
+                       page_size=P, seq_lens=(37, 100, 5), extra_pages=4, table_pad=3,
+                       kv_dtype=kv_dtype, k_scale=FP8_SCALE if kv_dtype == W.FP8_E4M3 else 1.0)
     o, lse = run_gpu(mla, inp, splits, mode)
     o2, lse2 = run_gpu(mla, W.poison_unreferenced(inp), splits, mode)
     assert np.all(np.isfinite(o2)) and np.array_equal(o, o2) and np.array_equal(lse, lse2)
@@ -196,7 +252,7 @@ def sample_batches(inp, k=6):
     return sorted(pick)
 
 
-@pytest.mark.parametrize("name", ["dsv3", "skewed", "h320"])
+@pytest.mark.parametrize("name", ["dsv3", "skewed", "h320", "fp8"])
 def test_full_size_configs(mla, name):
     inp = W.generate(name)
     w = inp.workload
@@ -205,6 +261,8 @@ def test_full_size_configs(mla, name):
     ro, rl = ref(inp, picks)
     max_len, tot = int(inp.seq_lens.max()), int(inp.seq_lens.sum())
     shape = mla.shape_of(*dev_inputs[:2], dev_inputs[2])
+    print(f"{name}: B={w.batch} H={w.num_heads} D={w.head_size} {w.kv_dtype} "
+          f"tokens={tot} sampled={picks}", flush=True)
     mode, units, _ = mla.mla_plan(shape, max_len, tot, 256)
     runs = [(mode, units)] + [(0, s) for s in w.parity_splits]
     for mode, splits in runs:
