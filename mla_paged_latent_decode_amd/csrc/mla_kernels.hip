@@ -1106,23 +1106,41 @@ struct Stage2Params {
   const float* ws_lse;
   void* o;
   float* lse;
-  int32_t batch, heads, o_f32, split_mode, num_splits, head_groups;
+  int32_t batch, heads, o_f32, split_mode, num_splits, head_groups, kgroups;
 };
 
-// One workgroup per (sequence, 16 heads); 16 threads per head, 4 floats each
-// per step.
+// One workgroup per (sequence, 8/KG heads, 128 output columns), 256 threads:
+// 32 threads per (head, partial group), each owning 4 consecutive columns.
+// The KG groups of a head take every KG-th partial and are combined through
+// LDS at the end, so a sequence with hundreds of partials is read by many
+// threads at once; each thread keeps 8 partial loads in flight.
+constexpr int kS2Rows = 8, kS2Cols = 128, kS2Batch = 8;
+
 template <int DV>
 __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
-  const int b = blockIdx.x / p.head_groups;
-  const int hg = blockIdx.x % p.head_groups;
+  static_assert(DV % kS2Cols == 0, "");
+  constexpr int NVC = DV / kS2Cols;
+  __shared__ f32x4 red_o[kS2Rows][32];
+  __shared__ float red_m[kS2Rows], red_l[kS2Rows];
+  const int KG = p.kgroups;               // partial groups per head (1, 2, 4 or 8)
+  const int HPB = kS2Rows / KG;           // heads per workgroup
+  int id = blockIdx.x;
+  const int vc = id % NVC;
+  id /= NVC;
+  const int hg = id % p.head_groups;
+  const int b = id / p.head_groups;
   const int t = threadIdx.x;
   const int lane = t & 63;
+  const int row = t >> 5, j = t & 31;
+  const int hl = row / KG, g = row % KG;
   const int H = p.heads;
-  const int h = hg * 16 + (t >> 4);
-  const int j = t & 15;
+  const int h = hg * HPB + hl;  // < H: H is a multiple of 16
+  const int v = vc * kS2Cols + 4 * j;
   const int n = p.seq_lens[b];
 
-  int first, count, unit0 = 0, units = 1;
+  int first, count;
+  bool all_live = true;
+  int unit0 = 0, units = 1;
   int64_t tiles_total = 1;
   if (p.split_mode == 0) {
     const int S = p.num_splits;
@@ -1147,10 +1165,9 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
     }
     const int nt = tiles_of(n);
     if (nt == 0) {
-      if (h < H) {
-        for (int v = 4 * j; v < DV; v += 64)
-          store_out4(p.o, p.o_f32, ((size_t)b * H + h) * DV + v, f32x4{0.f, 0.f, 0.f, 0.f});
-        if (j == 0) p.lse[(size_t)b * H + h] = -INFINITY;
+      if (g == 0) {
+        store_out4(p.o, p.o_f32, ((size_t)b * H + h) * DV + v, f32x4{0.f, 0.f, 0.f, 0.f});
+        if (vc == 0 && j == 0) p.lse[(size_t)b * H + h] = -INFINITY;
       }
       return;
     }
@@ -1159,40 +1176,65 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
     if (uf == ul) return;  // stage 1 wrote the final result
     first = uf + b;
     count = ul - uf + 1;
-    // with more units than tiles some units in [uf, ul] own no tile and wrote
-    // no partial; they are skipped below
+    // with more units than tiles, some units own no tile and wrote no
+    // partial: they get weight 0 and their slots are never read
+    all_live = U <= TT;
     tiles_total = TT;
     units = U;
     unit0 = uf;
   }
-  if (h >= H) return;
   auto live = [&](int k) {
-    if (p.split_mode == 0) return true;
+    if (all_live) return true;
     const int64_t u = unit0 + k;
     return (u + 1) * tiles_total / units > u * tiles_total / units;
   };
+  const float* lse_h = p.ws_lse + (size_t)first * H + h;  // partial k at lse_h[k * H]
 
+  // M = max of the partial lse of head h, over its KG groups x 32 lanes
   float M = -INFINITY;
-  for (int k = 0; k < count; ++k)
-    if (live(k)) M = fmaxf(M, p.ws_lse[(size_t)(first + k) * H + h]);
+  for (int k = g * 32 + j; k < count; k += 32 * KG)
+    if (live(k)) M = fmaxf(M, lse_h[(size_t)k * H]);
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+  if (j == 0) red_m[row] = M;
+  __syncthreads();
+  for (int r = hl * KG; r < hl * KG + KG; ++r) M = fmaxf(M, red_m[r]);
+
+  // this group's partials k = g, g + KG, ...: weights e^(lse_k - M)
   float tot = 0.f;
-  f32x4 acc[DV / 64];
-#pragma unroll
-  for (int c = 0; c < DV / 64; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < count; ++k) {
-    if (!live(k)) continue;
-    const size_t slot = (size_t)(first + k);
-    const float w = __expf(p.ws_lse[slot * H + h] - M);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const size_t stride = (size_t)H * DV;  // floats between consecutive partials
+  const float* src = p.ws_o + ((size_t)first * H + h) * DV + v;
+  auto add = [&](int k, const f32x4& x) {
+    if (!live(k)) return;  // a slot without a partial may hold anything
+    const float w = __expf(lse_h[(size_t)k * H] - M);
     tot += w;
-    const float* src = p.ws_o + (slot * H + h) * DV + 4 * j;
+    acc += w * x;
+  };
+  int k = g;
+  for (; k + (kS2Batch - 1) * KG < count; k += kS2Batch * KG) {
+    f32x4 x[kS2Batch];
 #pragma unroll
-    for (int c = 0; c < DV / 64; ++c) acc[c] += w * *reinterpret_cast<const f32x4*>(src + 64 * c);
+    for (int i = 0; i < kS2Batch; ++i)
+      x[i] = *reinterpret_cast<const f32x4*>(src + (size_t)(k + i * KG) * stride);
+#pragma unroll
+    for (int i = 0; i < kS2Batch; ++i) add(k + i * KG, x[i]);
   }
-  const float inv = 1.f / tot;
-#pragma unroll
-  for (int c = 0; c < DV / 64; ++c)
-    store_out4(p.o, p.o_f32, ((size_t)b * H + h) * DV + 4 * j + 64 * c, acc[c] * inv);
-  if (j == 0) p.lse[(size_t)b * H + h] = M + __logf(tot);
+  for (; k < count; k += KG) add(k, *reinterpret_cast<const f32x4*>(src + (size_t)k * stride));
+
+  // combine the KG groups of each head
+  if (KG > 1) {
+    red_o[row][j] = acc;
+    if (j == 0) red_l[row] = tot;
+    __syncthreads();
+    if (g != 0) return;
+    for (int r = row + 1; r < row + KG; ++r) {
+      acc += red_o[r][j];
+      tot += red_l[r];
+    }
+  }
+  store_out4(p.o, p.o_f32, ((size_t)b * H + h) * DV + v, acc * (1.f / tot));
+  if (vc == 0 && j == 0) p.lse[(size_t)b * H + h] = M + __logf(tot);
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -1269,8 +1311,12 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   s2.o_f32 = a.o_f32;
   s2.split_mode = a.split_mode;
   s2.num_splits = a.num_splits;
-  s2.head_groups = (a.heads + 15) / 16;
-  const int grid2 = a.batch * s2.head_groups;
+  // partial groups per head: about a quarter of the mean partial count per
+  // sequence (units / batch + 1), a power of two up to 8
+  const int per_seq = a.split_mode == 0 ? a.num_splits : a.num_splits / a.batch + 1;
+  s2.kgroups = per_seq >= 32 ? 8 : per_seq >= 16 ? 4 : per_seq >= 8 ? 2 : 1;
+  s2.head_groups = a.heads / (kS2Rows / s2.kgroups);
+  const int grid2 = a.batch * s2.head_groups * (a.d_v / kS2Cols);
   if (a.d_v == 512) hipLaunchKernelGGL(mla_stage2<512>, dim3(grid2), dim3(256), 0, st, s2);
   else hipLaunchKernelGGL(mla_stage2<256>, dim3(grid2), dim3(256), 0, st, s2);
   return (int)hipGetLastError();
