@@ -26,9 +26,9 @@ WorkspaceLayout workspace_layout(int32_t batch, int32_t heads, int32_t d_v, int3
   } else {
     return w;
   }
-  const int64_t o_bytes = w.slots * heads * (int64_t)d_v * 4;
+  const int64_t o_bytes = w.slots * heads * (int64_t)d_v * 2;
   const int64_t lse_off = align_up(o_bytes, 256);
-  const int64_t total = lse_off + align_up(w.slots * heads * 4, 256);
+  const int64_t total = lse_off + align_up(w.slots * heads * 8, 256);
   w.o_bytes = (size_t)o_bytes;
   w.lse_offset = (size_t)lse_off;
   w.total = (size_t)total;
@@ -164,9 +164,8 @@ static mla_status decode_stages(const mla_shape* shape, const void* q, const voi
   a.seq_lens = seq_lens;
   a.o = o;
   a.lse = lse;
-  a.ws_o = wl.total ? reinterpret_cast<float*>(workspace) : nullptr;
-  a.ws_lse = wl.total ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + wl.lse_offset)
-                      : nullptr;
+  a.ws_o = wl.total ? workspace : nullptr;
+  a.ws_ls = wl.total ? reinterpret_cast<char*>(workspace) + wl.lse_offset : nullptr;
   a.batch = shape->batch;
   a.heads = shape->num_heads;
   a.head_size = shape->head_size;

@@ -10,9 +10,10 @@ namespace mla {
 constexpr int kTile = 32;  // context positions per stage-1 tile
 
 // Workspace layout (both split modes): `slots` partial results, each
-//   ws_o   [slots][H][D_v]  float32, the segment's normalised output
-//   ws_lse [slots][H]       float32, the segment's natural-log lse
-// ws_lse starts at the first 256-byte boundary after ws_o.
+//   ws_o  [slots][H][D_v]  fp16, the segment's normalised output o_s stored
+//                          as o_s * 2^-e (e per row, see ws_ls)
+//   ws_ls [slots][H][2]    float32 {lse_s (natural log), 2^e}
+// ws_ls starts at the first 256-byte boundary after ws_o.
 struct WorkspaceLayout {
   int64_t slots = 0;
   size_t o_bytes = 0;
@@ -66,8 +67,8 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   void* o;
   float* lse;
-  float* ws_o;
-  float* ws_lse;
+  void* ws_o;
+  void* ws_ls;
   int32_t batch;
   int32_t heads;
   int32_t head_size;

@@ -226,8 +226,8 @@ struct Stage1Params {
   const int32_t* seq_lens;
   void* o;
   float* lse;
-  float* ws_o;
-  float* ws_lse;
+  _Float16* ws_o;  // partial outputs, fp16, each row scaled by a power of two
+  f32x2* ws_ls;    // per partial row: {lse (natural log), that power of two}
   int32_t batch, heads, page_size, bt_stride;
   int32_t o_f32, split_mode, num_splits, head_chunks;
   float score_log2;  // scale * log2(e) (* k_scale for fp8 caches)
@@ -299,6 +299,12 @@ struct Cfg {
   static constexpr int NIW = 2 * NIH / W;                   // DMA copies per wave per tile
   static constexpr int STG_TILE = F8 ? kTile * D : 0;       // fp8 staging tile bytes
   static constexpr int STG_BYTES = 2 * STG_TILE;
+  // Pipelined bf16 loop: the k-th of a wave's NIW tile loads goes out at step
+  // dma_step(k) of the iteration's NKS QK^T + 2*NVB PV MFMA steps.  Spread
+  // evenly, the loads leave the memory pipeline at about the rate HBM drains
+  // it, so an issue rarely blocks the wave (and its MFMAs); bunched together
+  // they would block while the pipeline runs dry for the rest of the tile.
+  static constexpr int dma_step(int k) { return k * (NKS + 2 * NVB) / NIW; }
   // software-pipelined loop (softmax of tile j behind the QK^T of tile j+1)
   static constexpr bool PIPE = HPW == 32 && (F8 ? W == 4 : NBUF >= 3);
   static_assert(NBUF == stage1_ring_depth(HPW, W, D, F8), "ring depth");
@@ -333,12 +339,16 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
 
-  // XCD-aware decode of the workgroup id: consecutive ids go to different
-  // XCDs, so the head chunks of one unit share an XCD (and its L2).
+  // XCD-aware decode of the workgroup id.  Consecutive ids go to different
+  // XCDs (id % 8), so XCD x is given the x-th contiguous run of units, and
+  // the head chunks of one unit share it: neighbouring units mostly belong
+  // to the same sequence, whose query rows then come from that XCD's L2
+  // after the first read.
   const int id = blockIdx.x;
-  const int hc = (id >> 3) % p.head_chunks;
-  const int unit = ((id >> 3) / p.head_chunks) * 8 + (id & 7);
   const int num_units = p.split_mode == 0 ? p.batch * p.num_splits : p.num_splits;
+  const int units_per_xcd = (num_units + 7) >> 3;
+  const int hc = (id >> 3) % p.head_chunks;
+  const int unit = (id & 7) * units_per_xcd + (id >> 3) / p.head_chunks;
   if (unit >= num_units) return;
 
   const int h0 = hc * C::HEADS_PER_WG + wave * HPW;  // first head of this wave
@@ -498,8 +508,13 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     };
 
     // Q fragments of this wave's heads (B operand of S^T = K Q^T): the first
-    // NQR k-steps in VGPRs, the rest in this wave's LDS region (lane-linear)
+    // NQR k-steps in VGPRs, the rest in this wave's LDS region (lane-linear).
+    // In the pipelined bf16 loop the LDS part is held in registers until the
+    // first tiles' loads are issued, so that the query, the block-table
+    // window and the first tiles are all in flight together.
+    constexpr bool kEarlyRing = C::PIPE && !F8;
     bf16x8 qf[C::NQR];
+    bf16x8 qtmp[kEarlyRing ? (C::QLDS > 0 ? C::QLDS : 1) : 1];
     LDS_AS uint8_t* qlds =
         (LDS_AS uint8_t*)ring + NBUF * C::TILE_BYTES + C::STG_BYTES + wave * C::QLDS * 1024;
     {
@@ -509,9 +524,13 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
 #pragma unroll
         for (int ks = 0; ks < C::NQR; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qr + 16 * ks);
 #pragma unroll
-        for (int ks = C::NQR; ks < C::NKS; ++ks)
-          *reinterpret_cast<LDS_AS bf16x8*>(qlds + (ks - C::NQR) * 1024 + lane * 16) =
-              *reinterpret_cast<const bf16x8*>(qr + 16 * ks);
+        for (int ks = C::NQR; ks < C::NKS; ++ks) {
+          if constexpr (kEarlyRing)
+            qtmp[ks - C::NQR] = *reinterpret_cast<const bf16x8*>(qr + 16 * ks);
+          else
+            *reinterpret_cast<LDS_AS bf16x8*>(qlds + (ks - C::NQR) * 1024 + lane * 16) =
+                *reinterpret_cast<const bf16x8*>(qr + 16 * ks);
+        }
       } else {
         const __bf16* qr = qb + (int64_t)(lane & 15) * D + 8 * (lane >> 4);
 #pragma unroll
@@ -540,8 +559,24 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       // into a free slot), so every iteration issues the same number of
       // loads and the waits are constants.
       constexpr int AHEAD = F8 ? 3 : NBUF - 1;  // tile whose loads iteration j issues: j + AHEAD
+      if constexpr (!F8) {
+        // every wave is done with the ring of a previous segment; the first
+        // tiles go out behind the query loads, then the query's LDS part is
+        // stored (asm: no compiler wait for the ring loads it cannot alias)
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int i = 0; i < NBUF - 1; ++i) issue(i);
+#pragma unroll
+        for (int k = 0; k < C::QLDS; ++k)
+          ds_write_b128_asm((uint32_t)(uintptr_t)(qlds + k * 1024 + lane * 16),
+                            __builtin_bit_cast(u32x4, qtmp[k]));
+        wait_vmcnt<(NBUF - 2) * C::LPW>();
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the query's LDS part is written
+        __builtin_amdgcn_s_barrier();
+      } else {
       wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
+      }
       if constexpr (F8) {
         issue(0);
         issue(1);
@@ -552,11 +587,6 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();  // ring tiles 0, 1 written; staging slot 0 free
         issue(2);
-      } else {
-#pragma unroll
-        for (int i = 0; i < NBUF - 1; ++i) issue(i);
-        wait_vmcnt<(NBUF - 2) * C::LPW>();
-        __builtin_amdgcn_s_barrier();
       }
 
       auto kread = [&](const LDS_AS uint8_t* t, int ks) __attribute__((always_inline)) {
@@ -634,6 +664,12 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
         auto hook = [&](auto ksc) __attribute__((always_inline)) {
           constexpr int ks = decltype(ksc)::value;
           if constexpr (F8 && ks < C::NIW) dma(tl, ks);  // fp8: staging loads of tile j+3
+          // bf16: the loads of tile j+NBUF-1, spread evenly over the QK^T and PV steps
+          if constexpr (!F8) {
+            static_for<C::NIW>([&](auto kc) __attribute__((always_inline)) {
+              if constexpr (C::dma_step(decltype(kc)::value) == ks) dma(tl, decltype(kc)::value);
+            });
+          }
           if constexpr (ks < 4) {
             mt = fmaxf(mt, fmaxf(fmaxf(sv[4 * ks], sv[4 * ks + 1]), fmaxf(sv[4 * ks + 2], sv[4 * ks + 3])));
           } else if constexpr (ks == 4) {
@@ -737,11 +773,12 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
 #pragma unroll
               for (int r = 4 * st; r < 4 * st + 4; ++r) s_cur[r] = s_next.e[r] + s_next.o[r];
             }
-            // bf16: loads of tile j+NBUF-1, spread over the PV MFMAs
+            // bf16: the rest of the loads of tile j+NBUF-1
             if constexpr (!F8) {
-#pragma unroll
-              for (int k = 0; k < C::NIW; ++k)
-                if ((k + 1) * NST / C::NIW - 1 == st) dma(tl, k);
+              static_for<C::NIW>([&](auto kc) __attribute__((always_inline)) {
+                if constexpr (C::dma_step(decltype(kc)::value) == C::NKS + st)
+                  dma(tl, decltype(kc)::value);
+              });
             }
             __builtin_amdgcn_sched_barrier(0);
             a0 = a1;
@@ -999,32 +1036,84 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     const float lse_v = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
     const int hl = HPW == 32 ? (lane & 31) : (lane & 15);
     const int h = h0 + hl;
-    // final results go to o (bf16 or fp32), partials to the fp32 workspace
-    const bool out16 = final_out && !p.o_f32;
-    float* dst32 = final_out ? reinterpret_cast<float*>(p.o) : p.ws_o;
-    const size_t row = final_out ? (size_t)b * H + h : (size_t)slot * H + h;
+    // lane holds O^T[v, h] for v = 32*vb + 8*g4 + 4*(lane/32) + i (32-head
+    // waves) or v = 16*vb + 4*(lane/16) + i (16-head waves), i = 0..3
+    auto vals = [&](int vb, int g4) __attribute__((always_inline)) {
+      if constexpr (HPW == 32)
+        return f32x4{oacc[vb][4 * g4], oacc[vb][4 * g4 + 1], oacc[vb][4 * g4 + 2],
+                     oacc[vb][4 * g4 + 3]};
+      else
+        return (f32x4)oacc[vb];
+    };
+    auto col = [&](int vb, int g4) __attribute__((always_inline)) {
+      return HPW == 32 ? 32 * vb + 8 * g4 + 4 * (lane >> 5) : 16 * vb + 4 * (lane >> 4);
+    };
+    constexpr int NG4 = HPW == 32 ? 4 : 1;
+    if (final_out) {
+      // the sequence's final o (bf16 or fp32) and lse
+      const size_t row = (size_t)b * H + h;
 #pragma unroll
-    for (int vb = 0; vb < C::NVB; ++vb) {
+      for (int vb = 0; vb < C::NVB; ++vb) {
 #pragma unroll
-      for (int g4 = 0; g4 < (HPW == 32 ? 4 : 1); ++g4) {
-        int v;
-        f32x4 val;
-        if constexpr (HPW == 32) {
-          v = 32 * vb + 8 * g4 + 4 * (lane >> 5);
-          val = f32x4{oacc[vb][4 * g4], oacc[vb][4 * g4 + 1], oacc[vb][4 * g4 + 2],
-                      oacc[vb][4 * g4 + 3]} * inv;
-        } else {
-          v = 16 * vb + 4 * (lane >> 4);
-          val = oacc[vb] * inv;
+        for (int g4 = 0; g4 < NG4; ++g4) {
+          const f32x4 val = vals(vb, g4) * inv;
+          const int v = col(vb, g4);
+          if (!p.o_f32)
+            *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(p.o) + row * DV + v) =
+                __builtin_convertvector(val, bf16x4);
+          else
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + row * DV + v) = val;
         }
-        if (out16)
-          *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(p.o) + row * DV + v) =
-              __builtin_convertvector(val, bf16x4);
-        else
-          *reinterpret_cast<f32x4*>(dst32 + row * DV + v) = val;
       }
+      if (HPW == 32 ? (lane < 32) : (lane < 16)) p.lse[row] = lse_v;
+    } else {
+      // A partial (o_s, lse_s) for the merge.  o_s is stored in fp16 as
+      // o_s * 2^-e, with e chosen per row so that the row's largest |value|
+      // lands in [2^14, 2^15): no overflow whatever the cache's range, and a
+      // relative rounding error of at most 2^-12 of that largest value.
+      const size_t row = (size_t)slot * H + h;
+      float mx = 0.f;
+#pragma unroll
+      for (int vb = 0; vb < C::NVB; ++vb)
+#pragma unroll
+        for (int r = 0; r < (HPW == 32 ? 16 : 4); ++r) mx = fmaxf(mx, fabsf(oacc[vb][r]));
+      if constexpr (HPW == 16) mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = max_halves(mx) * inv;
+      int e = 0;
+      if (mx > 0.f && mx <= 3.0e38f) {
+        int ex;
+        (void)frexpf(mx, &ex);  // mx in [2^(ex-1), 2^ex)
+        e = ex - 15;
+      }
+      const float sinv = ldexpf(inv, -e);
+      _Float16* dst = p.ws_o + row * DV;
+#pragma unroll
+      for (int vb = 0; vb < C::NVB; ++vb) {
+        if constexpr (HPW == 32) {
+          // g4 pairs (0,1) and (2,3): the two half-waves swap halves so that
+          // each lane stores 8 consecutive columns (16 bytes)
+#pragma unroll
+          for (int gp = 0; gp < 2; ++gp) {
+            typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+            const u32x2 a = __builtin_bit_cast(
+                u32x2, __builtin_convertvector(vals(vb, 2 * gp) * sinv, f16x4));
+            const u32x2 c = __builtin_bit_cast(
+                u32x2, __builtin_convertvector(vals(vb, 2 * gp + 1) * sinv, f16x4));
+            // lanes 0-31 end with columns +0..7, lanes 32-63 with +8..15
+            const auto s0 = __builtin_amdgcn_permlane32_swap(a[0], c[0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(a[1], c[1], false, false);
+            const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
+            const int v = 32 * vb + 16 * gp + 8 * (lane >> 5);
+            *reinterpret_cast<u32x4*>(dst + v) = w;
+          }
+        } else {
+          typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+          *reinterpret_cast<f16x4*>(dst + col(vb, 0)) =
+              __builtin_convertvector(vals(vb, 0) * sinv, f16x4);
+        }
+      }
+      if (HPW == 32 ? (lane < 32) : (lane < 16)) p.ws_ls[row] = f32x2{lse_v, ldexpf(1.f, e)};
     }
-    if (HPW == 32 ? (lane < 32) : (lane < 16)) (final_out ? p.lse : p.ws_lse)[row] = lse_v;
   };
 
   // ---------------- enumerate this unit's segments; process has one call site
@@ -1102,25 +1191,36 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
 
 struct Stage2Params {
   const int32_t* seq_lens;
-  const float* ws_o;
-  const float* ws_lse;
+  const _Float16* ws_o;
+  const f32x2* ws_ls;
   void* o;
   float* lse;
   int32_t batch, heads, o_f32, split_mode, num_splits, head_groups, kgroups;
 };
 
-// One workgroup per (sequence, 8/KG heads, 128 output columns), 256 threads:
-// 32 threads per (head, partial group), each owning 4 consecutive columns.
-// The KG groups of a head take every KG-th partial and are combined through
-// LDS at the end, so a sequence with hundreds of partials is read by many
-// threads at once; each thread keeps 8 partial loads in flight.
-constexpr int kS2Rows = 8, kS2Cols = 128, kS2Batch = 8;
+// One workgroup per (sequence, 8/KG heads, 256 output columns), 256 threads:
+// 32 threads per (head, partial group), each owning 8 consecutive columns
+// (one 16-byte fp16 load per partial).  The KG groups of a head take every
+// KG-th partial and are combined through LDS at the end, so a sequence with
+// hundreds of partials is read by many threads at once; each thread keeps 8
+// partial loads in flight.
+constexpr int kS2Rows = 8, kS2Cols = 256, kS2Batch = 8;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void store_out8(void* o, int o_f32, size_t idx, const f32x8& v) {
+  if (o_f32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + idx) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + idx + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  } else {
+    *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(o) + idx) = __builtin_convertvector(v, bf16x8);
+  }
+}
 
 template <int DV>
 __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
   static_assert(DV % kS2Cols == 0, "");
   constexpr int NVC = DV / kS2Cols;
-  __shared__ f32x4 red_o[kS2Rows][32];
+  __shared__ f32x8 red_o[kS2Rows][32];
   __shared__ float red_m[kS2Rows], red_l[kS2Rows];
   const int KG = p.kgroups;               // partial groups per head (1, 2, 4 or 8)
   const int HPB = kS2Rows / KG;           // heads per workgroup
@@ -1135,7 +1235,7 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
   const int hl = row / KG, g = row % KG;
   const int H = p.heads;
   const int h = hg * HPB + hl;  // < H: H is a multiple of 16
-  const int v = vc * kS2Cols + 4 * j;
+  const int v = vc * kS2Cols + 8 * j;
   const int n = p.seq_lens[b];
 
   int first, count;
@@ -1166,7 +1266,7 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
     const int nt = tiles_of(n);
     if (nt == 0) {
       if (g == 0) {
-        store_out4(p.o, p.o_f32, ((size_t)b * H + h) * DV + v, f32x4{0.f, 0.f, 0.f, 0.f});
+        store_out8(p.o, p.o_f32, ((size_t)b * H + h) * DV + v, f32x8{});
         if (vc == 0 && j == 0) p.lse[(size_t)b * H + h] = -INFINITY;
       }
       return;
@@ -1188,39 +1288,41 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
     const int64_t u = unit0 + k;
     return (u + 1) * tiles_total / units > u * tiles_total / units;
   };
-  const float* lse_h = p.ws_lse + (size_t)first * H + h;  // partial k at lse_h[k * H]
+  const f32x2* ls_h = p.ws_ls + (size_t)first * H + h;  // partial k at ls_h[k * H]
 
   // M = max of the partial lse of head h, over its KG groups x 32 lanes
   float M = -INFINITY;
   for (int k = g * 32 + j; k < count; k += 32 * KG)
-    if (live(k)) M = fmaxf(M, lse_h[(size_t)k * H]);
+    if (live(k)) M = fmaxf(M, ls_h[(size_t)k * H][0]);
 #pragma unroll
   for (int m = 16; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
   if (j == 0) red_m[row] = M;
   __syncthreads();
   for (int r = hl * KG; r < hl * KG + KG; ++r) M = fmaxf(M, red_m[r]);
 
-  // this group's partials k = g, g + KG, ...: weights e^(lse_k - M)
+  // this group's partials k = g, g + KG, ...: weight e^(lse_k - M); the
+  // stored row is o_k * 2^-e_k, so it enters with e^(lse_k - M) * 2^e_k
   float tot = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const size_t stride = (size_t)H * DV;  // floats between consecutive partials
-  const float* src = p.ws_o + ((size_t)first * H + h) * DV + v;
-  auto add = [&](int k, const f32x4& x) {
+  f32x8 acc = {};
+  const size_t stride = (size_t)H * DV;  // elements between consecutive partials
+  const _Float16* src = p.ws_o + ((size_t)first * H + h) * DV + v;
+  auto add = [&](int k, const f16x8& x) {
     if (!live(k)) return;  // a slot without a partial may hold anything
-    const float w = __expf(lse_h[(size_t)k * H] - M);
+    const f32x2 ls = ls_h[(size_t)k * H];
+    const float w = __expf(ls[0] - M);
     tot += w;
-    acc += w * x;
+    acc += (w * ls[1]) * __builtin_convertvector(x, f32x8);
   };
   int k = g;
   for (; k + (kS2Batch - 1) * KG < count; k += kS2Batch * KG) {
-    f32x4 x[kS2Batch];
+    f16x8 x[kS2Batch];
 #pragma unroll
     for (int i = 0; i < kS2Batch; ++i)
-      x[i] = *reinterpret_cast<const f32x4*>(src + (size_t)(k + i * KG) * stride);
+      x[i] = *reinterpret_cast<const f16x8*>(src + (size_t)(k + i * KG) * stride);
 #pragma unroll
     for (int i = 0; i < kS2Batch; ++i) add(k + i * KG, x[i]);
   }
-  for (; k < count; k += KG) add(k, *reinterpret_cast<const f32x4*>(src + (size_t)k * stride));
+  for (; k < count; k += KG) add(k, *reinterpret_cast<const f16x8*>(src + (size_t)k * stride));
 
   // combine the KG groups of each head
   if (KG > 1) {
@@ -1233,7 +1335,7 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
       tot += red_l[r];
     }
   }
-  store_out4(p.o, p.o_f32, ((size_t)b * H + h) * DV + v, acc * (1.f / tot));
+  store_out8(p.o, p.o_f32, ((size_t)b * H + h) * DV + v, acc * (1.f / tot));
   if (vc == 0 && j == 0) p.lse[(size_t)b * H + h] = M + __logf(tot);
 }
 
@@ -1273,8 +1375,8 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   sp.seq_lens = a.seq_lens;
   sp.o = a.o;
   sp.lse = a.lse;
-  sp.ws_o = a.ws_o;
-  sp.ws_lse = a.ws_lse;
+  sp.ws_o = reinterpret_cast<_Float16*>(a.ws_o);
+  sp.ws_ls = reinterpret_cast<f32x2*>(a.ws_ls);
   sp.batch = a.batch;
   sp.heads = a.heads;
   sp.page_size = a.page_size;
@@ -1302,8 +1404,8 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   if (!merge || !(stages & kStage2)) return 0;
   Stage2Params s2;
   s2.seq_lens = a.seq_lens;
-  s2.ws_o = a.ws_o;
-  s2.ws_lse = a.ws_lse;
+  s2.ws_o = reinterpret_cast<const _Float16*>(a.ws_o);
+  s2.ws_ls = reinterpret_cast<const f32x2*>(a.ws_ls);
   s2.o = a.o;
   s2.lse = a.lse;
   s2.batch = a.batch;

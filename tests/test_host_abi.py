@@ -55,12 +55,13 @@ def shape(**kw):
 def test_workspace_sizes():
     s = shape()
     assert mla.mla_workspace_size(s, mla.SPLIT_PER_SEQUENCE, 1) == 0
-    per = 64 * 16 * 128 * 512 * 4
+    # fp16 partial rows plus an {lse, row scale} float pair per row
+    per = 64 * 16 * 128 * 512 * 2
     got = mla.mla_workspace_size(s, mla.SPLIT_PER_SEQUENCE, 16)
-    lse_bytes = 64 * 16 * 128 * 4
-    assert got == per + lse_bytes  # both parts are 256-byte multiples here
+    ls_bytes = 64 * 16 * 128 * 8
+    assert got == per + ls_bytes  # both parts are 256-byte multiples here
     bal = mla.mla_workspace_size(s, mla.SPLIT_BALANCED, 256)
-    assert bal == (256 + 64) * 128 * (512 + 1) * 4
+    assert bal == (256 + 64) * 128 * (512 * 2 + 8)
     assert mla.mla_workspace_size(s, 7, 4) == 0
     assert mla.mla_workspace_size(s, mla.SPLIT_BALANCED, 0) == 0
     assert mla.mla_workspace_size(shape(head_size=400), mla.SPLIT_BALANCED, 4) == 0
