@@ -95,8 +95,11 @@ typedef enum mla_dtype {
  *
  * MLA_SPLIT_BALANCED -- the batch's 32-position tiles, sequence after
  *   sequence, are cut into S equal runs ("work units"), one per workgroup and
- *   head chunk, so that every workgroup streams the same amount of cache
- *   whatever the mix of lengths.  A unit may hold the end of one sequence and
+ *   head chunk, so that every workgroup does the same amount of work whatever
+ *   the mix of lengths.  Each non-empty sequence is charged a few extra
+ *   virtual tiles for the fixed cost of starting a segment (its query load
+ *   and partial store), so a unit that also starts a new sequence streams
+ *   correspondingly fewer tiles.  A unit may hold the end of one sequence and
  *   the start of the next.  Results are reproducible run to run for the same
  *   batch, but a sequence's rounding may depend on the other lengths.
  */

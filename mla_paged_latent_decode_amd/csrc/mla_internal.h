@@ -45,7 +45,9 @@ constexpr int kLdsBytes = 160 * 1024;
 constexpr int stage1_ring_depth(int hpw, int waves, int d, bool fp8) {
   if (fp8) return (hpw == 32 && waves == 4) ? 3 : 2;
   if (d != 576) return 4;
-  if (hpw == 32) return waves == 4 ? 4 : (waves == 2 ? 3 : 2);
+  // 32-head waves at D = 576: three tiles, so that 12 of Q's 36 k-steps fit
+  // in LDS and the score accumulators stay in VGPRs beside Q and O
+  if (hpw == 32) return waves == 4 ? 3 : (waves == 2 ? 3 : 2);
   return waves == 4 ? 4 : 2;
 }
 constexpr int stage1_staging_bytes(int d, bool fp8) { return fp8 ? 2 * kTile * d : 0; }

@@ -230,6 +230,7 @@ struct Stage1Params {
   f32x2* ws_ls;    // per partial row: {lse (natural log), that power of two}
   int32_t batch, heads, page_size, bt_stride;
   int32_t o_f32, split_mode, num_splits, head_chunks;
+  int32_t seg_cost;  // balanced mode: virtual tiles charged per sequence start
   float score_log2;  // scale * log2(e) (* k_scale for fp8 caches)
   float out_scale;   // 1, or k_scale for fp8 caches
 };
@@ -260,11 +261,18 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
   return x;
 }
 
-__device__ __forceinline__ int64_t total_tiles(const int32_t* seq_lens, int B, int lane) {
+// Balanced mode cuts a "cost stream" into equal runs: every non-empty
+// sequence contributes SC virtual tiles (what starting a segment costs: the
+// query load, the first tiles' latency and a partial's store) and then its
+// 32-position tiles.  A unit that starts a sequence part-way through
+// therefore streams fewer tiles, and units finish together.
+__device__ __forceinline__ int cost_of(int n, int sc) { return n > 0 ? sc + tiles_of(n) : 0; }
+
+__device__ __forceinline__ int64_t total_cost(const int32_t* seq_lens, int B, int sc, int lane) {
   int64_t tot = 0;
   for (int c0 = 0; c0 < B; c0 += 64) {
     int b = c0 + lane;
-    int nt = b < B ? tiles_of(seq_lens[b]) : 0;
+    int nt = b < B ? cost_of(seq_lens[b], sc) : 0;
     int s = wave_incl_scan(nt, lane);
     tot += __shfl(s, 63, 64);
   }
@@ -304,7 +312,11 @@ struct Cfg {
   // evenly, the loads leave the memory pipeline at about the rate HBM drains
   // it, so an issue rarely blocks the wave (and its MFMAs); bunched together
   // they would block while the pipeline runs dry for the rest of the tile.
-  static constexpr int dma_step(int k) { return k * (NKS + 2 * NVB) / NIW; }
+  // With a ring of three the loads of tile j+2 must land before iteration
+  // j+1 starts, so they go out over the first half of the QK^T steps.
+  static constexpr int dma_step(int k) {
+    return NBUF >= 4 ? k * (NKS + 2 * NVB) / NIW : k * (NKS / 2) / NIW;
+  }
   // software-pipelined loop (softmax of tile j behind the QK^T of tile j+1)
   static constexpr bool PIPE = HPW == 32 && (F8 ? W == 4 : NBUF >= 3);
   static_assert(NBUF == stage1_ring_depth(HPW, W, D, F8), "ring depth");
@@ -726,9 +738,12 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
             });
           }
         };
-        S2 s_next = {};
-        if (j + 1 < n_tiles) s_next = qk(tnext, hook);
-        else static_for<C::NKS>(hook);
+        // QK^T of tile j+1 runs unconditionally: on the segment's last tile it
+        // reads the zero-filled slot past the end and its scores are never
+        // used.  A branch here would make the compiler zero the score
+        // accumulators explicitly every tile instead of starting the chains
+        // from an inline zero.
+        const S2 s_next = qk(tnext, hook);
         if (rescale) {  // uniform, rare: the running max moved by more than kTau
 #pragma unroll
           for (int vb = 0; vb < C::NVB; ++vb) scale_acc(oacc[vb], alpha);
@@ -1144,17 +1159,17 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     fin = (n + Cb - 1) / Cb == 1;
     slot = b * S + s;
   } else {
-    // the unit covers global tiles [a0, a1) of the batch's tile stream
+    // the unit covers positions [a0, a1) of the batch's cost stream
     const int U = p.num_splits;
-    const int64_t TT = uniform64(total_tiles(p.seq_lens, p.batch, lane));
-    if (TT == 0) return;
-    a0 = (int64_t)unit * TT / U;
-    a1 = (int64_t)(unit + 1) * TT / U;
+    const int64_t TC = uniform64(total_cost(p.seq_lens, p.batch, p.seg_cost, lane));
+    if (TC == 0) return;
+    a0 = (int64_t)unit * TC / U;
+    a1 = (int64_t)(unit + 1) * TC / U;
     if (a0 >= a1) return;
-    // first sequence whose tiles reach past a0, and its first global tile
+    // first sequence whose cost range reaches past a0, and where it starts
     for (int c0 = 0; c0 < p.batch; c0 += 64) {
       const int bl = c0 + lane;
-      const int ntl = bl < p.batch ? tiles_of(p.seq_lens[bl]) : 0;
+      const int ntl = bl < p.batch ? cost_of(p.seq_lens[bl], p.seg_cost) : 0;
       const int incl = wave_incl_scan(ntl, lane);
       const uint64_t past = __builtin_amdgcn_ballot_w64(bl < p.batch && st + incl > a0);
       if (past) {
@@ -1172,13 +1187,14 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     if (p.split_mode != 0) {
       const int n = p.seq_lens[b];
       const int nt = tiles_of(n);
-      const int64_t lo = (a0 > st ? a0 : st) - st;
-      const int64_t hi = (a1 < st + nt ? a1 : st + nt) - st;
+      const int64_t rs = st + (nt > 0 ? p.seg_cost : 0);  // position of tile 0
+      const int64_t lo = (a0 > rs ? a0 : rs) - rs;
+      const int64_t hi = (a1 < rs + nt ? a1 : rs + nt) - rs;
       ts = (int)lo * kTile;
       te = hi > lo ? min((int)hi * kTile, n) : ts;
       fin = lo == 0 && hi == nt;
       slot = unit + b;
-      st += nt;
+      st += cost_of(n, p.seg_cost);
     }
     if (te > ts) process(b, ts, te, fin, slot);
     if (p.split_mode == 0) break;
@@ -1196,6 +1212,7 @@ struct Stage2Params {
   void* o;
   float* lse;
   int32_t batch, heads, o_f32, split_mode, num_splits, head_groups, kgroups;
+  int32_t seg_cost;  // balanced mode: the same cost stream as stage 1
 };
 
 // One workgroup per (sequence, 8/KG heads, 256 output columns), 256 threads:
@@ -1252,11 +1269,11 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
     count = nseg;
   } else {
     const int U = p.num_splits;
-    // tiles before sequence b, and in total
+    // cost before sequence b, and in total
     int64_t before = 0, TT = 0;
     for (int c0 = 0; c0 < p.batch; c0 += 64) {
       const int bl = c0 + lane;
-      const int nt = bl < p.batch ? tiles_of(p.seq_lens[bl]) : 0;
+      const int nt = bl < p.batch ? cost_of(p.seq_lens[bl], p.seg_cost) : 0;
       const int incl = wave_incl_scan(nt, lane);
       const int tot = __shfl(incl, 63, 64);
       if (b >= c0 + 64) before += tot;
@@ -1271,8 +1288,9 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
       }
       return;
     }
-    const int uf = unit_of_tile(before, TT, U);
-    const int ul = unit_of_tile(before + nt - 1, TT, U);
+    const int64_t rs = before + p.seg_cost;  // position of the sequence's tile 0
+    const int uf = unit_of_tile(rs, TT, U);
+    const int ul = unit_of_tile(rs + nt - 1, TT, U);
     if (uf == ul) return;  // stage 1 wrote the final result
     first = uf + b;
     count = ul - uf + 1;
@@ -1364,6 +1382,15 @@ int launch_stage1_for(const HeadTiling& ht, const Stage1Params& sp, int grid, hi
 
 }  // namespace
 
+// What starting a segment costs, in tiles of the balanced cost stream: the
+// query rows of a workgroup's heads and one partial row per head, plus about
+// one tile of latency.  Measured on the dsv3 shape (128 heads per
+// workgroup) a segment start costs about as much as 8-9 tiles.
+int segment_cost_tiles(int heads, const HeadTiling& ht) {
+  const int per_wg = heads / ht.head_chunks;
+  return 1 + (per_wg + 15) / 16;
+}
+
 int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const HeadTiling ht = head_tiling(a.heads);
@@ -1385,6 +1412,7 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   sp.split_mode = a.split_mode;
   sp.num_splits = a.num_splits;
   sp.head_chunks = ht.head_chunks;
+  sp.seg_cost = segment_cost_tiles(a.heads, ht);
   sp.score_log2 = a.scale * kLog2e * (a.kv_fp8 ? a.k_scale : 1.f);
   sp.out_scale = a.kv_fp8 ? a.k_scale : 1.f;
 
@@ -1413,6 +1441,7 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   s2.o_f32 = a.o_f32;
   s2.split_mode = a.split_mode;
   s2.num_splits = a.num_splits;
+  s2.seg_cost = sp.seg_cost;
   // partial groups per head: about a quarter of the mean partial count per
   // sequence (units / batch + 1), a power of two up to 8
   const int per_seq = a.split_mode == 0 ? a.num_splits : a.num_splits / a.batch + 1;
