@@ -1307,54 +1307,64 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
     return (u + 1) * tiles_total / units > u * tiles_total / units;
   };
   const f32x2* ls_h = p.ws_ls + (size_t)first * H + h;  // partial k at ls_h[k * H]
-
-  // M = max of the partial lse of head h, over its KG groups x 32 lanes
-  float M = -INFINITY;
-  for (int k = g * 32 + j; k < count; k += 32 * KG)
-    if (live(k)) M = fmaxf(M, ls_h[(size_t)k * H][0]);
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
-  if (j == 0) red_m[row] = M;
-  __syncthreads();
-  for (int r = hl * KG; r < hl * KG + KG; ++r) M = fmaxf(M, red_m[r]);
-
-  // this group's partials k = g, g + KG, ...: weight e^(lse_k - M); the
-  // stored row is o_k * 2^-e_k, so it enters with e^(lse_k - M) * 2^e_k
-  float tot = 0.f;
-  f32x8 acc = {};
   const size_t stride = (size_t)H * DV;  // elements between consecutive partials
   const _Float16* src = p.ws_o + ((size_t)first * H + h) * DV + v;
-  auto add = [&](int k, const f16x8& x) {
-    if (!live(k)) return;  // a slot without a partial may hold anything
-    const f32x2 ls = ls_h[(size_t)k * H];
-    const float w = __expf(ls[0] - M);
-    tot += w;
-    acc += (w * ls[1]) * __builtin_convertvector(x, f32x8);
-  };
-  int k = g;
-  for (; k + (kS2Batch - 1) * KG < count; k += kS2Batch * KG) {
-    f16x8 x[kS2Batch];
-#pragma unroll
-    for (int i = 0; i < kS2Batch; ++i)
-      x[i] = *reinterpret_cast<const f16x8*>(src + (size_t)(k + i * KG) * stride);
-#pragma unroll
-    for (int i = 0; i < kS2Batch; ++i) add(k + i * KG, x[i]);
-  }
-  for (; k < count; k += KG) add(k, *reinterpret_cast<const f16x8*>(src + (size_t)k * stride));
 
-  // combine the KG groups of each head
+  // One pass over this group's partials k = g, g + KG, ..., kS2Batch at a
+  // time: all of a batch's rows and {lse, 2^e} pairs are loaded before any is
+  // used, then folded into a running max m, weight sum tot and accumulator
+  // (the stored row is o_k * 2^-e_k, so it enters with e^(lse_k - m) * 2^e_k)
+  float m = -INFINITY, tot = 0.f;
+  f32x8 acc = {};
+  for (int k0 = g; k0 < count; k0 += kS2Batch * KG) {
+    f16x8 x[kS2Batch];
+    f32x2 ls[kS2Batch];
+#pragma unroll
+    for (int i = 0; i < kS2Batch; ++i) {
+      const int k = k0 + i * KG;
+      const bool use = k < count && live(k);  // a slot without a partial may hold anything
+      x[i] = use ? *reinterpret_cast<const f16x8*>(src + (size_t)k * stride) : f16x8{};
+      ls[i] = use ? ls_h[(size_t)k * H] : f32x2{-INFINITY, 0.f};
+    }
+    float mb = m;
+#pragma unroll
+    for (int i = 0; i < kS2Batch; ++i) mb = fmaxf(mb, ls[i][0]);
+    if (mb == -INFINITY) continue;  // nothing live yet
+    const float r = __expf(m - mb);  // 0 while m is still -inf
+    tot *= r;
+    acc *= r;
+#pragma unroll
+    for (int i = 0; i < kS2Batch; ++i) {
+      const float w = __expf(ls[i][0] - mb);  // 0 for the unused entries
+      tot += w;
+      acc += (w * ls[i][1]) * __builtin_convertvector(x[i], f32x8);
+    }
+    m = mb;
+  }
+
+  // combine the KG groups of each head (every group saw at least one partial)
   if (KG > 1) {
     red_o[row][j] = acc;
-    if (j == 0) red_l[row] = tot;
+    if (j == 0) {
+      red_m[row] = m;
+      red_l[row] = tot;
+    }
     __syncthreads();
     if (g != 0) return;
-    for (int r = row + 1; r < row + KG; ++r) {
-      acc += red_o[r][j];
-      tot += red_l[r];
+    float M = m;
+    for (int r2 = row + 1; r2 < row + KG; ++r2) M = fmaxf(M, red_m[r2]);
+    const float r0 = __expf(m - M);
+    acc *= r0;
+    tot *= r0;
+    for (int r2 = row + 1; r2 < row + KG; ++r2) {
+      const float rr = __expf(red_m[r2] - M);
+      acc += rr * red_o[r2][j];
+      tot += rr * red_l[r2];
     }
+    m = M;
   }
   store_out8(p.o, p.o_f32, ((size_t)b * H + h) * DV + v, acc * (1.f / tot));
-  if (vc == 0 && j == 0) p.lse[(size_t)b * H + h] = M + __logf(tot);
+  if (vc == 0 && j == 0) p.lse[(size_t)b * H + h] = m + __logf(tot);
 }
 
 // ---------------------------------------------------------------- dispatch
