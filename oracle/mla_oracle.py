@@ -153,6 +153,47 @@ def decode(q_bits: np.ndarray, kv_bits: np.ndarray, block_table: np.ndarray,
     return np.stack(outs), np.stack(lses)
 
 
+# ---------------------------------------------------------------- multi-token decode
+
+def visible_keys(n: int, q_len: int, i: int) -> int:
+    """lshu.cn article, section 10 (verifying several new positions at once):
+    the sequence length n counts every key, the q_len new positions included,
+    so the context before them is n - q_len; query token i sits at absolute
+    position n - q_len + i and sees the keys at positions up to and including
+    it, i.e. the first n - q_len + i + 1 of them (none if that is < 1)."""
+    return max(0, min(n, n - q_len + i + 1))
+
+
+def decode_mtp(q_bits: np.ndarray, kv_bits: np.ndarray, block_table: np.ndarray,
+               seq_lens: np.ndarray, *, scale: float, k_scale: float, kv_dtype: str,
+               kv_lora_rank: int, batches: Optional[Sequence[int]] = None
+               ) -> Tuple[np.ndarray, np.ndarray]:
+    """Multi-token MLA decode: q_bits [B, q_len, H, D] bf16 bits.  Query token
+    i of sequence b attends to the first visible_keys(n_b, q_len, i) rows of
+    its cache (section 10's rectangle plus lower triangle), each exactly as in
+    ``decode``.  Returns o [B', q_len, H, kv_lora_rank] and lse [B', q_len, H]."""
+    B, q_len, H, D = q_bits.shape
+    NB, P, D2 = kv_bits.shape
+    if D2 != D:
+        raise ValueError("q and cache head sizes differ")
+    bits = kv_bits.reshape(NB * P, D)
+    sc = float(np.float32(scale))
+    idx = range(B) if batches is None else batches
+    outs, lses = [], []
+    for b in idx:
+        n = int(seq_lens[b])
+        K = decode_kv(gather_rows(bits, block_table[b], n, P), kv_dtype, k_scale)
+        ob, lb = [], []
+        for i in range(q_len):
+            o, lse = attend(bf16_bits_to_f64(q_bits[b, i]), K[:visible_keys(n, q_len, i)],
+                            kv_lora_rank, sc)
+            ob.append(o)
+            lb.append(lse)
+        outs.append(np.stack(ob))
+        lses.append(np.stack(lb))
+    return np.stack(outs), np.stack(lses)
+
+
 # ---------------------------------------------------------------- split-KV merge
 
 def segment_bounds(n: int, chunk: int) -> List[Tuple[int, int]]:
@@ -249,4 +290,5 @@ __all__ = [
     "ROPE_DIM", "bf16_bits_to_f64", "e4m3fn_bits_to_f64", "E4M3FN_VALUES", "decode_kv",
     "physical_slot", "gather_rows", "attend", "decode", "segment_bounds", "merge_partials",
     "merge_normalised", "segment_partial", "decode_split", "pages_split_count",
+    "visible_keys", "decode_mtp",
 ]

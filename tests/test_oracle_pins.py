@@ -383,3 +383,130 @@ def test_planted_mistakes_are_caught(monkeypatch):
                        ("physical_slot", slot_off_by_one), ("physical_slot", slot_transposed),
                        ("decode_kv", k_scale_ignored)):
         assert _pins_fail(monkeypatch, name, fake) > 0, (name, fake.__name__)
+
+
+# ---------------------------------------------------------------- multi-token decode
+# (lshu.cn article, section 10: q_len new positions verified at once; query i
+# sees the whole context and new positions 0..i)
+
+def mtp_case(seed, seq_lens, q_len, H=16, D=576, DV=512, P=16, kv="bf16", k_scale=1.0):
+    return W.small_case(seed=seed, batch=len(seq_lens), num_heads=H, head_size=D,
+                        kv_lora_rank=DV, page_size=P, seq_lens=seq_lens, kv_dtype=kv,
+                        k_scale=k_scale, q_len=q_len)
+
+
+def run_mtp(inp, **kw):
+    w = inp.workload
+    return O.decode_mtp(inp.q_bits, inp.kv_bits, inp.block_table, inp.seq_lens, scale=w.scale,
+                        k_scale=w.k_scale, kv_dtype=w.kv_dtype, kv_lora_rank=w.kv_lora_rank,
+                        **kw)
+
+
+def test_visibility_matches_the_pages_worked_example():
+    g = golden()["multi_token_verification"]
+    n, ql, ctx = g["kv_length"], g["query_length"], g["history_tokens"]
+    assert ctx == n - ql
+    for i in range(ql):
+        vis = O.visible_keys(n, ql, i)
+        assert vis == g["visible_keys_per_query"][i]
+        assert vis >= ctx  # the whole history is visible to every query
+        for j in range(ql):
+            assert (ctx + j < vis) == bool(g["new_position_visibility"][i][j])
+
+
+@pytest.mark.parametrize("kv,D,DV,lens,ql", [
+    ("bf16", 576, 512, (9, 40, 3), 3),
+    ("bf16", 576, 512, (17, 64), 8),
+    ("fp8_e4m3", 576, 512, (33, 8), 4),
+    ("bf16", 320, 256, (21, 2, 50), 2),
+])
+def test_mtp_matches_causal_sdpa(kv, D, DV, lens, ql):
+    """torch float64 SDPA with an explicit boolean mask key_t <= n - q_len + i."""
+    inp = mtp_case(seed=41, seq_lens=lens, q_len=ql, D=D, DV=DV, kv=kv,
+                   k_scale=float(np.float32(0.05)) if kv != "bf16" else 1.0)
+    o, lse = run_mtp(inp)
+    sc = float(np.float32(inp.workload.scale))
+    H = inp.workload.num_heads
+    for b, n in enumerate(lens):
+        K = dense_keys(inp, b)
+        q = q_of(inp, b).reshape(ql * H, D)  # row = token * H + head
+        tok = torch.arange(ql * H) // H
+        mask = torch.arange(n)[None, :] <= (n - ql + tok)[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q[None], K[None], K[None, :, :DV], attn_mask=mask[None], scale=sc)[0]
+        s = (q @ K.T) * sc
+        ref_lse = torch.logsumexp(s.masked_fill(~mask, -math.inf), dim=1)
+        assert np.abs(o[b].reshape(ql * H, DV) - ref.numpy()).max() < 1e-12
+        assert np.abs(lse[b].reshape(ql * H) - ref_lse.numpy()).max() < 1e-12
+
+
+def test_mtp_with_one_token_is_plain_decode():
+    flat = mtp_case(seed=42, seq_lens=(37, 100, 1), q_len=1)  # q [B, H, D]
+    o0, l0 = run(flat)
+    inp = W.DecodeInputs(workload=flat.workload, q_bits=flat.q_bits[:, None].copy(),
+                         kv_bits=flat.kv_bits, block_table=flat.block_table,
+                         seq_lens=flat.seq_lens)  # the same query as [B, 1, H, D]
+    o1, l1 = run_mtp(inp)
+    assert np.array_equal(o1[:, 0], o0) and np.array_equal(l1[:, 0], l0)
+
+
+def test_mtp_rows_reduce_to_single_token_decode_at_the_visible_length():
+    lens, ql = (12, 70), 5
+    inp = mtp_case(seed=43, seq_lens=lens, q_len=ql)
+    o, lse = run_mtp(inp)
+    for i in range(ql):
+        vis = [O.visible_keys(n, ql, i) for n in lens]
+        one = W.DecodeInputs(workload=inp.workload, q_bits=inp.q_bits[:, i].copy(),
+                             kv_bits=inp.kv_bits, block_table=inp.block_table,
+                             seq_lens=np.asarray(vis, dtype=np.int32))
+        oi, li = run(one)
+        assert np.array_equal(o[:, i], oi) and np.array_equal(lse[:, i], li)
+
+
+def test_mtp_identical_keys_closed_form():
+    """Every key equal: each query's weights are uniform over its visible keys,
+    so o is that row and lse = s + ln(visible)."""
+    lens, ql = (11,), 4
+    inp = mtp_case(seed=44, seq_lens=lens, q_len=ql)
+    P = inp.workload.page_size
+    kv = inp.kv_bits.copy()
+    row = kv[inp.block_table[0, 0], 0].copy()
+    kv[:] = row
+    inp = W.DecodeInputs(workload=inp.workload, q_bits=inp.q_bits, kv_bits=kv,
+                         block_table=inp.block_table, seq_lens=inp.seq_lens)
+    o, lse = run_mtp(inp)
+    v = O.bf16_bits_to_f64(row)
+    sc = float(np.float32(inp.workload.scale))
+    for i in range(ql):
+        s = (O.bf16_bits_to_f64(inp.q_bits[0, i]) @ v) * sc
+        assert np.abs(o[0, i] - v[None, :512]).max() < 1e-12
+        assert np.abs(lse[0, i] - (s + math.log(11 - ql + i + 1))).max() < 1e-12
+
+
+def test_mtp_rows_that_see_no_key():
+    """seq_len < q_len: the first q_len - n queries see nothing (o = 0,
+    lse = -inf, the empty sum); the others see 1..n keys."""
+    inp = mtp_case(seed=45, seq_lens=(2,), q_len=5)
+    o, lse = run_mtp(inp)
+    assert [O.visible_keys(2, 5, i) for i in range(5)] == [0, 0, 0, 1, 2]
+    assert np.all(o[0, :3] == 0) and np.all(np.isneginf(lse[0, :3]))
+    assert np.all(np.isfinite(lse[0, 3:]))
+
+
+def test_planted_visibility_mistakes_are_caught(monkeypatch):
+    """An off-by-one or a mirrored triangle in the causal rule of section 10
+    makes the SDPA-with-mask pin fail."""
+    def excludes_own_position(n, q_len, i):
+        return max(0, min(n, n - q_len + i))
+
+    def mirrored(n, q_len, i):
+        return max(0, min(n, n - i))
+
+    def no_mask(n, q_len, i):
+        return n
+
+    for fake in (excludes_own_position, mirrored, no_mask):
+        monkeypatch.setattr(OM, "visible_keys", fake)
+        with pytest.raises(AssertionError):
+            test_mtp_matches_causal_sdpa("bf16", 576, 512, (9, 40, 3), 3)
+        monkeypatch.undo()

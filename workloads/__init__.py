@@ -51,6 +51,9 @@ class Workload:
     seq_len_head: Optional[Sequence[int]] = None  # fixed leading lengths, rest drawn
     parity_splits: Sequence[int] = (1,)
     description: str = ""
+    # query tokens per sequence (multi-token decode: the last q_len positions
+    # are verified at once; q is then [B, q_len, H, D])
+    q_len: int = 1
 
     def draw_seq_lens(self, rng: np.random.Generator) -> np.ndarray:
         if self.seq_lens_fixed is not None:
@@ -89,6 +92,12 @@ WORKLOADS: Dict[str, Workload] = {
             page_size=64, num_blocks=16384, kv_dtype=FP8_E4M3, k_scale=float(np.float32(0.05)),
             scale=DSV3_SCALE, seq_len_range=(2048, 8192), parity_splits=(16, 1),
             description="B=128 H=128 D=576 fp8 e4m3 cache (k_scale 0.05), page 64, U[2048,8192]"),
+        Workload(
+            name="dsv3_mtp2", seed=6, batch=64, num_heads=128, head_size=576, kv_lora_rank=512,
+            page_size=64, num_blocks=8192, kv_dtype=BF16, k_scale=1.0, scale=DSV3_SCALE,
+            seq_len_range=(1024, 8192), parity_splits=(16, 1), q_len=2,
+            description="B=64 q_len=2 H=128 D=576/512 bf16 multi-token decode, page 64, "
+                        "8192 pages, seq_lens U[1024,8192]"),
     ]
 }
 
@@ -97,7 +106,7 @@ WORKLOADS: Dict[str, Workload] = {
 class DecodeInputs:
     """One decode batch, every array in its storage format (raw bits)."""
     workload: Workload
-    q_bits: np.ndarray          # uint16 [B, H, D]  (bf16 bits)
+    q_bits: np.ndarray          # uint16 [B, H, D] or [B, q_len, H, D] (bf16 bits)
     kv_bits: np.ndarray         # uint16 [NB, P, D] (bf16) or uint8 [NB, P, D] (fp8)
     block_table: np.ndarray     # int32 [B, max_blocks_per_seq]
     seq_lens: np.ndarray        # int32 [B]
@@ -166,7 +175,9 @@ def generate(workload: Workload | str, *, seq_lens: Optional[Sequence[int]] = No
     nb = num_blocks if num_blocks is not None else w.num_blocks
     table = make_block_table(rng, sl, w.page_size, nb)
     B = len(sl)
-    q = _normal_f32(rng, (B, w.num_heads, w.head_size))
+    qshape = (B, w.num_heads, w.head_size) if w.q_len == 1 else (B, w.q_len, w.num_heads,
+                                                                  w.head_size)
+    q = _normal_f32(rng, qshape)
     q_bits = f32_to_bf16_bits(q)
     pool = _normal_f32(rng, (nb, w.page_size, w.head_size))
     if w.kv_dtype == BF16:
@@ -180,13 +191,13 @@ def generate(workload: Workload | str, *, seq_lens: Optional[Sequence[int]] = No
 def small_case(*, seed: int, batch: int, num_heads: int, head_size: int, kv_lora_rank: int,
                page_size: int, seq_lens: Sequence[int], kv_dtype: str = BF16,
                k_scale: float = 1.0, extra_pages: int = 3, scale: float = DSV3_SCALE,
-               table_pad: int = 0) -> DecodeInputs:
+               table_pad: int = 0, q_len: int = 1) -> DecodeInputs:
     """A custom small batch (edge cases, ragged lengths) with the same recipe."""
     pages = sum((int(n) + page_size - 1) // page_size for n in seq_lens) + extra_pages
     w = Workload(name=f"case{seed}", seed=seed, batch=batch, num_heads=num_heads,
                  head_size=head_size, kv_lora_rank=kv_lora_rank, page_size=page_size,
                  num_blocks=max(1, pages), kv_dtype=kv_dtype, k_scale=k_scale, scale=scale,
-                 seq_lens_fixed=tuple(int(n) for n in seq_lens))
+                 seq_lens_fixed=tuple(int(n) for n in seq_lens), q_len=q_len)
     inp = generate(w)
     if table_pad:
         inp.block_table = np.pad(inp.block_table, ((0, 0), (0, table_pad)))
