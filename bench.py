@@ -49,17 +49,21 @@ def kernel_hash():
 def algorithmic(inp):
     """Bytes and FLOPs the method itself must move / compute (no workspace,
     no padding): the cache rows read once, q, o, lse, the table entries and
-    seq_lens; FLOPs = 2 H sum(n) (D + D_v)."""
+    seq_lens; FLOPs = 2 H (D + D_v) times the keys each query token sees
+    (sum(n) for single-token decode; multi-token decode: query token i sees
+    n - q_len + 1 + i keys)."""
     import numpy as np
     w = inp.workload
     n = np.asarray(inp.seq_lens, dtype=np.int64)
     e_kv = 2 if w.kv_dtype == "bf16" else 1
     B, H, D, DV, P = w.batch, w.num_heads, w.head_size, w.kv_lora_rank, w.page_size
+    ql = w.q_len
     kv = int(n.sum()) * D * e_kv
     table = int(((n + P - 1) // P).sum()) * 4
-    stage1 = kv + B * H * D * 2 + table + 4 * B
-    total = stage1 + B * H * DV * 2 + B * H * 4
-    flops = 2 * H * int(n.sum()) * (D + DV)
+    stage1 = kv + B * ql * H * D * 2 + table + 4 * B
+    total = stage1 + B * ql * H * DV * 2 + B * ql * H * 4
+    seen = sum(int(np.clip(n - ql + 1 + i, 0, n).sum()) for i in range(ql))
+    flops = 2 * H * seen * (D + DV)
     return {"kv_bytes": kv, "stage1_bytes": stage1, "total_bytes": total, "flops": flops,
             "tokens": int(n.sum())}
 
@@ -78,10 +82,10 @@ def cpu_baseline(inp, alg, budget_s=25.0):
         threads = None
     done, tok = 0, 0
     t0 = time.perf_counter()
+    fn = oracle.decode if w.q_len == 1 else oracle.decode_mtp
     for b in range(w.batch):
-        oracle.decode(inp.q_bits, inp.kv_bits, inp.block_table, inp.seq_lens, scale=w.scale,
-                      k_scale=w.k_scale, kv_dtype=w.kv_dtype, kv_lora_rank=w.kv_lora_rank,
-                      batches=[b])
+        fn(inp.q_bits, inp.kv_bits, inp.block_table, inp.seq_lens, scale=w.scale,
+           k_scale=w.k_scale, kv_dtype=w.kv_dtype, kv_lora_rank=w.kv_lora_rank, batches=[b])
         done += 1
         tok += int(inp.seq_lens[b])
         if time.perf_counter() - t0 > budget_s:
@@ -201,16 +205,18 @@ def main():
     shape = mla.shape_of(q, kv, bt)
     max_len, tot = int(inp.seq_lens.max()), int(inp.seq_lens.sum())
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    ql = w.q_len
     if args.split == "plan":
-        mode, splits, ws_bytes = mla.mla_plan(shape, max_len, tot, cus)
+        mode, splits, ws_bytes = mla.mla_plan(shape, max_len, tot, cus, q_len=ql)
     elif args.split == "pages":
         mode, splits = mla.SPLIT_PER_SEQUENCE, mla.mla_pages_split_count(max_len, cus)
-        ws_bytes = mla.mla_workspace_size(shape, mode, splits)
+        ws_bytes = mla.mla_workspace_size(shape, mode, splits, ql)
     else:
         mode, splits, ws_bytes = mla.SPLIT_PER_SEQUENCE, 1, 0
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    o = torch.empty((w.batch, w.num_heads, w.kv_lora_rank), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((w.batch, w.num_heads), dtype=torch.float32, device=dev)
+    rows = (w.batch, w.num_heads) if ql == 1 else (w.batch, ql, w.num_heads)
+    o = torch.empty(rows + (w.kv_lora_rank,), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(rows, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     calls = [mla.PreparedDecode(q, k, b, sl, w.scale, w.page_size, w.k_scale, splits, mode, o,
                                 lse, ws, stream=stream.cuda_stream) for (k, b) in sets]
@@ -277,7 +283,7 @@ def main():
         "config": {"workload": f"{w.name}: {w.description}", "batch": w.batch,
                    "heads": w.num_heads, "head_size": w.head_size,
                    "kv_lora_rank": w.kv_lora_rank, "page_size": w.page_size,
-                   "total_tokens": alg["tokens"], "split_mode": int(mode),
+                   "total_tokens": alg["tokens"], "q_len": ql, "split_mode": int(mode),
                    "num_kv_splits": int(splits), "seed": w.seed},
         "tflops": round(tflops, 1),
         "tokens_heads_per_s": round(alg["tokens"] * w.num_heads / (ms_step * 1e-3), 1),

@@ -73,7 +73,8 @@ typedef enum mla_status {
   MLA_ERR_WORKSPACE = 7, /* workspace NULL or smaller than mla_workspace_size() for the
                             same shape, split mode and split count                       */
   MLA_ERR_LAUNCH = 8,    /* HIP reported an error when the kernels were enqueued        */
-  MLA_ERR_ARGUMENT = 9   /* a non-finite or non-positive scale / k_scale, or num_cus < 1 */
+  MLA_ERR_ARGUMENT = 9   /* a non-finite or non-positive scale / k_scale, num_cus < 1,
+                            q_len outside [1, MLA_MAX_Q_LEN], or a misaligned pointer    */
 } mla_status;
 
 typedef enum mla_dtype {
@@ -110,6 +111,7 @@ typedef enum mla_split_mode {
 
 #define MLA_MAX_KV_SPLITS 65536
 #define MLA_ROPE_DIM 64
+#define MLA_MAX_Q_LEN 16 /* query tokens per sequence in multi-token decode */
 
 /* Problem shape.  Layouts (all row-major, densely packed unless noted):
  *   q           [batch, num_heads, head_size]              q_dtype (bf16)
@@ -206,6 +208,45 @@ mla_status mla_decode_stage2(const mla_shape* shape, const void* q, const void* 
                              int32_t page_size, float k_scale, int32_t num_kv_splits,
                              int32_t split_mode, void* o, float* lse, void* workspace,
                              size_t workspace_bytes, void* hip_stream);
+
+/* Multi-token decode (verification of q_len new positions per sequence,
+ * "vLLM 中 Attention Kernel 如何并行处理多个请求", section 十).  Each sequence
+ * has q_len query tokens; seq_lens[b] = n counts every key, the q_len new
+ * positions included (their cache rows are written before the call), so the
+ * context before them is n - q_len.  Query token i sits at absolute position
+ * n - q_len + i and sees the keys at positions <= n - q_len + i: the whole
+ * context and new positions 0..i (a rectangle plus a lower triangle).
+ *
+ * Layouts: q [batch, q_len, num_heads, head_size], o [batch, q_len, num_heads,
+ * kv_lora_rank], lse [batch, q_len, num_heads]; shape->num_heads is H per
+ * token.  Every other argument, check and ownership rule is that of the
+ * corresponding single-token function, which is the case q_len = 1.  Plan
+ * and size the workspace with the _mtp functions (the q_len x H rows share
+ * one cache stream).  A query row that sees no key (seq_lens[b] < q_len, or
+ * 0) gets o = 0 and lse = -inf.  q_len outside [1, MLA_MAX_Q_LEN] is
+ * MLA_ERR_ARGUMENT. */
+mla_status mla_plan_mtp(const mla_shape* shape, int32_t q_len, int32_t max_seq_len,
+                        int64_t total_seq_len, int32_t num_cus, int32_t deterministic,
+                        int32_t* split_mode, int32_t* num_kv_splits, size_t* workspace_bytes);
+size_t mla_workspace_size_mtp(const mla_shape* shape, int32_t q_len, int32_t split_mode,
+                              int32_t num_kv_splits);
+mla_status mla_decode_mtp(const mla_shape* shape, int32_t q_len, const void* q,
+                          const void* kv_cache, const int32_t* block_table,
+                          const int32_t* seq_lens, float scale, int32_t page_size, float k_scale,
+                          int32_t num_kv_splits, int32_t split_mode, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes, void* hip_stream);
+mla_status mla_decode_mtp_stage1(const mla_shape* shape, int32_t q_len, const void* q,
+                                 const void* kv_cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, float scale, int32_t page_size,
+                                 float k_scale, int32_t num_kv_splits, int32_t split_mode,
+                                 void* o, float* lse, void* workspace, size_t workspace_bytes,
+                                 void* hip_stream);
+mla_status mla_decode_mtp_stage2(const mla_shape* shape, int32_t q_len, const void* q,
+                                 const void* kv_cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, float scale, int32_t page_size,
+                                 float k_scale, int32_t num_kv_splits, int32_t split_mode,
+                                 void* o, float* lse, void* workspace, size_t workspace_bytes,
+                                 void* hip_stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char* mla_status_string(int32_t status);

@@ -9,11 +9,13 @@ be loaded, every call raises.
     o, lse = mla_decode(q, kv_cache, block_table, seq_lens, scale, page_size,
                         k_scale, num_kv_splits)
 
-``q`` [B, H, D] bf16 = [q_nope (D_v) | q_pe (64)]; ``kv_cache``
+``q`` [B, H, D] bf16 = [q_nope (D_v) | q_pe (64)], or [B, q_len, H, D] for a
+multi-token decode (query token i of a sequence with n keys sees positions
+< n - q_len + 1 + i); ``kv_cache``
 [num_blocks, page_size, D] bf16 or fp8 e4m3fn with rows [kv_c | k_pe];
 ``block_table`` [B, max_blocks_per_seq] int32; ``seq_lens`` [B] int32.
 Returns ``o`` [B, H, D_v] (bf16 by default) and ``lse`` [B, H] float32
-(natural log).
+(natural log), or [B, q_len, H, D_v] and [B, q_len, H].
 """
 from __future__ import annotations
 
@@ -35,6 +37,7 @@ MLA_ERR_SHAPE, MLA_ERR_SPLITS, MLA_ERR_WORKSPACE, MLA_ERR_LAUNCH, MLA_ERR_ARGUME
 MLA_BF16, MLA_FP8_E4M3, MLA_FP32 = 0, 1, 2
 SPLIT_PER_SEQUENCE, SPLIT_BALANCED = 0, 1
 MLA_MAX_KV_SPLITS = 65536
+MLA_MAX_Q_LEN = 16
 
 
 class MlaShape(ctypes.Structure):
@@ -69,11 +72,20 @@ def load_library():
         lib.mla_plan.argtypes = [shp, i32, i64, i32, i32, ctypes.POINTER(i32),
                                  ctypes.POINTER(i32), ctypes.POINTER(sz)]
         lib.mla_plan.restype = i32
+        lib.mla_plan_mtp.argtypes = [shp, i32, i32, i64, i32, i32, ctypes.POINTER(i32),
+                                     ctypes.POINTER(i32), ctypes.POINTER(sz)]
+        lib.mla_plan_mtp.restype = i32
         lib.mla_workspace_size.argtypes = [shp, i32, i32]
         lib.mla_workspace_size.restype = sz
+        lib.mla_workspace_size_mtp.argtypes = [shp, i32, i32, i32]
+        lib.mla_workspace_size_mtp.restype = sz
         for fn in (lib.mla_decode, lib.mla_decode_stage1, lib.mla_decode_stage2):
             fn.argtypes = [shp, vp, vp, vp, vp, ctypes.c_float, i32, ctypes.c_float, i32, i32,
                            vp, vp, vp, sz, vp]
+            fn.restype = i32
+        for fn in (lib.mla_decode_mtp, lib.mla_decode_mtp_stage1, lib.mla_decode_mtp_stage2):
+            fn.argtypes = [shp, i32, vp, vp, vp, vp, ctypes.c_float, i32, ctypes.c_float, i32,
+                           i32, vp, vp, vp, sz, vp]
             fn.restype = i32
         lib.mla_status_string.argtypes = [i32]
         lib.mla_status_string.restype = ctypes.c_char_p
@@ -107,18 +119,19 @@ def mla_pages_split_count(max_seq_len: int, num_cus: int) -> int:
     return int(load_library().mla_pages_split_count(int(max_seq_len), int(num_cus)))
 
 
-def mla_workspace_size(shape: MlaShape, split_mode: int, num_kv_splits: int) -> int:
-    return int(load_library().mla_workspace_size(ctypes.byref(shape), int(split_mode),
-                                                 int(num_kv_splits)))
+def mla_workspace_size(shape: MlaShape, split_mode: int, num_kv_splits: int,
+                       q_len: int = 1) -> int:
+    return int(load_library().mla_workspace_size_mtp(ctypes.byref(shape), int(q_len),
+                                                     int(split_mode), int(num_kv_splits)))
 
 
 def mla_plan(shape: MlaShape, max_seq_len: int, total_seq_len: int = 0, num_cus: int = 256,
-             deterministic: bool = False) -> Tuple[int, int, int]:
+             deterministic: bool = False, q_len: int = 1) -> Tuple[int, int, int]:
     """Returns (split_mode, num_kv_splits, workspace_bytes)."""
     mode, splits, ws = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_size_t()
-    st = load_library().mla_plan(ctypes.byref(shape), int(max_seq_len), int(total_seq_len),
-                                 int(num_cus), 1 if deterministic else 0, ctypes.byref(mode),
-                                 ctypes.byref(splits), ctypes.byref(ws))
+    st = load_library().mla_plan_mtp(ctypes.byref(shape), int(q_len), int(max_seq_len),
+                                     int(total_seq_len), int(num_cus), 1 if deterministic else 0,
+                                     ctypes.byref(mode), ctypes.byref(splits), ctypes.byref(ws))
     if st != MLA_OK:
         _raise(st, "mla_plan")
     return mode.value, splits.value, ws.value
@@ -147,10 +160,12 @@ def _dtype_code(t):
 
 
 def shape_of(q, kv_cache, block_table, *, kv_dtype=None, o_dtype=None) -> MlaShape:
+    """The mla_shape of a call; q is [B, H, D] or [B, q_len, H, D] (H per token)."""
     torch = _torch()
-    if q.dim() != 3 or kv_cache.dim() != 3 or block_table.dim() != 2:
-        raise ValueError("expected q [B,H,D], kv_cache [num_blocks,page,D], block_table [B,W]")
-    B, H, D = q.shape
+    if q.dim() not in (3, 4) or kv_cache.dim() != 3 or block_table.dim() != 2:
+        raise ValueError("expected q [B,H,D] or [B,q_len,H,D], kv_cache [num_blocks,page,D], "
+                         "block_table [B,W]")
+    B, H, D = q.shape[0], q.shape[-2], q.shape[-1]
     return make_shape(B, H, D, kv_cache.shape[1], kv_cache.shape[0], block_table.shape[1],
                       kv_dtype=_kv_code(kv_cache, kv_dtype),
                       o_dtype=_dtype_code(o_dtype or torch.bfloat16),
@@ -185,6 +200,8 @@ def mla_decode(q, kv_cache, block_table, seq_lens, scale: float, page_size: int,
         o_dtype = o.dtype
     shape = shape_of(q, kv_cache, block_table, kv_dtype=kv_dtype, o_dtype=o_dtype)
     B, H = shape.batch, shape.num_heads
+    q_len = q.shape[1] if q.dim() == 4 else 1
+    rows = (B, q_len, H) if q.dim() == 4 else (B, H)
     if num_kv_splits is None:
         if max_seq_len is None:
             max_seq_len = int(seq_lens.max().item()) if B else 0
@@ -193,18 +210,19 @@ def mla_decode(q, kv_cache, block_table, seq_lens, scale: float, page_size: int,
         if num_cus is None:
             num_cus = torch.cuda.get_device_properties(q.device).multi_processor_count
         split_mode, num_kv_splits, _ = mla_plan(shape, max_seq_len, total_seq_len or 0,
-                                                num_cus, deterministic)
+                                                num_cus, deterministic, q_len=q_len)
     elif split_mode is None:
         split_mode = SPLIT_PER_SEQUENCE
-    ws_need = mla_workspace_size(shape, split_mode, num_kv_splits)
+    ws_need = mla_workspace_size(shape, split_mode, num_kv_splits, q_len)
     if o is None:
-        o = torch.empty((B, H, shape.kv_lora_rank), dtype=o_dtype or torch.bfloat16,
+        o = torch.empty(rows + (shape.kv_lora_rank,), dtype=o_dtype or torch.bfloat16,
                         device=q.device)
     if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    if (tuple(o.shape) != (B, H, shape.kv_lora_rank) or tuple(lse.shape) != (B, H)
+        lse = torch.empty(rows, dtype=torch.float32, device=q.device)
+    if (tuple(o.shape) != rows + (shape.kv_lora_rank,) or tuple(lse.shape) != rows
             or lse.dtype != torch.float32 or not o.is_contiguous() or not lse.is_contiguous()):
-        raise ValueError("o must be [B,H,kv_lora_rank] and lse [B,H] float32, contiguous")
+        raise ValueError("o must be [B,(q_len,)H,kv_lora_rank] and lse [B,(q_len,)H] float32, "
+                         "contiguous")
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -213,9 +231,9 @@ def mla_decode(q, kv_cache, block_table, seq_lens, scale: float, page_size: int,
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
-    fn = {"both": lib.mla_decode, "stage1": lib.mla_decode_stage1,
-          "stage2": lib.mla_decode_stage2}[stages]
-    st = fn(ctypes.byref(shape), q.data_ptr(), kv_cache.data_ptr(),
+    fn = {"both": lib.mla_decode_mtp, "stage1": lib.mla_decode_mtp_stage1,
+          "stage2": lib.mla_decode_mtp_stage2}[stages]
+    st = fn(ctypes.byref(shape), int(q_len), q.data_ptr(), kv_cache.data_ptr(),
                         block_table.data_ptr(), seq_lens.data_ptr(), float(scale),
                         int(page_size), float(k_scale), int(num_kv_splits), int(split_mode),
                         o.data_ptr(), lse.data_ptr(), ws_ptr, int(ws_bytes), stream)
@@ -236,19 +254,20 @@ class PreparedDecode:
         self.lib = load_library()
         self.keep = (q, kv_cache, block_table, seq_lens, o, lse, workspace)
         self.shape = shape_of(q, kv_cache, block_table, kv_dtype=kv_dtype, o_dtype=o.dtype)
-        need = mla_workspace_size(self.shape, split_mode, num_kv_splits)
+        q_len = q.shape[1] if q.dim() == 4 else 1
+        need = mla_workspace_size(self.shape, split_mode, num_kv_splits, q_len)
         if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
             raise MlaError(MLA_ERR_WORKSPACE, "workspace too small")
         if stream is None:
             stream = torch.cuda.current_stream(q.device).cuda_stream
-        self.args = (ctypes.byref(self.shape), q.data_ptr(), kv_cache.data_ptr(),
+        self.args = (ctypes.byref(self.shape), int(q_len), q.data_ptr(), kv_cache.data_ptr(),
                      block_table.data_ptr(), seq_lens.data_ptr(), float(scale), int(page_size),
                      float(k_scale), int(num_kv_splits), int(split_mode), o.data_ptr(),
                      lse.data_ptr(), workspace.data_ptr() if workspace is not None else None,
                      workspace.numel() * workspace.element_size() if workspace is not None else 0,
                      stream)
-        self.fns = {"both": self.lib.mla_decode, "stage1": self.lib.mla_decode_stage1,
-                    "stage2": self.lib.mla_decode_stage2}
+        self.fns = {"both": self.lib.mla_decode_mtp, "stage1": self.lib.mla_decode_mtp_stage1,
+                    "stage2": self.lib.mla_decode_mtp_stage2}
 
     def __call__(self, stages: str = "both"):
         st = self.fns[stages](*self.args)

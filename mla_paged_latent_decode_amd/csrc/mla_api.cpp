@@ -77,6 +77,15 @@ static mla_status check_shape(const mla_shape* s) {
 
 static bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// The row shape of a multi-token decode: q_len query tokens x H heads are the
+// kernels' rows (row = token * H + head), so q [B, q_len, H, D] is q [B, rows, D].
+static bool row_shape(const mla_shape* s, int32_t q_len, mla_shape* out) {
+  if (!s || q_len < 1 || q_len > MLA_MAX_Q_LEN) return false;
+  *out = *s;
+  out->num_heads = s->num_heads * q_len;
+  return true;
+}
+
 extern "C" {
 
 int32_t mla_pages_split_count(int32_t max_seq_len, int32_t num_cus) {
@@ -87,7 +96,11 @@ int32_t mla_pages_split_count(int32_t max_seq_len, int32_t num_cus) {
   return (int32_t)s;
 }
 
-size_t mla_workspace_size(const mla_shape* shape, int32_t split_mode, int32_t num_kv_splits) {
+size_t mla_workspace_size_mtp(const mla_shape* shape, int32_t q_len, int32_t split_mode,
+                              int32_t num_kv_splits) {
+  mla_shape rs;
+  if (!row_shape(shape, q_len, &rs)) return 0;
+  shape = &rs;
   if (check_shape(shape) != MLA_OK) return 0;
   if (num_kv_splits < 1 || num_kv_splits > MLA_MAX_KV_SPLITS) return 0;
   return workspace_layout(shape->batch, shape->num_heads, shape->kv_lora_rank, split_mode,
@@ -95,10 +108,19 @@ size_t mla_workspace_size(const mla_shape* shape, int32_t split_mode, int32_t nu
       .total;
 }
 
-mla_status mla_plan(const mla_shape* shape, int32_t max_seq_len, int64_t total_seq_len,
-                    int32_t num_cus, int32_t deterministic, int32_t* split_mode,
-                    int32_t* num_kv_splits, size_t* workspace_bytes) {
+size_t mla_workspace_size(const mla_shape* shape, int32_t split_mode, int32_t num_kv_splits) {
+  return mla_workspace_size_mtp(shape, 1, split_mode, num_kv_splits);
+}
+
+mla_status mla_plan_mtp(const mla_shape* shape, int32_t q_len, int32_t max_seq_len,
+                        int64_t total_seq_len, int32_t num_cus, int32_t deterministic,
+                        int32_t* split_mode, int32_t* num_kv_splits, size_t* workspace_bytes) {
   mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  mla_shape rs;
+  if (!row_shape(shape, q_len, &rs)) return MLA_ERR_ARGUMENT;
+  shape = &rs;
+  st = check_shape(shape);
   if (st != MLA_OK) return st;
   if (!split_mode || !num_kv_splits || !workspace_bytes) return MLA_ERR_NULL;
   if (num_cus < 1 || max_seq_len < 0) return MLA_ERR_ARGUMENT;
@@ -128,13 +150,26 @@ mla_status mla_plan(const mla_shape* shape, int32_t max_seq_len, int64_t total_s
   return MLA_OK;
 }
 
-static mla_status decode_stages(const mla_shape* shape, const void* q, const void* kv_cache,
+mla_status mla_plan(const mla_shape* shape, int32_t max_seq_len, int64_t total_seq_len,
+                    int32_t num_cus, int32_t deterministic, int32_t* split_mode,
+                    int32_t* num_kv_splits, size_t* workspace_bytes) {
+  return mla_plan_mtp(shape, 1, max_seq_len, total_seq_len, num_cus, deterministic, split_mode,
+                      num_kv_splits, workspace_bytes);
+}
+
+static mla_status decode_stages(const mla_shape* shape, int32_t q_len, const void* q,
+                                const void* kv_cache,
                                 const int32_t* block_table, const int32_t* seq_lens,
                                 float scale, int32_t page_size, float k_scale,
                                 int32_t num_kv_splits, int32_t split_mode, void* o, float* lse,
                                 void* workspace, size_t workspace_bytes, void* hip_stream,
                                 int stages) {
   mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  mla_shape rs;
+  if (!row_shape(shape, q_len, &rs)) return MLA_ERR_ARGUMENT;
+  shape = &rs;
+  st = check_shape(shape);
   if (st != MLA_OK) return st;
   if (!q || !kv_cache || !block_table || !seq_lens || !o || !lse) return MLA_ERR_NULL;
   if (page_size != shape->page_size) return MLA_ERR_PAGE_SIZE;
@@ -167,7 +202,8 @@ static mla_status decode_stages(const mla_shape* shape, const void* q, const voi
   a.ws_o = wl.total ? workspace : nullptr;
   a.ws_ls = wl.total ? reinterpret_cast<char*>(workspace) + wl.lse_offset : nullptr;
   a.batch = shape->batch;
-  a.heads = shape->num_heads;
+  a.heads = shape->num_heads;  // rows: q_len tokens x heads
+  a.q_len = q_len;
   a.head_size = shape->head_size;
   a.d_v = shape->kv_lora_rank;
   a.page_size = shape->page_size;
@@ -186,7 +222,17 @@ mla_status mla_decode(const mla_shape* shape, const void* q, const void* kv_cach
                       int32_t page_size, float k_scale, int32_t num_kv_splits,
                       int32_t split_mode, void* o, float* lse, void* workspace,
                       size_t workspace_bytes, void* hip_stream) {
-  return decode_stages(shape, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
+  return decode_stages(shape, 1, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
+                       num_kv_splits, split_mode, o, lse, workspace, workspace_bytes, hip_stream,
+                       kBothStages);
+}
+
+mla_status mla_decode_mtp(const mla_shape* shape, int32_t q_len, const void* q,
+                      const void* kv_cache, const int32_t* block_table, const int32_t* seq_lens,
+                      float scale, int32_t page_size, float k_scale, int32_t num_kv_splits,
+                      int32_t split_mode, void* o, float* lse, void* workspace,
+                      size_t workspace_bytes, void* hip_stream) {
+  return decode_stages(shape, q_len, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
                        num_kv_splits, split_mode, o, lse, workspace, workspace_bytes, hip_stream,
                        kBothStages);
 }
@@ -196,7 +242,17 @@ mla_status mla_decode_stage1(const mla_shape* shape, const void* q, const void* 
                              int32_t page_size, float k_scale, int32_t num_kv_splits,
                              int32_t split_mode, void* o, float* lse, void* workspace,
                              size_t workspace_bytes, void* hip_stream) {
-  return decode_stages(shape, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
+  return decode_stages(shape, 1, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
+                       num_kv_splits, split_mode, o, lse, workspace, workspace_bytes, hip_stream,
+                       kStage1);
+}
+
+mla_status mla_decode_mtp_stage1(const mla_shape* shape, int32_t q_len, const void* q,
+                      const void* kv_cache, const int32_t* block_table, const int32_t* seq_lens,
+                      float scale, int32_t page_size, float k_scale, int32_t num_kv_splits,
+                      int32_t split_mode, void* o, float* lse, void* workspace,
+                      size_t workspace_bytes, void* hip_stream) {
+  return decode_stages(shape, q_len, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
                        num_kv_splits, split_mode, o, lse, workspace, workspace_bytes, hip_stream,
                        kStage1);
 }
@@ -206,7 +262,17 @@ mla_status mla_decode_stage2(const mla_shape* shape, const void* q, const void* 
                              int32_t page_size, float k_scale, int32_t num_kv_splits,
                              int32_t split_mode, void* o, float* lse, void* workspace,
                              size_t workspace_bytes, void* hip_stream) {
-  return decode_stages(shape, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
+  return decode_stages(shape, 1, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
+                       num_kv_splits, split_mode, o, lse, workspace, workspace_bytes, hip_stream,
+                       kStage2);
+}
+
+mla_status mla_decode_mtp_stage2(const mla_shape* shape, int32_t q_len, const void* q,
+                      const void* kv_cache, const int32_t* block_table, const int32_t* seq_lens,
+                      float scale, int32_t page_size, float k_scale, int32_t num_kv_splits,
+                      int32_t split_mode, void* o, float* lse, void* workspace,
+                      size_t workspace_bytes, void* hip_stream) {
+  return decode_stages(shape, q_len, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
                        num_kv_splits, split_mode, o, lse, workspace, workspace_bytes, hip_stream,
                        kStage2);
 }
@@ -222,7 +288,7 @@ const char* mla_status_string(int32_t status) {
     case MLA_ERR_SPLITS: return "MLA_ERR_SPLITS: num_kv_splits or split_mode out of range";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
     case MLA_ERR_LAUNCH: return "MLA_ERR_LAUNCH: HIP kernel launch failed";
-    case MLA_ERR_ARGUMENT: return "MLA_ERR_ARGUMENT: non-finite/non-positive scale or k_scale, num_cus < 1, or a misaligned pointer";
+    case MLA_ERR_ARGUMENT: return "MLA_ERR_ARGUMENT: non-finite/non-positive scale or k_scale, num_cus < 1, q_len outside [1, MLA_MAX_Q_LEN], or a misaligned pointer";
     default: return "unknown mla_status";
   }
 }

@@ -72,7 +72,8 @@ struct DecodeArgs {
   void* ws_o;
   void* ws_ls;
   int32_t batch;
-  int32_t heads;
+  int32_t heads;  // rows: q_len query tokens x heads per token
+  int32_t q_len;  // query tokens per sequence (1: plain decode)
   int32_t head_size;
   int32_t d_v;
   int32_t page_size;

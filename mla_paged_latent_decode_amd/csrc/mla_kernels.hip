@@ -231,6 +231,10 @@ struct Stage1Params {
   int32_t batch, heads, page_size, bt_stride;
   int32_t o_f32, split_mode, num_splits, head_chunks;
   int32_t seg_cost;  // balanced mode: virtual tiles charged per sequence start
+  // Multi-token decode: the rows are q_len query tokens x heads_per_token
+  // heads (row = token * heads_per_token + head).  Token i of a sequence with
+  // n keys sees positions t < n - q_len + 1 + i.  Plain decode: q_len = 1.
+  int32_t q_len, heads_per_token;
   float score_log2;  // scale * log2(e) (* k_scale for fp8 caches)
   float out_scale;   // 1, or k_scale for fp8 caches
 };
@@ -400,8 +404,12 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   const int P = p.page_size;
 
   // ---------------- one segment [ts, te) of sequence b
-  auto process = [&](int b, int ts, int te, bool final_out, int slot) __attribute__((always_inline)) {
+  auto process = [&](int b, int ts, int te, bool final_out, int slot, int vis_n) __attribute__((always_inline)) {
     const int n_tiles = (te - ts + kTile - 1) / kTile;
+    // this lane's row sees positions t < row_end (causal limit of its query
+    // token; vis_n = n - q_len + 1 is the limit of token 0)
+    const int row_end =
+        vis_n + (h0 + (HPW == 32 ? (lane & 31) : (lane & 15))) / p.heads_per_token;
     // page cursor of the next 16-position half to load
     int cur_lb = ts / P;
     int cur_off = ts - cur_lb * P;
@@ -659,7 +667,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
         const int nvalid = min(kTile, te - (ts + j * kTile));
         const TileLoad tl = prepare(j + AHEAD);
 
-        float mt = -INFINITY, alpha = 1.f;
+        float mt = -INFINITY, alpha = 1.f, m_exp = 0.f;
         bool rescale = false;
         bf16x8 p0, p1;
         f32x16& sv = s_cur;  // scores of tile j, turned into weights in place
@@ -685,13 +693,16 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           if constexpr (ks < 4) {
             mt = fmaxf(mt, fmaxf(fmaxf(sv[4 * ks], sv[4 * ks + 1]), fmaxf(sv[4 * ks + 2], sv[4 * ks + 3])));
           } else if constexpr (ks == 4) {
-            // position of sv[r] is 8*(r/4) + 4*(lane/32) + r%4
-            if (nvalid < kTile) {
+            // position of sv[r] is 8*(r/4) + 4*(lane/32) + r%4; mask past the
+            // segment and past the row's causal limit (multi-token decode)
+            const int t0 = ts + j * kTile;
+            if (nvalid < kTile || t0 + kTile > vis_n) {
+              const int lim = min(nvalid, row_end - t0);
               mt = -INFINITY;
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
                 const int t = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (t >= nvalid) sv[r] = -INFINITY;
+                if (t >= lim) sv[r] = -INFINITY;
                 mt = fmaxf(mt, sv[r]);
               }
             }
@@ -703,17 +714,21 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
             if (j == 0) {
               m_run = m_new;  // nothing accumulated yet: no rescale
             } else if (__builtin_amdgcn_ballot_w64(m_new > m_run + kTau)) {
-              alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+              // a row that has seen no position yet has nothing to rescale
+              alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
               rescale = true;
               m_run = m_new;
               l_part *= alpha;
               lr_part *= alpha;
             }
+            // exponent base: a row with no visible position yet (m = -inf)
+            // takes 0, so its masked scores give weight 0, not NaN
+            m_exp = m_run == -INFINITY ? 0.f : m_run;
           } else {
             static_for<16>([&](auto rc) __attribute__((always_inline)) {
               constexpr int r = decltype(rc)::value;
               if constexpr (6 + r * E / 16 == ks) {
-                sv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], p.score_log2, -m_run));
+                sv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], p.score_log2, -m_exp));
                 l_part += sv[r];
                 if constexpr (r & 1) {
                   const bf16x2 pk = __builtin_convertvector((f32x2){sv[r - 1], sv[r]}, bf16x2);
@@ -887,12 +902,15 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
             q1 = q2;
           });
         }
-        // position of s[r] is 8*(r/4) + 4*(lane/32) + r%4; mask past the segment
-        if (nvalid < kTile) {
+        // position of s[r] is 8*(r/4) + 4*(lane/32) + r%4; mask past the
+        // segment and past the row's causal limit (multi-token decode)
+        const int t0 = ts + i * kTile;
+        if (nvalid < kTile || t0 + kTile > vis_n) {
+          const int lim = min(nvalid, row_end - t0);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int t = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (t >= nvalid) s[r] = -INFINITY;
+            if (t >= lim) s[r] = -INFINITY;
           }
         }
         float mt = s[0];
@@ -903,17 +921,18 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
         if (i == 0) {
           m_run = m_new;  // nothing accumulated yet: no rescale
         } else if (__builtin_amdgcn_ballot_w64(m_new > m_run + kTau)) {
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
           m_run = m_new;
           l_part *= alpha;
           lr_part *= alpha;
 #pragma unroll
           for (int vb = 0; vb < C::NVB; ++vb) scale_acc(oacc[vb], alpha);
         }
+        const float m_exp = m_run == -INFINITY ? 0.f : m_run;  // rows with no visible position
         f32x16 pr;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.score_log2, -m_run));
+          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.score_log2, -m_exp));
         {
           const f32x8 a = (f32x8){pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]} +
                           (f32x8){pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]};
@@ -970,13 +989,16 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks], s1, 0, 0, 0);
           dma_at(ks);
         });
-        // position of s_th[r] is 16*th + 4*(lane/16) + r
-        if (nvalid < kTile) {
+        // position of s_th[r] is 16*th + 4*(lane/16) + r; mask past the
+        // segment and past the row's causal limit (multi-token decode)
+        const int t0 = ts + i * kTile;
+        if (nvalid < kTile || t0 + kTile > vis_n) {
+          const int lim = min(nvalid, row_end - t0);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int t = 4 * (lane >> 4) + r;
-            if (t >= nvalid) s0[r] = -INFINITY;
-            if (t + 16 >= nvalid) s1[r] = -INFINITY;
+            if (t >= lim) s0[r] = -INFINITY;
+            if (t + 16 >= lim) s1[r] = -INFINITY;
           }
         }
         float mt = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
@@ -987,18 +1009,19 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
         if (i == 0) {
           m_run = m_new;
         } else if (__builtin_amdgcn_ballot_w64(m_new > m_run + kTau)) {
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
           m_run = m_new;
           l_part *= alpha;
           lr_part *= alpha;
 #pragma unroll
           for (int vb = 0; vb < C::NVB; ++vb) scale_acc(oacc[vb], alpha);
         }
+        const float m_exp = m_run == -INFINITY ? 0.f : m_run;  // rows with no visible position
         f32x8 pr;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], p.score_log2, -m_run));
-          pr[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.score_log2, -m_run));
+          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], p.score_log2, -m_exp));
+          pr[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.score_log2, -m_exp));
         }
         const bf16x8 pb = __builtin_convertvector(pr, bf16x8);
         l_part += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
@@ -1047,7 +1070,8 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       l_tot = sum_halves(l_part + __shfl_xor(l_part, 16, 64));
       lr_tot = sum_halves(lr_part + __shfl_xor(lr_part, 16, 64));
     }
-    const float inv = p.out_scale / lr_tot;
+    // a row that saw no position (multi-token decode) gets o = 0, lse = -inf
+    const float inv = lr_tot > 0.f ? p.out_scale / lr_tot : 0.f;
     const float lse_v = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
     const int hl = HPW == 32 ? (lane & 31) : (lane & 15);
     const int h = h0 + hl;
@@ -1132,7 +1156,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   };
 
   // ---------------- enumerate this unit's segments; process has one call site
-  int b = 0, ts = 0, te = 0, slot = 0;
+  int b = 0, ts = 0, te = 0, slot = 0, vis_n = 0;
   bool fin = false;
   int64_t st = 0, a0 = 0, a1 = 0;  // balanced mode: tile cursor and unit range
   if (p.split_mode == 0) {
@@ -1158,6 +1182,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     te = min(ts + Cb, n);
     fin = (n + Cb - 1) / Cb == 1;
     slot = b * S + s;
+    vis_n = n - (p.q_len - 1);
   } else {
     // the unit covers positions [a0, a1) of the batch's cost stream
     const int U = p.num_splits;
@@ -1194,9 +1219,10 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       te = hi > lo ? min((int)hi * kTile, n) : ts;
       fin = lo == 0 && hi == nt;
       slot = unit + b;
+      vis_n = n - (p.q_len - 1);
       st += cost_of(n, p.seg_cost);
     }
-    if (te > ts) process(b, ts, te, fin, slot);
+    if (te > ts) process(b, ts, te, fin, slot, vis_n);
     if (p.split_mode == 0) break;
     ++b;
     if (b >= p.batch || st >= a1) break;
@@ -1330,7 +1356,7 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
 #pragma unroll
     for (int i = 0; i < kS2Batch; ++i) mb = fmaxf(mb, ls[i][0]);
     if (mb == -INFINITY) continue;  // nothing live yet
-    const float r = __expf(m - mb);  // 0 while m is still -inf
+    const float r = m == -INFINITY ? 0.f : __expf(m - mb);  // nothing accumulated yet
     tot *= r;
     acc *= r;
 #pragma unroll
@@ -1353,18 +1379,21 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
     if (g != 0) return;
     float M = m;
     for (int r2 = row + 1; r2 < row + KG; ++r2) M = fmaxf(M, red_m[r2]);
-    const float r0 = __expf(m - M);
+    // groups (or whole rows, in multi-token decode) with no visible
+    // position carry m = -inf and weight 0
+    const float r0 = m == -INFINITY ? 0.f : __expf(m - M);
     acc *= r0;
     tot *= r0;
     for (int r2 = row + 1; r2 < row + KG; ++r2) {
-      const float rr = __expf(red_m[r2] - M);
+      const float rr = red_m[r2] == -INFINITY ? 0.f : __expf(red_m[r2] - M);
       acc += rr * red_o[r2][j];
       tot += rr * red_l[r2];
     }
     m = M;
   }
-  store_out8(p.o, p.o_f32, ((size_t)b * H + h) * DV + v, acc * (1.f / tot));
-  if (vc == 0 && j == 0) p.lse[(size_t)b * H + h] = m + __logf(tot);
+  const bool any = tot > 0.f;  // a row that saw no position: o = 0, lse = -inf
+  store_out8(p.o, p.o_f32, ((size_t)b * H + h) * DV + v, any ? acc * (1.f / tot) : f32x8{});
+  if (vc == 0 && j == 0) p.lse[(size_t)b * H + h] = any ? m + __logf(tot) : -INFINITY;
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -1423,6 +1452,8 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   sp.num_splits = a.num_splits;
   sp.head_chunks = ht.head_chunks;
   sp.seg_cost = segment_cost_tiles(a.heads, ht);
+  sp.q_len = a.q_len;
+  sp.heads_per_token = a.heads / a.q_len;
   sp.score_log2 = a.scale * kLog2e * (a.kv_fp8 ? a.k_scale : 1.f);
   sp.out_scale = a.kv_fp8 ? a.k_scale : 1.f;
 
