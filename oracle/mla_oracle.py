@@ -194,6 +194,38 @@ def decode_mtp(q_bits: np.ndarray, kv_bits: np.ndarray, block_table: np.ndarray,
     return np.stack(outs), np.stack(lses)
 
 
+# ---------------------------------------------------------------- sparse decode
+
+def decode_sparse(q_bits: np.ndarray, kv_bits: np.ndarray, block_table: np.ndarray,
+                  topk_indices: np.ndarray, topk_lens: np.ndarray, *, scale: float,
+                  k_scale: float, kv_dtype: str, kv_lora_rank: int,
+                  batches: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """lshu.cn article, section 13 (dense versus sparse attention): each query
+    attends only to a selected list of its positions (e.g. the top 2048), so
+    one head's scores are [1, D] x [D, k] instead of a scan of every key; the
+    request's isolation is unchanged: its logical positions go through its
+    own block table to physical slots.  Sequence b uses the entries
+    topk_indices[b, :topk_lens[b]] (a position listed twice counts twice).
+    Returns o [B', H, kv_lora_rank] and lse [B', H]."""
+    B, H, D = q_bits.shape
+    NB, P, D2 = kv_bits.shape
+    if D2 != D:
+        raise ValueError("q and cache head sizes differ")
+    bits = kv_bits.reshape(NB * P, D)
+    sc = float(np.float32(scale))
+    idx = range(B) if batches is None else batches
+    outs, lses = [], []
+    for b in idx:
+        chosen = [int(t) for t in topk_indices[b, :int(topk_lens[b])]]
+        slots = [physical_slot(block_table[b], t, P) for t in chosen]
+        K = decode_kv(bits[np.asarray(slots, dtype=np.int64)] if slots else bits[:0], kv_dtype,
+                      k_scale)
+        o, lse = attend(bf16_bits_to_f64(q_bits[b]), K, kv_lora_rank, sc)
+        outs.append(o)
+        lses.append(lse)
+    return np.stack(outs), np.stack(lses)
+
+
 # ---------------------------------------------------------------- split-KV merge
 
 def segment_bounds(n: int, chunk: int) -> List[Tuple[int, int]]:
@@ -290,5 +322,5 @@ __all__ = [
     "ROPE_DIM", "bf16_bits_to_f64", "e4m3fn_bits_to_f64", "E4M3FN_VALUES", "decode_kv",
     "physical_slot", "gather_rows", "attend", "decode", "segment_bounds", "merge_partials",
     "merge_normalised", "segment_partial", "decode_split", "pages_split_count",
-    "visible_keys", "decode_mtp",
+    "visible_keys", "decode_mtp", "decode_sparse",
 ]

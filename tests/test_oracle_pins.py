@@ -510,3 +510,99 @@ def test_planted_visibility_mistakes_are_caught(monkeypatch):
         with pytest.raises(AssertionError):
             test_mtp_matches_causal_sdpa("bf16", 576, 512, (9, 40, 3), 3)
         monkeypatch.undo()
+
+
+# ---------------------------------------------------------------- sparse decode
+# (lshu.cn article, section 13: each query attends only to its selected
+# positions, still reached through the request's own block table)
+
+def sparse_case(seed, seq_lens, topk, H=16, P=16):
+    return W.small_case(seed=seed, batch=len(seq_lens), num_heads=H, head_size=576,
+                        kv_lora_rank=512, page_size=P, seq_lens=seq_lens, topk=topk)
+
+
+def run_sparse(inp, idx=None, lens=None):
+    w = inp.workload
+    return O.decode_sparse(inp.q_bits, inp.kv_bits, inp.block_table,
+                           inp.topk_indices if idx is None else idx,
+                           inp.topk_lens if lens is None else lens, scale=w.scale,
+                           k_scale=w.k_scale, kv_dtype=w.kv_dtype, kv_lora_rank=w.kv_lora_rank)
+
+
+def test_sparse_matches_sdpa_over_the_selected_keys_at_the_pages_size():
+    """The page's example size (k = 2048 keys of dimension 576): torch float64
+    SDPA over the selected rows, gathered with numpy fancy indexing."""
+    g = golden()["sparse_topk"]
+    inp = sparse_case(seed=51, seq_lens=(4096, 2100), topk=g["topk"])
+    assert inp.q_bits.shape[-1] == g["query_dim"]
+    o, lse = run_sparse(inp)
+    sc = float(np.float32(inp.workload.scale))
+    for b in range(2):
+        K = dense_keys(inp, b)[torch.from_numpy(inp.topk_indices[b, :inp.topk_lens[b]].astype(
+            np.int64))]
+        assert K.shape[0] == g["score_shape"][1]
+        q = q_of(inp, b)
+        ref = torch.nn.functional.scaled_dot_product_attention(q[None], K[None],
+                                                               K[None, :, :512], scale=sc)[0]
+        ref_lse = torch.logsumexp((q @ K.T) * sc, dim=1)
+        assert np.abs(o[b] - ref.numpy()).max() < 1e-12
+        assert np.abs(lse[b] - ref_lse.numpy()).max() < 1e-12
+
+
+def test_sparse_over_every_position_in_order_is_dense_decode():
+    lens = (37, 100, 1)
+    inp = sparse_case(seed=52, seq_lens=lens, topk=128)
+    idx = np.zeros((3, 128), np.int32)
+    for b, n in enumerate(lens):
+        idx[b, :n] = np.arange(n)
+    o, lse = run_sparse(inp, idx, np.asarray(lens, np.int32))
+    od, ld = run(inp)
+    assert np.array_equal(o, od) and np.array_equal(lse, ld)
+
+
+def test_sparse_is_order_invariant_and_counts_duplicates_twice():
+    inp = sparse_case(seed=53, seq_lens=(300,), topk=64)
+    o, lse = run_sparse(inp)
+    rng = np.random.default_rng(0)
+    shuf = inp.topk_indices.copy()
+    shuf[0] = rng.permutation(shuf[0])
+    o2, l2 = run_sparse(inp, shuf)
+    assert np.abs(o - o2).max() < 1e-12 and np.abs(lse - l2).max() < 1e-12
+    # one position listed twice: exactly a key set in which that row appears twice
+    dup = inp.topk_indices.copy()
+    dup[0, 1] = dup[0, 0]
+    o3, l3 = run_sparse(inp, dup)
+    K = dense_keys(inp, 0)[torch.from_numpy(dup[0].astype(np.int64))]
+    q = q_of(inp, 0)
+    sc = float(np.float32(inp.workload.scale))
+    ref = torch.nn.functional.scaled_dot_product_attention(q[None], K[None], K[None, :, :512],
+                                                           scale=sc)[0]
+    assert np.abs(o3[0] - ref.numpy()).max() < 1e-12
+
+
+def test_sparse_empty_list_is_the_empty_sum():
+    inp = sparse_case(seed=54, seq_lens=(50, 20), topk=8)
+    o, lse = run_sparse(inp, lens=np.asarray([0, 8], np.int32))
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0])) and np.all(np.isfinite(lse[1]))
+
+
+def test_planted_sparse_mistakes_are_caught(monkeypatch):
+    """Reading the listed positions as physical slots (skipping the block
+    table), or attending to the first k positions instead of the listed ones,
+    fails the SDPA pin."""
+    real = OM.decode_sparse
+
+    def no_table(q_bits, kv_bits, block_table, topk_indices, topk_lens, **kw):
+        ident = np.tile(np.arange(block_table.shape[1], dtype=np.int32), (block_table.shape[0], 1))
+        return real(q_bits, kv_bits, ident, topk_indices, topk_lens, **kw)
+
+    def first_k(q_bits, kv_bits, block_table, topk_indices, topk_lens, **kw):
+        firsts = np.tile(np.arange(topk_indices.shape[1], dtype=np.int32),
+                         (topk_indices.shape[0], 1))
+        return real(q_bits, kv_bits, block_table, firsts, topk_lens, **kw)
+
+    for fake in (no_table, first_k):
+        monkeypatch.setattr(O, "decode_sparse", fake)
+        with pytest.raises(AssertionError):
+            test_sparse_matches_sdpa_over_the_selected_keys_at_the_pages_size()
+        monkeypatch.undo()

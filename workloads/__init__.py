@@ -54,6 +54,9 @@ class Workload:
     # query tokens per sequence (multi-token decode: the last q_len positions
     # are verified at once; q is then [B, q_len, H, D])
     q_len: int = 1
+    # sparse decode: each sequence attends to min(topk, n) positions drawn at
+    # random (distinct, unsorted); 0 = dense
+    topk: int = 0
 
     def draw_seq_lens(self, rng: np.random.Generator) -> np.ndarray:
         if self.seq_lens_fixed is not None:
@@ -98,6 +101,12 @@ WORKLOADS: Dict[str, Workload] = {
             seq_len_range=(1024, 8192), parity_splits=(16, 1), q_len=2,
             description="B=64 q_len=2 H=128 D=576/512 bf16 multi-token decode, page 64, "
                         "8192 pages, seq_lens U[1024,8192]"),
+        Workload(
+            name="dsv3_sparse", seed=7, batch=64, num_heads=128, head_size=576,
+            kv_lora_rank=512, page_size=64, num_blocks=8192, kv_dtype=BF16, k_scale=1.0,
+            scale=DSV3_SCALE, seq_len_range=(2048, 8192), parity_splits=(4, 1), topk=2048,
+            description="B=64 H=128 D=576/512 bf16 sparse decode over top-2048 positions, "
+                        "page 64, 8192 pages, seq_lens U[2048,8192]"),
     ]
 }
 
@@ -110,6 +119,8 @@ class DecodeInputs:
     kv_bits: np.ndarray         # uint16 [NB, P, D] (bf16) or uint8 [NB, P, D] (fp8)
     block_table: np.ndarray     # int32 [B, max_blocks_per_seq]
     seq_lens: np.ndarray        # int32 [B]
+    topk_indices: Optional[np.ndarray] = None  # int32 [B, topk] logical positions (sparse)
+    topk_lens: Optional[np.ndarray] = None     # int32 [B] entries used per sequence
 
     @property
     def kv_dtype(self) -> str:
@@ -184,20 +195,29 @@ def generate(workload: Workload | str, *, seq_lens: Optional[Sequence[int]] = No
         kv_bits = f32_to_bf16_bits(pool)
     else:
         kv_bits = f32_to_e4m3fn_bits(pool / np.float32(w.k_scale))
-    return DecodeInputs(workload=w, q_bits=q_bits, kv_bits=kv_bits, block_table=table,
-                        seq_lens=sl)
+    inp = DecodeInputs(workload=w, q_bits=q_bits, kv_bits=kv_bits, block_table=table,
+                       seq_lens=sl)
+    if w.topk:
+        idx = np.zeros((B, w.topk), dtype=np.int32)
+        lens = np.zeros(B, dtype=np.int32)
+        for b in range(B):
+            k = min(w.topk, int(sl[b]))
+            idx[b, :k] = rng.choice(int(sl[b]), size=k, replace=False)
+            lens[b] = k
+        inp.topk_indices, inp.topk_lens = idx, lens
+    return inp
 
 
 def small_case(*, seed: int, batch: int, num_heads: int, head_size: int, kv_lora_rank: int,
                page_size: int, seq_lens: Sequence[int], kv_dtype: str = BF16,
                k_scale: float = 1.0, extra_pages: int = 3, scale: float = DSV3_SCALE,
-               table_pad: int = 0, q_len: int = 1) -> DecodeInputs:
+               table_pad: int = 0, q_len: int = 1, topk: int = 0) -> DecodeInputs:
     """A custom small batch (edge cases, ragged lengths) with the same recipe."""
     pages = sum((int(n) + page_size - 1) // page_size for n in seq_lens) + extra_pages
     w = Workload(name=f"case{seed}", seed=seed, batch=batch, num_heads=num_heads,
                  head_size=head_size, kv_lora_rank=kv_lora_rank, page_size=page_size,
                  num_blocks=max(1, pages), kv_dtype=kv_dtype, k_scale=k_scale, scale=scale,
-                 seq_lens_fixed=tuple(int(n) for n in seq_lens), q_len=q_len)
+                 seq_lens_fixed=tuple(int(n) for n in seq_lens), q_len=q_len, topk=topk)
     inp = generate(w)
     if table_pad:
         inp.block_table = np.pad(inp.block_table, ((0, 0), (0, table_pad)))
