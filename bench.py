@@ -58,6 +58,15 @@ def algorithmic(inp):
     e_kv = 2 if w.kv_dtype == "bf16" else 1
     B, H, D, DV, P = w.batch, w.num_heads, w.head_size, w.kv_lora_rank, w.page_size
     ql = w.q_len
+    if w.topk:
+        # sparse decode: the selected rows, the index lists and one table entry each
+        k = int(np.asarray(inp.topk_lens, dtype=np.int64).sum())
+        kv = k * D * e_kv
+        stage1 = kv + B * H * D * 2 + k * 4 + k * 4 + 4 * B
+        total = stage1 + B * H * DV * 2 + B * H * 4
+        flops = 2 * H * k * (D + DV)
+        return {"kv_bytes": kv, "stage1_bytes": stage1, "total_bytes": total, "flops": flops,
+                "tokens": k}
     kv = int(n.sum()) * D * e_kv
     table = int(((n + P - 1) // P).sum()) * 4
     stage1 = kv + B * ql * H * D * 2 + table + 4 * B
@@ -84,10 +93,17 @@ def cpu_baseline(inp, alg, budget_s=25.0):
     t0 = time.perf_counter()
     fn = oracle.decode if w.q_len == 1 else oracle.decode_mtp
     for b in range(w.batch):
-        fn(inp.q_bits, inp.kv_bits, inp.block_table, inp.seq_lens, scale=w.scale,
-           k_scale=w.k_scale, kv_dtype=w.kv_dtype, kv_lora_rank=w.kv_lora_rank, batches=[b])
+        if w.topk:
+            oracle.decode_sparse(inp.q_bits, inp.kv_bits, inp.block_table, inp.topk_indices,
+                                 inp.topk_lens, scale=w.scale, k_scale=w.k_scale,
+                                 kv_dtype=w.kv_dtype, kv_lora_rank=w.kv_lora_rank, batches=[b])
+            tok += int(inp.topk_lens[b])
+        else:
+            fn(inp.q_bits, inp.kv_bits, inp.block_table, inp.seq_lens, scale=w.scale,
+               k_scale=w.k_scale, kv_dtype=w.kv_dtype, kv_lora_rank=w.kv_lora_rank,
+               batches=[b])
+            tok += int(inp.seq_lens[b])
         done += 1
-        tok += int(inp.seq_lens[b])
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
@@ -204,6 +220,11 @@ def main():
 
     shape = mla.shape_of(q, kv, bt)
     max_len, tot = int(inp.seq_lens.max()), int(inp.seq_lens.sum())
+    topk_dev = None
+    if w.topk:  # sparse decode: the plan counts list entries
+        max_len, tot = w.topk, int(inp.topk_lens.sum())
+        topk_dev = torch.from_numpy(inp.topk_indices).to(dev)
+        sl = torch.from_numpy(inp.topk_lens).to(dev)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     ql = w.q_len
     if args.split == "plan":
@@ -219,7 +240,8 @@ def main():
     lse = torch.empty(rows, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     calls = [mla.PreparedDecode(q, k, b, sl, w.scale, w.page_size, w.k_scale, splits, mode, o,
-                                lse, ws, stream=stream.cuda_stream) for (k, b) in sets]
+                                lse, ws, stream=stream.cuda_stream, topk_indices=topk_dev)
+             for (k, b) in sets]
 
     for i in range(args.warmup):
         calls[i % 2]("stage1")
@@ -283,7 +305,8 @@ def main():
         "config": {"workload": f"{w.name}: {w.description}", "batch": w.batch,
                    "heads": w.num_heads, "head_size": w.head_size,
                    "kv_lora_rank": w.kv_lora_rank, "page_size": w.page_size,
-                   "total_tokens": alg["tokens"], "q_len": ql, "split_mode": int(mode),
+                   "total_tokens": alg["tokens"], "q_len": ql, "topk": w.topk,
+                   "split_mode": int(mode),
                    "num_kv_splits": int(splits), "seed": w.seed},
         "tflops": round(tflops, 1),
         "tokens_heads_per_s": round(alg["tokens"] * w.num_heads / (ms_step * 1e-3), 1),

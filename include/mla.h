@@ -248,6 +248,44 @@ mla_status mla_decode_mtp_stage2(const mla_shape* shape, int32_t q_len, const vo
                                  void* o, float* lse, void* workspace, size_t workspace_bytes,
                                  void* hip_stream);
 
+/* Sparse (top-k) decode ("vLLM 中 Attention Kernel 如何并行处理多个请求",
+ * section 十三): each sequence attends only to a selected list of its
+ * positions, e.g. the top 2048, instead of all of them.  Request isolation is
+ * unchanged: the selected logical positions go through the sequence's block
+ * table to physical slots.  Sequence b attends to the cache rows of
+ *     topk_indices[b * topk + e]   for e < topk_lens[b]
+ * (logical positions, each < that sequence's length; a position listed twice
+ * counts twice).  Everything else is as in mla_decode, with topk_lens[b] in
+ * place of seq_lens[b] for the split plan (plan with max_seq_len = topk and
+ * total_seq_len = sum of topk_lens; workspace from mla_workspace_size).
+ *   topk_indices  [batch, topk] int32, device; entries and topk_lens[b] <= topk
+ *                 are trusted like block_table entries
+ *   topk_lens     [batch] int32, device; 0 gives o = 0, lse = -inf
+ * The index-driven gather is built for one configuration: head_size 576, a
+ * bf16 cache of at most 4 GB (else MLA_ERR_HEAD_SIZE / MLA_ERR_DTYPE /
+ * MLA_ERR_SHAPE) and num_heads a multiple of 128 (else MLA_ERR_SHAPE);
+ * topk < 1 is MLA_ERR_ARGUMENT, NULL lists MLA_ERR_NULL. */
+mla_status mla_decode_sparse(const mla_shape* shape, int32_t topk, const void* q,
+                             const void* kv_cache, const int32_t* block_table,
+                             const int32_t* topk_indices, const int32_t* topk_lens, float scale,
+                             int32_t page_size, float k_scale, int32_t num_kv_splits,
+                             int32_t split_mode, void* o, float* lse, void* workspace,
+                             size_t workspace_bytes, void* hip_stream);
+mla_status mla_decode_sparse_stage1(const mla_shape* shape, int32_t topk, const void* q,
+                                    const void* kv_cache, const int32_t* block_table,
+                                    const int32_t* topk_indices, const int32_t* topk_lens,
+                                    float scale, int32_t page_size, float k_scale,
+                                    int32_t num_kv_splits, int32_t split_mode, void* o,
+                                    float* lse, void* workspace, size_t workspace_bytes,
+                                    void* hip_stream);
+mla_status mla_decode_sparse_stage2(const mla_shape* shape, int32_t topk, const void* q,
+                                    const void* kv_cache, const int32_t* block_table,
+                                    const int32_t* topk_indices, const int32_t* topk_lens,
+                                    float scale, int32_t page_size, float k_scale,
+                                    int32_t num_kv_splits, int32_t split_mode, void* o,
+                                    float* lse, void* workspace, size_t workspace_bytes,
+                                    void* hip_stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char* mla_status_string(int32_t status);
 

@@ -27,7 +27,7 @@ from typing import Optional, Tuple
 from . import _build
 
 __all__ = [
-    "MlaError", "mla_decode", "mla_plan", "mla_workspace_size", "mla_pages_split_count",
+    "MlaError", "mla_decode", "mla_decode_sparse", "mla_plan", "mla_workspace_size", "mla_pages_split_count",
     "mla_status_string", "SPLIT_PER_SEQUENCE", "SPLIT_BALANCED", "library_path", "load_library",
     "MLA_BF16", "MLA_FP8_E4M3", "MLA_FP32",
 ]
@@ -86,6 +86,11 @@ def load_library():
         for fn in (lib.mla_decode_mtp, lib.mla_decode_mtp_stage1, lib.mla_decode_mtp_stage2):
             fn.argtypes = [shp, i32, vp, vp, vp, vp, ctypes.c_float, i32, ctypes.c_float, i32,
                            i32, vp, vp, vp, sz, vp]
+            fn.restype = i32
+        for fn in (lib.mla_decode_sparse, lib.mla_decode_sparse_stage1,
+                   lib.mla_decode_sparse_stage2):
+            fn.argtypes = [shp, i32, vp, vp, vp, vp, vp, ctypes.c_float, i32, ctypes.c_float,
+                           i32, i32, vp, vp, vp, sz, vp]
             fn.restype = i32
         lib.mla_status_string.argtypes = [i32]
         lib.mla_status_string.restype = ctypes.c_char_p
@@ -242,6 +247,57 @@ def mla_decode(q, kv_cache, block_table, seq_lens, scale: float, page_size: int,
     return o, lse
 
 
+def mla_decode_sparse(q, kv_cache, block_table, topk_indices, topk_lens, scale: float,
+                      page_size: int, k_scale: float = 1.0,
+                      num_kv_splits: Optional[int] = None, o=None, lse=None, *,
+                      split_mode: Optional[int] = None, workspace=None, o_dtype=None,
+                      num_cus: Optional[int] = None, stream=None, stages: str = "both"):
+    """Sparse (top-k) MLA decode: sequence b attends to the cache rows of the
+    logical positions ``topk_indices[b, :topk_lens[b]]`` (int32 [B, topk] and
+    [B]).  Other arguments as in ``mla_decode``; the split plan counts list
+    entries.  Returns (o [B, H, D_v], lse [B, H])."""
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
+                    ("topk_indices", topk_indices), ("topk_lens", topk_lens)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if topk_indices.dtype != torch.int32 or topk_lens.dtype != torch.int32:
+        raise ValueError("topk_indices and topk_lens must be int32")
+    if o is not None:
+        o_dtype = o.dtype
+    shape = shape_of(q, kv_cache, block_table, o_dtype=o_dtype)
+    B, H = shape.batch, shape.num_heads
+    topk = int(topk_indices.shape[1])
+    if num_kv_splits is None:
+        if num_cus is None:
+            num_cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        split_mode, num_kv_splits, _ = mla_plan(shape, topk, int(topk_lens.sum().item()),
+                                                num_cus)
+    elif split_mode is None:
+        split_mode = SPLIT_PER_SEQUENCE
+    ws_need = mla_workspace_size(shape, split_mode, num_kv_splits)
+    if o is None:
+        o = torch.empty((B, H, shape.kv_lora_rank), dtype=o_dtype or torch.bfloat16,
+                        device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    fn = {"both": lib.mla_decode_sparse, "stage1": lib.mla_decode_sparse_stage1,
+          "stage2": lib.mla_decode_sparse_stage2}[stages]
+    st = fn(ctypes.byref(shape), topk, q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
+            topk_indices.data_ptr(), topk_lens.data_ptr(), float(scale), int(page_size),
+            float(k_scale), int(num_kv_splits), int(split_mode), o.data_ptr(), lse.data_ptr(),
+            workspace.data_ptr() if workspace is not None else None,
+            workspace.numel() * workspace.element_size() if workspace is not None else 0, stream)
+    if st != MLA_OK:
+        _raise(st, "mla_decode_sparse")
+    return o, lse
+
+
 class PreparedDecode:
     """A decode call with every argument marshalled once, for loops that
     launch the same step repeatedly (benchmarks, graph capture).  Calling it
@@ -249,7 +305,10 @@ class PreparedDecode:
     alive by this object."""
 
     def __init__(self, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
-                 num_kv_splits, split_mode, o, lse, workspace=None, kv_dtype=None, stream=None):
+                 num_kv_splits, split_mode, o, lse, workspace=None, kv_dtype=None, stream=None,
+                 topk_indices=None):
+        """``topk_indices`` [B, topk] selects sparse decode; ``seq_lens`` then
+        holds the list lengths."""
         torch = _torch()
         self.lib = load_library()
         self.keep = (q, kv_cache, block_table, seq_lens, o, lse, workspace)
@@ -260,14 +319,23 @@ class PreparedDecode:
             raise MlaError(MLA_ERR_WORKSPACE, "workspace too small")
         if stream is None:
             stream = torch.cuda.current_stream(q.device).cuda_stream
-        self.args = (ctypes.byref(self.shape), int(q_len), q.data_ptr(), kv_cache.data_ptr(),
-                     block_table.data_ptr(), seq_lens.data_ptr(), float(scale), int(page_size),
+        lead = (ctypes.byref(self.shape), int(q_len), q.data_ptr(), kv_cache.data_ptr(),
+                block_table.data_ptr())
+        if topk_indices is not None:
+            self.keep = self.keep + (topk_indices,)
+            lead = (ctypes.byref(self.shape), int(topk_indices.shape[1]), q.data_ptr(),
+                    kv_cache.data_ptr(), block_table.data_ptr(), topk_indices.data_ptr())
+        self.args = lead + (seq_lens.data_ptr(), float(scale), int(page_size),
                      float(k_scale), int(num_kv_splits), int(split_mode), o.data_ptr(),
                      lse.data_ptr(), workspace.data_ptr() if workspace is not None else None,
                      workspace.numel() * workspace.element_size() if workspace is not None else 0,
                      stream)
         self.fns = {"both": self.lib.mla_decode_mtp, "stage1": self.lib.mla_decode_mtp_stage1,
                     "stage2": self.lib.mla_decode_mtp_stage2}
+        if topk_indices is not None:
+            self.fns = {"both": self.lib.mla_decode_sparse,
+                        "stage1": self.lib.mla_decode_sparse_stage1,
+                        "stage2": self.lib.mla_decode_sparse_stage2}
 
     def __call__(self, stages: str = "both"):
         st = self.fns[stages](*self.args)

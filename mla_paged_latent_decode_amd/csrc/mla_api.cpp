@@ -163,7 +163,8 @@ static mla_status decode_stages(const mla_shape* shape, int32_t q_len, const voi
                                 float scale, int32_t page_size, float k_scale,
                                 int32_t num_kv_splits, int32_t split_mode, void* o, float* lse,
                                 void* workspace, size_t workspace_bytes, void* hip_stream,
-                                int stages) {
+                                int stages, const int32_t* topk_idx = nullptr,
+                                int32_t topk = 0) {
   mla_status st = check_shape(shape);
   if (st != MLA_OK) return st;
   mla_shape rs;
@@ -214,6 +215,11 @@ static mla_status decode_stages(const mla_shape* shape, int32_t q_len, const voi
   a.num_splits = num_kv_splits;
   a.scale = scale;
   a.k_scale = k_scale;
+  a.pool_bytes = (uint64_t)shape->num_blocks * shape->page_size * shape->head_size * (fp8 ? 1 : 2);
+  if (topk_idx) {
+    a.topk_idx = topk_idx;
+    a.topk_stride = topk;
+  }
   return launch_decode(a, hip_stream, stages) == 0 ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
@@ -276,6 +282,39 @@ mla_status mla_decode_mtp_stage2(const mla_shape* shape, int32_t q_len, const vo
                        num_kv_splits, split_mode, o, lse, workspace, workspace_bytes, hip_stream,
                        kStage2);
 }
+
+// Sparse (top-k) decode: checks of the configurations its gather is built for.
+static mla_status check_sparse(const mla_shape* shape, int32_t topk, const int32_t* topk_indices,
+                               const int32_t* topk_lens) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!topk_indices || !topk_lens) return MLA_ERR_NULL;
+  if (topk < 1) return MLA_ERR_ARGUMENT;
+  if (shape->head_size != 576) return MLA_ERR_HEAD_SIZE;
+  if (shape->kv_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (shape->num_heads % 128 != 0) return MLA_ERR_SHAPE;
+  const uint64_t pool = (uint64_t)shape->num_blocks * shape->page_size * shape->head_size * 2;
+  if (pool + 65536 >= ((uint64_t)1 << 32)) return MLA_ERR_SHAPE;
+  if (!aligned(topk_indices, 4)) return MLA_ERR_ARGUMENT;
+  return MLA_OK;
+}
+
+#define MLA_SPARSE_ENTRY(NAME, STAGES)                                                          \
+  mla_status NAME(const mla_shape* shape, int32_t topk, const void* q, const void* kv_cache,    \
+                  const int32_t* block_table, const int32_t* topk_indices,                      \
+                  const int32_t* topk_lens, float scale, int32_t page_size, float k_scale,      \
+                  int32_t num_kv_splits, int32_t split_mode, void* o, float* lse,               \
+                  void* workspace, size_t workspace_bytes, void* hip_stream) {                  \
+    const mla_status st = check_sparse(shape, topk, topk_indices, topk_lens);                   \
+    if (st != MLA_OK) return st;                                                                \
+    return decode_stages(shape, 1, q, kv_cache, block_table, topk_lens, scale, page_size,       \
+                         k_scale, num_kv_splits, split_mode, o, lse, workspace,                 \
+                         workspace_bytes, hip_stream, STAGES, topk_indices, topk);              \
+  }
+MLA_SPARSE_ENTRY(mla_decode_sparse, kBothStages)
+MLA_SPARSE_ENTRY(mla_decode_sparse_stage1, kStage1)
+MLA_SPARSE_ENTRY(mla_decode_sparse_stage2, kStage2)
+#undef MLA_SPARSE_ENTRY
 
 const char* mla_status_string(int32_t status) {
   switch (status) {

@@ -84,6 +84,11 @@ struct DecodeArgs {
   int32_t num_splits;
   float scale;
   float k_scale;
+  // sparse decode: top-k list [batch][topk_stride] of logical positions
+  // (NULL for dense decode; seq_lens then holds the list lengths)
+  const int32_t* topk_idx = nullptr;
+  int32_t topk_stride = 0;
+  uint64_t pool_bytes = 0;  // num_blocks * page_size * head_size * kv bytes
 };
 
 enum Stages { kStage1 = 1, kStage2 = 2, kBothStages = 3 };

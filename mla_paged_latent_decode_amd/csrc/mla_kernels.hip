@@ -235,6 +235,14 @@ struct Stage1Params {
   // heads (row = token * heads_per_token + head).  Token i of a sequence with
   // n keys sees positions t < n - q_len + 1 + i.  Plain decode: q_len = 1.
   int32_t q_len, heads_per_token;
+  // Sparse (top-k) decode: sequence b attends to the cache rows of the
+  // logical positions topk_idx[b * topk_stride + e], e < seq_lens[b] (the
+  // split logic then counts list entries, not positions).  pool_bytes bounds
+  // the one buffer resource over the whole cache (< 4 GB); page_shift is
+  // log2(page_size) when that is a power of two, else -1.
+  const int32_t* topk_idx;
+  int32_t topk_stride, page_shift;
+  uint32_t pool_bytes;
   float score_log2;  // scale * log2(e) (* k_scale for fp8 caches)
   float out_scale;   // 1, or k_scale for fp8 caches
 };
@@ -344,9 +352,11 @@ __device__ __forceinline__ int tile_slot(int t16, int c4) {
   return (t16 ^ (8 * (c4 & 1) + 4 * (c4 >> 1))) + 16 * c4;
 }
 
-template <int HPW, int W, int D, int DV, int NBUF, bool F8>
+template <int HPW, int W, int D, int DV, int NBUF, bool F8, bool SP>
 __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   using C = Cfg<HPW, W, D, DV, NBUF, F8>;
+  static_assert(!SP || (C::PIPE && !F8 && NBUF == 3),
+                "the index-driven gather is built for the pipelined bf16 loop with a ring of 3");
   // [bf16 ring: NBUF tiles][fp8 staging: 2 tiles][Q k-steps of each wave]
   __shared__ __attribute__((aligned(1024)))
   uint8_t ring[NBUF * C::TILE_BYTES + C::STG_BYTES + C::QLDS_BYTES];
@@ -374,8 +384,8 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   // DMA: lane l writes slot l of a block: chunk c4 = l / 16 of position
   // t16 = (l % 16) ^ f(c4); its source offset within the 16-row page run.
   const int dma_c4 = lane >> 4;
-  const int dma_voff =
-      ((lane & 15) ^ (8 * (dma_c4 & 1) + 4 * (dma_c4 >> 1))) * C::SRC_ROW + 16 * dma_c4;
+  const int dma_t16 = (lane & 15) ^ (8 * (dma_c4 & 1) + 4 * (dma_c4 >> 1));
+  const int dma_voff = dma_t16 * C::SRC_ROW + 16 * dma_c4;
   // fp8 widening: lane l converts chunk c4 = l % 4 of position t16 = l / 4
   // of a block, read from the row-major staging tile and written to the
   // chunk's slot of the bf16 tile layout
@@ -424,7 +434,41 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       const int k = win_lb + lane;
       win = k < lb_end ? bt_row[k] : 0;
     };
-    load_window();
+    if constexpr (!SP) load_window();
+
+    // Sparse gather ("vLLM 中 Attention Kernel 如何并行处理多个请求", section
+    // 十三: the request's top-k logical positions go through its block table
+    // to physical slots).  Every lane loads the same row dma_t16 of each
+    // 16-entry half of a tile, so per tile it needs two row offsets.  They
+    // come from a per-lane pipeline: prepare(i) uses the pages of tile i
+    // (loaded one tile earlier), loads the pages of tile i+1 from its
+    // entries (loaded two tiles earlier) and loads the entries of tile i+2.
+    // Entries past the segment get the offset pool_bytes, which the buffer
+    // range check turns into zero rows.
+    const int32_t* sp_list = SP ? p.topk_idx + (int64_t)b * p.topk_stride : nullptr;
+    int spA0 = -1, spA1 = -1, spG0 = 0, spG1 = 0, spB0 = -1, spB1 = -1;
+    auto sp_entries = [&](int x, int& i0, int& i1) __attribute__((always_inline)) {
+      const int e0 = ts + x * kTile + dma_t16;
+      i0 = e0 < te ? sp_list[e0] : -1;
+      i1 = e0 + 16 < te ? sp_list[e0 + 16] : -1;
+    };
+    auto sp_block = [&](int pos) __attribute__((always_inline)) {
+      return p.page_shift >= 0 ? pos >> p.page_shift : pos / P;
+    };
+    auto sp_pages = [&](int i0, int i1, int& g0, int& g1) __attribute__((always_inline)) {
+      g0 = i0 >= 0 ? bt_row[sp_block(i0)] : 0;
+      g1 = i1 >= 0 ? bt_row[sp_block(i1)] : 0;
+    };
+    auto sp_offset = [&](int pos, int page) __attribute__((always_inline)) {
+      return pos >= 0 ? ((uint32_t)page * (uint32_t)P + (uint32_t)(pos - sp_block(pos) * P)) *
+                            (uint32_t)C::SRC_ROW
+                      : p.pool_bytes;
+    };
+    if constexpr (SP) {
+      sp_entries(0, spA0, spA1);
+      sp_entries(1, spB0, spB1);
+      sp_pages(spA0, spA1, spG0, spG1);
+    }
 
     // Issue the loads of the next tile (ring slot i % NBUF).  Each 16-row
     // half lies in one page (P and 16-position boundaries are multiples of
@@ -434,12 +478,22 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     struct TileLoad {  // plain fields: the buffer resources are built at each use
       uint64_t base[2];
       int bytes[2];
+      uint32_t off[2];  // sparse: this lane's row offset in each half
       uint8_t* dst;
     };
     // Resources of the next tile to load (ring slot i % NBUF); advances the cursor.
     auto prepare = [&](int i) __attribute__((always_inline)) {
       TileLoad tl;
       tl.dst = F8 ? stg + (i & 1) * C::STG_TILE : ring + (i % NBUF) * C::TILE_BYTES;
+      if constexpr (SP) {
+        tl.off[0] = sp_offset(spA0, spG0);
+        tl.off[1] = sp_offset(spA1, spG1);
+        spA0 = spB0;
+        spA1 = spB1;
+        sp_pages(spA0, spA1, spG0, spG1);
+        sp_entries(i + 2, spB0, spB1);
+        return tl;
+      }
 #pragma unroll
       for (int th = 0; th < 2; ++th) {
         const int nv = uniform(max(0, min(16, te - cur_tok)));
@@ -478,6 +532,15 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       const int j = wave + k * W;  // copy index
       const int th = j >= C::NIH ? 1 : 0;
       const int r = j - th * C::NIH;
+      if constexpr (SP) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)p.kv, (short)0, (int)p.pool_bytes, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(tl.dst + j * 1024), 16,
+                                                 (int)((th ? tl.off[1] : tl.off[0]) +
+                                                       16 * dma_c4) + sgpr_here(64 * r),
+                                                 0, 0, 0);
+        return;
+      }
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(th ? tl.base[1] : tl.base[0]), (short)0, th ? tl.bytes[1] : tl.bytes[0],
           0x00020000);
@@ -1398,10 +1461,11 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
 
 // ---------------------------------------------------------------- dispatch
 
-template <int HPW, int W, int D, int DV, bool F8>
+template <int HPW, int W, int D, int DV, bool F8, bool SP = false>
 int launch_stage1(const Stage1Params& sp, int grid, hipStream_t st) {
   constexpr int NBUF = stage1_ring_depth(HPW, W, D, F8);
-  hipLaunchKernelGGL((mla_stage1<HPW, W, D, DV, NBUF, F8>), dim3(grid), dim3(64 * W), 0, st, sp);
+  hipLaunchKernelGGL((mla_stage1<HPW, W, D, DV, NBUF, F8, SP>), dim3(grid), dim3(64 * W), 0, st,
+                     sp);
   return (int)hipGetLastError();
 }
 
@@ -1454,6 +1518,12 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   sp.seg_cost = segment_cost_tiles(a.heads, ht);
   sp.q_len = a.q_len;
   sp.heads_per_token = a.heads / a.q_len;
+  sp.topk_idx = a.topk_idx;
+  sp.topk_stride = a.topk_stride;
+  sp.pool_bytes = (uint32_t)a.pool_bytes;
+  sp.page_shift = -1;
+  for (int sh = 0; sh < 31; ++sh)
+    if ((1 << sh) == a.page_size) sp.page_shift = sh;
   sp.score_log2 = a.scale * kLog2e * (a.kv_fp8 ? a.k_scale : 1.f);
   sp.out_scale = a.kv_fp8 ? a.k_scale : 1.f;
 
@@ -1461,7 +1531,11 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   const int grid1 = (units + 7) / 8 * 8 * ht.head_chunks;
   if (stages & kStage1) {
     int err;
-    if (a.kv_fp8)
+    if (a.topk_idx) {
+      // the host admits the sparse gather only for this configuration
+      if (a.kv_fp8 || a.head_size != 576 || ht.heads_per_wave != 32 || ht.waves != 4) return -1;
+      err = launch_stage1<32, 4, 576, 512, false, true>(sp, grid1, st);
+    } else if (a.kv_fp8)
       err = a.head_size == 576 ? launch_stage1_for<576, 512, true>(ht, sp, grid1, st)
                                : launch_stage1_for<320, 256, true>(ht, sp, grid1, st);
     else

@@ -1,0 +1,165 @@
+"""GPU parity of sparse (top-k) decode (lshu.cn article, section 13) against
+the float64 oracle, through the C ABI.
+
+Sequence b attends to the cache rows of the logical positions
+topk_indices[b, :topk_lens[b]], each reached through its block table.  The
+kernels are those of dense decode with an index-driven gather, so beside the
+oracle comparison (o 1e-2, lse 1e-3) a list of every position in order must
+reproduce dense decode bitwise, and slots no list names may hold NaN.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL_O, TOL_LSE = 1e-2, 1e-3
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_paged_latent_decode_amd as m
+    m.load_library()
+    return m
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.device("cuda:0"))
+
+
+def run_sparse(mla, inp, splits, mode, idx=None, lens=None, o_dtype=None):
+    w = inp.workload
+    q = dev(inp.q_bits.view(np.int16)).view(torch.bfloat16)
+    kv = dev(inp.kv_bits.view(np.int16)).view(torch.bfloat16)
+    o, lse = mla.mla_decode_sparse(q, kv, dev(inp.block_table),
+                                   dev(inp.topk_indices if idx is None else idx),
+                                   dev(inp.topk_lens if lens is None else lens), w.scale,
+                                   w.page_size, w.k_scale, splits, split_mode=mode,
+                                   o_dtype=o_dtype or torch.bfloat16)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def ref(inp, idx=None, lens=None, batches=None):
+    w = inp.workload
+    return oracle.decode_sparse(inp.q_bits, inp.kv_bits, inp.block_table,
+                                inp.topk_indices if idx is None else idx,
+                                inp.topk_lens if lens is None else lens, scale=w.scale,
+                                k_scale=w.k_scale, kv_dtype=w.kv_dtype,
+                                kv_lora_rank=w.kv_lora_rank, batches=batches)
+
+
+def check(o, lse, ro, rl, lens, label):
+    lens = np.asarray(lens)
+    empty = lens == 0
+    if empty.any():
+        assert np.all(o[empty] == 0) and np.all(np.isneginf(lse[empty])), label
+    live = ~empty
+    do = np.abs(o[live] - ro[live]).max()
+    dl = np.abs(lse[live] - rl[live]).max()
+    print(f"{label}: max|do|={do:.3e} max|dlse|={dl:.3e}", flush=True)
+    assert np.all(np.isfinite(o[live])) and np.all(np.isfinite(lse[live])), label
+    assert do <= TOL_O and dl <= TOL_LSE, (label, do, dl)
+
+
+SPARSE_CASES = [
+    # (H, P, seq_lens, topk)
+    (128, 64, (300, 2000, 40, 1031), 256),
+    (128, 16, (1, 33, 64, 100), 48),
+    (256, 64, (700, 129), 100),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SPARSE_CASES)))
+@pytest.mark.parametrize("mode,splits", [(0, 1), (0, 3), (1, 1), (1, 5), (1, 37)])
+def test_sparse_cases(mla, case, mode, splits):
+    H, P, sl, k = SPARSE_CASES[case]
+    inp = W.small_case(seed=400 + case, batch=len(sl), num_heads=H, head_size=576,
+                       kv_lora_rank=512, page_size=P, seq_lens=sl, topk=k)
+    ro, rl = ref(inp)
+    o, lse = run_sparse(mla, inp, splits, mode, o_dtype=torch.float32)
+    check(o, lse, ro, rl, inp.topk_lens, f"sparse case{case} mode={mode} S={splits}")
+
+
+@pytest.mark.parametrize("mode,splits", [(0, 1), (0, 4), (1, 7)])
+def test_sparse_over_every_position_is_dense_decode_bitwise(mla, mode, splits):
+    sl = (37, 100, 1, 700)
+    inp = W.small_case(seed=410, batch=len(sl), num_heads=128, head_size=576, kv_lora_rank=512,
+                       page_size=64, seq_lens=sl)
+    idx = np.zeros((len(sl), 704), np.int32)
+    for b, n in enumerate(sl):
+        idx[b, :n] = np.arange(n)
+    w = inp.workload
+    q = dev(inp.q_bits.view(np.int16)).view(torch.bfloat16)
+    kv = dev(inp.kv_bits.view(np.int16)).view(torch.bfloat16)
+    bt, lens = dev(inp.block_table), dev(np.asarray(sl, np.int32))
+    od, ld = mla.mla_decode(q, kv, bt, lens, w.scale, w.page_size, w.k_scale, splits,
+                            split_mode=mode)
+    os_, ls_ = mla.mla_decode_sparse(q, kv, bt, dev(idx), lens, w.scale, w.page_size,
+                                     w.k_scale, splits, split_mode=mode)
+    torch.cuda.synchronize()
+    assert torch.equal(od, os_) and torch.equal(ld, ls_)
+
+
+@pytest.mark.parametrize("mode,splits", [(0, 1), (1, 5)])
+def test_sparse_ignores_unlisted_slots(mla, mode, splits):
+    """NaN in every cache slot that no list names (including the unused
+    entries of each list's row) changes nothing."""
+    sl = (300, 900, 64)
+    inp = W.small_case(seed=411, batch=len(sl), num_heads=128, head_size=576, kv_lora_rank=512,
+                       page_size=16, seq_lens=sl, topk=96)
+    a = run_sparse(mla, inp, splits, mode)
+    P = inp.workload.page_size
+    used = np.zeros(inp.kv_bits.shape[:2], dtype=bool)
+    for b in range(len(sl)):
+        for t in inp.topk_indices[b, :inp.topk_lens[b]]:
+            used[inp.block_table[b, t // P], t % P] = True
+    kv = inp.kv_bits.copy()
+    kv[~used] = np.uint16(0x7FC0)
+    poisoned = dataclasses.replace(inp, kv_bits=kv)
+    b_ = run_sparse(mla, poisoned, splits, mode)
+    assert np.all(np.isfinite(b_[0])) and np.all(np.isfinite(b_[1]))
+    assert np.array_equal(a[0], b_[0]) and np.array_equal(a[1], b_[1])
+
+
+def test_sparse_rejects_configurations_it_is_not_built_for(mla):
+    inp = W.small_case(seed=412, batch=1, num_heads=16, head_size=576, kv_lora_rank=512,
+                       page_size=16, seq_lens=(40,), topk=8)
+    with pytest.raises(mla.MlaError):  # 16 heads: not a multiple of 128
+        run_sparse(mla, inp, 1, 0)
+    inp = W.small_case(seed=413, batch=1, num_heads=128, head_size=320, kv_lora_rank=256,
+                       page_size=16, seq_lens=(40,), topk=8)
+    with pytest.raises(ValueError):  # head size 320
+        run_sparse(mla, inp, 1, 0)
+
+
+def test_sparse_full_size(mla):
+    """dsv3_sparse (B=64, H=128, top-2048 of U[2048,8192]) at the planner's
+    configuration and at per-sequence split counts, on sampled sequences."""
+    inp = W.generate("dsv3_sparse")
+    w = inp.workload
+    rng = np.random.default_rng(1234)
+    picks = sorted({0, w.batch - 1} | set(rng.choice(w.batch, size=6, replace=False).tolist()))
+    ro, rl = ref(inp, batches=picks)
+    q = dev(inp.q_bits.view(np.int16)).view(torch.bfloat16)
+    kv = dev(inp.kv_bits.view(np.int16)).view(torch.bfloat16)
+    bt, idx, lens = dev(inp.block_table), dev(inp.topk_indices), dev(inp.topk_lens)
+    shape = mla.shape_of(q, kv, bt)
+    mode, units, _ = mla.mla_plan(shape, w.topk, int(inp.topk_lens.sum()), 256)
+    print(f"dsv3_sparse: entries={int(inp.topk_lens.sum())} plan mode={mode} units={units}",
+          flush=True)
+    for mode, splits in [(mode, units)] + [(0, s) for s in w.parity_splits]:
+        o, lse = mla.mla_decode_sparse(q, kv, bt, idx, lens, w.scale, w.page_size, w.k_scale,
+                                       splits, split_mode=mode)
+        torch.cuda.synchronize()
+        o = o.float().cpu().numpy().astype(np.float64)
+        lse = lse.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+        check(o[picks], lse[picks], ro, rl, inp.topk_lens[picks], f"dsv3_sparse mode={mode} S={splits}")
