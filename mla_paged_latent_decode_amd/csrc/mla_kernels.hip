@@ -329,8 +329,13 @@ struct Cfg {
   static constexpr int dma_step(int k) {
     return NBUF >= 4 ? k * (NKS + 2 * NVB) / NIW : k * (NKS / 2) / NIW;
   }
-  // software-pipelined loop (softmax of tile j behind the QK^T of tile j+1)
-  static constexpr bool PIPE = HPW == 32 && (F8 ? W == 4 : NBUF >= 3);
+  // Software-pipelined loop (softmax of tile j interleaved with the QK^T of
+  // tile j+1): kept for fp8 caches and the 4-tile ring (D = 320).  With the
+  // 3-tile ring the plain loop is as fast with loads and faster without:
+  // within one wave gfx950 does not overlap VALU work with an executing
+  // MFMA, so the interleaving buys nothing, while the plain loop needs no
+  // second score buffer and can spread a tile's loads over two iterations.
+  static constexpr bool PIPE = HPW == 32 && (F8 ? W == 4 : NBUF >= 4);
   static_assert(NBUF == stage1_ring_depth(HPW, W, D, F8), "ring depth");
   static_assert(NBLK * 1024 == kTile * D * 2, "tile bytes");
   static_assert(NBLK % W == 0, "each wave loads or widens the same number of blocks");
@@ -355,8 +360,8 @@ __device__ __forceinline__ int tile_slot(int t16, int c4) {
 template <int HPW, int W, int D, int DV, int NBUF, bool F8, bool SP>
 __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   using C = Cfg<HPW, W, D, DV, NBUF, F8>;
-  static_assert(!SP || (C::PIPE && !F8 && NBUF == 3),
-                "the index-driven gather is built for the pipelined bf16 loop with a ring of 3");
+  static_assert(!SP || (!F8 && NBUF == 3),
+                "the index-driven gather is built for the bf16 loop with a ring of 3");
   // [bf16 ring: NBUF tiles][fp8 staging: 2 tiles][Q k-steps of each wave]
   __shared__ __attribute__((aligned(1024)))
   uint8_t ring[NBUF * C::TILE_BYTES + C::STG_BYTES + C::QLDS_BYTES];
@@ -917,11 +922,16 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       const bool more = F8 || i + NBUF - 1 < n_tiles;
       TileLoad tl;
       if (more) tl = prepare(F8 ? i + 2 : i + NBUF - 1);
-      auto dma_at = [&](int ks) __attribute__((always_inline)) {
-        // load k goes after k-step floor(k * NKS / NIW)
+      // Load k goes after step floor(k * TOT / NIW) of the tile's TOT MFMA
+      // steps (32-head waves: the QK^T and the PV steps; the loaded tile is
+      // not read before iteration i+NBUF-1, so the loads may be spread over
+      // the whole iteration and leave the memory pipeline at about the rate
+      // it drains instead of blocking the wave in a burst).
+      constexpr int TOT_STEPS = HPW == 32 ? C::NKS + 2 * C::NVB : C::NKS;
+      auto dma_at = [&](int step) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < C::NIW; ++k)
-          if ((k * C::NKS) / C::NIW == ks && more) dma(tl, k);
+          if ((k * TOT_STEPS) / C::NIW == step && more) dma(tl, k);
       };
 
       const LDS_AS uint8_t* tile = (const LDS_AS uint8_t*)ring + (i % NBUF) * C::TILE_BYTES;
@@ -1035,6 +1045,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
             lds_wait<later>(a0);
             oacc[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, a0), (st & 1) ? p1 : p0, oacc[st >> 1], 0, 0, 0);
+            dma_at(C::NKS + st);
             __builtin_amdgcn_sched_barrier(0);
             a0 = a1;
             a1 = a2;
