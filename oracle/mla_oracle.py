@@ -74,13 +74,31 @@ def e4m3fn_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return E4M3FN_VALUES[np.asarray(bits, dtype=np.uint8)]
 
 
+PER_TOKEN_PAD = 16  # bytes after the codes of a per-token row: fp32 scale + 12 unused
+
+
+def row_width(kv_dtype: str, head_size: int) -> int:
+    """Stored elements (bytes for fp8) per cache row: the head_size values, and
+    for the per-token layout the padding that holds the inline scale (Triton
+    MLA page, key files: in per-token-head modes the cache shape pads head_dim
+    to hold an inline scale)."""
+    return head_size + PER_TOKEN_PAD if kv_dtype == "fp8_per_token" else head_size
+
+
 def decode_kv(kv_bits: np.ndarray, kv_dtype: str, k_scale: float) -> np.ndarray:
     """Cache rows as float64.  fp8 values are multiplied by the fp32-rounded
-    k_scale (exact in float64); bf16 rows ignore k_scale."""
+    k_scale (exact in float64); bf16 rows ignore k_scale.  Per-token rows
+    ``[e4m3fn codes (D) | fp32 scale | pad]`` decode to code * scale of that
+    token (exact in float64); k_scale does not apply to them."""
     if kv_dtype == "bf16":
         return bf16_bits_to_f64(kv_bits)
     if kv_dtype == "fp8_e4m3":
         return e4m3fn_bits_to_f64(kv_bits) * float(np.float32(k_scale))
+    if kv_dtype == "fp8_per_token":
+        rows = np.ascontiguousarray(kv_bits, dtype=np.uint8)
+        D = rows.shape[-1] - PER_TOKEN_PAD
+        scale = rows[..., D:D + 4].copy().view("<f4")[..., 0].astype(np.float64)
+        return e4m3fn_bits_to_f64(rows[..., :D]) * scale[..., None]
     raise ValueError(f"unknown kv dtype {kv_dtype!r}")
 
 
@@ -137,9 +155,9 @@ def decode(q_bits: np.ndarray, kv_bits: np.ndarray, block_table: np.ndarray,
     the chosen ``batches`` (default: all, in order)."""
     B, H, D = q_bits.shape
     NB, P, D2 = kv_bits.shape
-    if D2 != D:
+    if D2 != row_width(kv_dtype, D):
         raise ValueError("q and cache head sizes differ")
-    bits = kv_bits.reshape(NB * P, D)
+    bits = kv_bits.reshape(NB * P, D2)
     sc = float(np.float32(scale))
     idx = range(B) if batches is None else batches
     outs, lses = [], []
@@ -174,9 +192,9 @@ def decode_mtp(q_bits: np.ndarray, kv_bits: np.ndarray, block_table: np.ndarray,
     ``decode``.  Returns o [B', q_len, H, kv_lora_rank] and lse [B', q_len, H]."""
     B, q_len, H, D = q_bits.shape
     NB, P, D2 = kv_bits.shape
-    if D2 != D:
+    if D2 != row_width(kv_dtype, D):
         raise ValueError("q and cache head sizes differ")
-    bits = kv_bits.reshape(NB * P, D)
+    bits = kv_bits.reshape(NB * P, D2)
     sc = float(np.float32(scale))
     idx = range(B) if batches is None else batches
     outs, lses = [], []
@@ -209,9 +227,9 @@ def decode_sparse(q_bits: np.ndarray, kv_bits: np.ndarray, block_table: np.ndarr
     Returns o [B', H, kv_lora_rank] and lse [B', H]."""
     B, H, D = q_bits.shape
     NB, P, D2 = kv_bits.shape
-    if D2 != D:
+    if D2 != row_width(kv_dtype, D):
         raise ValueError("q and cache head sizes differ")
-    bits = kv_bits.reshape(NB * P, D)
+    bits = kv_bits.reshape(NB * P, D2)
     sc = float(np.float32(scale))
     idx = range(B) if batches is None else batches
     outs, lses = [], []
@@ -289,8 +307,8 @@ def decode_split(q_bits: np.ndarray, kv_bits: np.ndarray, block_table: np.ndarra
     sequence b; each segment is attended on its own and the partials are merged
     by section 12's formula (or its (o_s, lse_s) form when ``normalised``)."""
     B, H, D = q_bits.shape
-    NB, P, _ = kv_bits.shape
-    bits = kv_bits.reshape(NB * P, D)
+    NB, P, D2 = kv_bits.shape
+    bits = kv_bits.reshape(NB * P, D2)
     sc = float(np.float32(scale))
     outs, lses = [], []
     for b in range(B):
@@ -322,5 +340,5 @@ __all__ = [
     "ROPE_DIM", "bf16_bits_to_f64", "e4m3fn_bits_to_f64", "E4M3FN_VALUES", "decode_kv",
     "physical_slot", "gather_rows", "attend", "decode", "segment_bounds", "merge_partials",
     "merge_normalised", "segment_partial", "decode_split", "pages_split_count",
-    "visible_keys", "decode_mtp", "decode_sparse",
+    "visible_keys", "decode_mtp", "decode_sparse", "row_width", "PER_TOKEN_PAD",
 ]

@@ -6,6 +6,7 @@ routine (torch's float64 SDPA, torch's bf16/fp8 decoders), exact rational
 arithmetic, or a brute-force loop.  The last group plants mistakes in the
 oracle and checks that at least one pin catches each of them.
 """
+import dataclasses
 import json
 import math
 import os
@@ -48,10 +49,15 @@ def dense_keys(inp, b):
     P = w.page_size
     pos = np.arange(n)
     rows = inp.block_table[b][pos // P] * P + pos % P
-    flat = inp.kv_bits.reshape(-1, w.head_size)[rows]
+    flat = inp.kv_bits.reshape(-1, inp.kv_bits.shape[-1])[rows]
     if w.kv_dtype == "bf16":
         t = torch.from_numpy(flat.view(np.int16).copy()).view(torch.bfloat16)
         return t.to(torch.float64)
+    if w.kv_dtype == "fp8_per_token":
+        D = w.head_size
+        codes = torch.from_numpy(flat[:, :D].copy()).view(torch.float8_e4m3fn).to(torch.float64)
+        scale = torch.from_numpy(flat[:, D:D + 4].copy()).view(torch.float32).to(torch.float64)
+        return codes * scale
     t = torch.from_numpy(flat.copy()).view(torch.float8_e4m3fn)
     return t.to(torch.float64) * float(np.float32(w.k_scale))
 
@@ -605,4 +611,89 @@ def test_planted_sparse_mistakes_are_caught(monkeypatch):
         monkeypatch.setattr(O, "decode_sparse", fake)
         with pytest.raises(AssertionError):
             test_sparse_matches_sdpa_over_the_selected_keys_at_the_pages_size()
+        monkeypatch.undo()
+
+
+# ---------------------------------------------------------------- per-token quantised cache
+# (Triton MLA page, key files: per-token-head modes pad head_dim to hold an
+# inline scale; rows here are [e4m3fn codes (D) | fp32 scale | 12 pad bytes])
+
+def pt_case(seed, seq_lens, H=16, D=576, P=16):
+    return W.small_case(seed=seed, batch=len(seq_lens), num_heads=H, head_size=D,
+                        kv_lora_rank=D - 64, page_size=P, seq_lens=seq_lens,
+                        kv_dtype=W.FP8_PER_TOKEN)
+
+
+def test_per_token_rows_decode_like_torch_times_their_scale():
+    inp = pt_case(seed=61, seq_lens=(40, 7))
+    rows = inp.kv_bits.reshape(-1, inp.kv_bits.shape[-1])
+    mine = O.decode_kv(rows, "fp8_per_token", 1.0)
+    D = inp.workload.head_size
+    codes = torch.from_numpy(rows[:, :D].copy()).view(torch.float8_e4m3fn).to(torch.float64)
+    scale = torch.from_numpy(rows[:, D:D + 4].copy()).view(torch.float32).to(torch.float64)
+    assert np.array_equal(mine, (codes * scale).numpy())
+    assert rows.shape[-1] == O.row_width("fp8_per_token", D) == D + 16
+
+
+def test_per_token_row_maximum_round_trips():
+    """The largest element of each token's row is quantised to +-448 exactly,
+    so it decodes to the row's max|x| (to the fp32 rounding of the scale)."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((64, 576), dtype=np.float32) * rng.uniform(0.01, 100, (64, 1)).astype(
+        np.float32)
+    rows = W.per_token_fp8_rows(x)
+    dec = O.decode_kv(rows, "fp8_per_token", 1.0)
+    amax = np.abs(x).max(axis=1).astype(np.float64)
+    got = np.abs(dec).max(axis=1)
+    assert np.all(np.abs(got - amax) <= amax * 2.0 ** -22)
+    assert np.all(np.abs(dec - x) <= amax[:, None] * 2.0 ** -4)  # e4m3: 3 mantissa bits
+
+
+@pytest.mark.parametrize("D", [576, 320])
+def test_per_token_cache_matches_torch_sdpa(D):
+    inp = pt_case(seed=62, seq_lens=(37, 100, 1), D=D)
+    w = inp.workload
+    o, lse = run(inp)
+    sc = float(np.float32(w.scale))
+    for b in range(3):
+        K = dense_keys(inp, b)
+        q = q_of(inp, b)
+        ref = torch.nn.functional.scaled_dot_product_attention(q[None], K[None],
+                                                               K[None, :, :D - 64], scale=sc)[0]
+        ref_lse = torch.logsumexp((q @ K.T) * sc, dim=1)
+        assert np.abs(o[b] - ref.numpy()).max() < 1e-12
+        assert np.abs(lse[b] - ref_lse.numpy()).max() < 1e-12
+
+
+def test_per_token_cache_ignores_k_scale():
+    inp = pt_case(seed=63, seq_lens=(20, 64))
+    a = run(inp)
+    w = dataclasses.replace(inp.workload, k_scale=0.05)
+    b = run(dataclasses.replace(inp, workload=w))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_planted_per_token_mistakes_are_caught(monkeypatch):
+    """Dropping the per-token scale, or reading it from the wrong bytes, fails
+    the SDPA pin."""
+    real = OM.decode_kv
+
+    def scale_dropped(bits, dt, ks):
+        if dt != "fp8_per_token":
+            return real(bits, dt, ks)
+        D = bits.shape[-1] - 16
+        return O.e4m3fn_bits_to_f64(np.asarray(bits)[..., :D])
+
+    def scale_misread(bits, dt, ks):
+        if dt != "fp8_per_token":
+            return real(bits, dt, ks)
+        b2 = np.array(bits, copy=True)
+        D = b2.shape[-1] - 16
+        b2[..., D:D + 4] = b2[..., D - 4:D]  # the last four codes taken as the scale
+        return real(b2, dt, ks)
+
+    for fake in (scale_dropped, scale_misread):
+        monkeypatch.setattr(OM, "decode_kv", fake)
+        with pytest.raises(AssertionError):
+            test_per_token_cache_matches_torch_sdpa(576)
         monkeypatch.undo()

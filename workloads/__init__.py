@@ -27,6 +27,10 @@ import numpy as np
 
 BF16 = "bf16"
 FP8_E4M3 = "fp8_e4m3"
+# per-token quantised fp8: each row [e4m3fn codes (D) | fp32 scale | 12 zero
+# bytes], scale = max|row| / 448 of the token's fp32 row
+FP8_PER_TOKEN = "fp8_per_token"
+PER_TOKEN_PAD = 16
 
 # fp32(192 ** -0.5): the softmax scale of a DeepSeek-V3 style head
 # (qk_nope 128 + qk_rope 64).  Kept as the fp32-rounded value.
@@ -107,6 +111,12 @@ WORKLOADS: Dict[str, Workload] = {
             scale=DSV3_SCALE, seq_len_range=(2048, 8192), parity_splits=(4, 1), topk=2048,
             description="B=64 H=128 D=576/512 bf16 sparse decode over top-2048 positions, "
                         "page 64, 8192 pages, seq_lens U[2048,8192]"),
+        Workload(
+            name="fp8_pt", seed=8, batch=64, num_heads=128, head_size=576, kv_lora_rank=512,
+            page_size=64, num_blocks=8192, kv_dtype=FP8_PER_TOKEN, k_scale=1.0,
+            scale=DSV3_SCALE, seq_len_range=(1024, 8192), parity_splits=(16, 1),
+            description="B=64 H=128 D=576/512 per-token fp8 cache (inline fp32 scale, rows of "
+                        "592 B), page 64, 8192 pages, seq_lens U[1024,8192]"),
     ]
 }
 
@@ -140,6 +150,19 @@ def f32_to_e4m3fn_bits(x: np.ndarray) -> np.ndarray:
     x = np.clip(np.ascontiguousarray(x, dtype=np.float32), -448.0, 448.0)
     t = torch.from_numpy(x).to(torch.float8_e4m3fn)
     return t.view(torch.uint8).numpy()
+
+
+def per_token_fp8_rows(pool: np.ndarray) -> np.ndarray:
+    """fp32 rows [..., D] -> per-token quantised rows [..., D + 16] bytes:
+    e4m3fn codes of row / s, then s as fp32, then zeros, with
+    s = fp32(max|row| / 448) (1 for an all-zero row)."""
+    amax = np.abs(pool).max(axis=-1, keepdims=True).astype(np.float32)
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    codes = f32_to_e4m3fn_bits(pool / s)
+    out = np.zeros(pool.shape[:-1] + (pool.shape[-1] + PER_TOKEN_PAD,), dtype=np.uint8)
+    out[..., :pool.shape[-1]] = codes
+    out[..., pool.shape[-1]:pool.shape[-1] + 4] = s.view(np.uint8)
+    return out
 
 
 def make_block_table(rng: np.random.Generator, seq_lens: np.ndarray, page_size: int,
@@ -193,6 +216,8 @@ def generate(workload: Workload | str, *, seq_lens: Optional[Sequence[int]] = No
     pool = _normal_f32(rng, (nb, w.page_size, w.head_size))
     if w.kv_dtype == BF16:
         kv_bits = f32_to_bf16_bits(pool)
+    elif w.kv_dtype == FP8_PER_TOKEN:
+        kv_bits = per_token_fp8_rows(pool)
     else:
         kv_bits = f32_to_e4m3fn_bits(pool / np.float32(w.k_scale))
     inp = DecodeInputs(workload=w, q_bits=q_bits, kv_bits=kv_bits, block_table=table,
@@ -247,7 +272,7 @@ def poison_unreferenced(inp: DecodeInputs, *, poison_table: bool = True) -> Deco
     used = referenced_slots(inp)
     kv = inp.kv_bits.copy()
     nan = np.uint16(0x7FC0) if inp.kv_dtype == BF16 else np.uint8(0x7F)
-    kv[~used] = nan
+    kv[~used] = nan  # per-token rows: NaN codes and a NaN scale (0x7F7F7F7F)
     table = inp.block_table.copy()
     if poison_table:
         free_pages = np.nonzero(~used.any(axis=1))[0]
