@@ -55,19 +55,21 @@ def algorithmic(inp):
     import numpy as np
     w = inp.workload
     n = np.asarray(inp.seq_lens, dtype=np.int64)
-    e_kv = 2 if w.kv_dtype == "bf16" else 1
     B, H, D, DV, P = w.batch, w.num_heads, w.head_size, w.kv_lora_rank, w.page_size
+    # bytes of one cache row the method needs: bf16 values, fp8 codes, or fp8
+    # codes and the token's fp32 scale (the rest of the per-token pad is unused)
+    row = {"bf16": 2 * D, "fp8_per_token": D + 4}.get(w.kv_dtype, D)
     ql = w.q_len
     if w.topk:
         # sparse decode: the selected rows, the index lists and one table entry each
         k = int(np.asarray(inp.topk_lens, dtype=np.int64).sum())
-        kv = k * D * e_kv
+        kv = k * row
         stage1 = kv + B * H * D * 2 + k * 4 + k * 4 + 4 * B
         total = stage1 + B * H * DV * 2 + B * H * 4
         flops = 2 * H * k * (D + DV)
         return {"kv_bytes": kv, "stage1_bytes": stage1, "total_bytes": total, "flops": flops,
                 "tokens": k}
-    kv = int(n.sum()) * D * e_kv
+    kv = int(n.sum()) * row
     table = int(((n + P - 1) // P).sum()) * 4
     stage1 = kv + B * ql * H * D * 2 + table + 4 * B
     total = stage1 + B * ql * H * DV * 2 + B * ql * H * 4
@@ -206,6 +208,8 @@ def main():
     q = torch.from_numpy(inp.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     if w.kv_dtype == "bf16":
         kv = torch.from_numpy(inp.kv_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    elif w.kv_dtype == "fp8_per_token":
+        kv = torch.from_numpy(inp.kv_bits).to(dev)  # uint8 rows: codes | fp32 scale | pad
     else:
         kv = torch.from_numpy(inp.kv_bits).view(torch.float8_e4m3fn).to(dev)
     bt = torch.from_numpy(inp.block_table).to(dev)
@@ -218,7 +222,7 @@ def main():
     bt2 = new_of_old.to(torch.int32)[bt.long()].contiguous()
     sets = [(kv, bt), (kv2, bt2)]
 
-    shape = mla.shape_of(q, kv, bt)
+    shape = mla.shape_of(q, kv, bt, kv_dtype=w.kv_dtype)
     max_len, tot = int(inp.seq_lens.max()), int(inp.seq_lens.sum())
     topk_dev = None
     if w.topk:  # sparse decode: the plan counts list entries
@@ -240,7 +244,8 @@ def main():
     lse = torch.empty(rows, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     calls = [mla.PreparedDecode(q, k, b, sl, w.scale, w.page_size, w.k_scale, splits, mode, o,
-                                lse, ws, stream=stream.cuda_stream, topk_indices=topk_dev)
+                                lse, ws, stream=stream.cuda_stream, topk_indices=topk_dev,
+                                kv_dtype=w.kv_dtype)
              for (k, b) in sets]
 
     for i in range(args.warmup):

@@ -64,7 +64,8 @@ typedef enum mla_status {
                             argument differs from shape->page_size ("AttentionBackend"
                             page, Limites et échecs: block sizes are multiples of 16)   */
   MLA_ERR_DTYPE = 4,     /* q not bf16 (an fp8 query is refused: "Triton と MLA" page,
-                            境界と失敗), kv not bf16/fp8 e4m3fn, o not bf16/fp32        */
+                            境界と失敗), kv not bf16 / fp8 e4m3fn (per-tensor or
+                            per-token scale), o not bf16/fp32                            */
   MLA_ERR_SHAPE = 5,     /* batch < 1, num_heads not a positive multiple of 16,
                             num_blocks < 1 (empty cache), max_blocks_per_seq < 1, or a
                             size whose byte count overflows                              */
@@ -80,8 +81,18 @@ typedef enum mla_status {
 typedef enum mla_dtype {
   MLA_BF16 = 0,     /* bfloat16                                                       */
   MLA_FP8_E4M3 = 1, /* OCP fp8 e4m3fn: bias 7, max 448, no infinity (cache only)      */
-  MLA_FP32 = 2      /* float32 (output only)                                          */
+  MLA_FP32 = 2,     /* float32 (output only)                                          */
+  /* Cache only: fp8 e4m3fn codes with one scale per token, stored inline.  A
+   * row is head_size code bytes followed by a MLA_PER_TOKEN_PAD-byte pad whose
+   * first 4 bytes are the token's little-endian float32 scale (the other 12
+   * are never read); value = code * scale, for K and V alike ("Triton と MLA"
+   * page, 主要ファイル: in the per-token-head modes the cache's head_dim is
+   * padded to hold an inline scale).  k_scale does not apply.  Rows start on
+   * 16-byte boundaries (head_size + 16 is a multiple of 16). */
+  MLA_FP8_E4M3_PER_TOKEN = 3
 } mla_dtype;
+
+#define MLA_PER_TOKEN_PAD 16 /* bytes after the codes of a per-token cache row */
 
 /* How stage 1 divides the positions of a batch among workgroups.
  *
@@ -116,7 +127,8 @@ typedef enum mla_split_mode {
 /* Problem shape.  Layouts (all row-major, densely packed unless noted):
  *   q           [batch, num_heads, head_size]              q_dtype (bf16)
  *   kv_cache    [num_blocks, page_size, head_size]         kv_dtype; row =
- *               [kv_c (kv_lora_rank) | k_pe (64)]
+ *               [kv_c (kv_lora_rank) | k_pe (64)]; with MLA_FP8_E4M3_PER_TOKEN
+ *               [num_blocks, page_size, head_size + MLA_PER_TOKEN_PAD] bytes
  *   block_table [batch, max_blocks_per_seq]                int32; entries at
  *               index >= ceil(seq_lens[b] / page_size) are never read
  *   seq_lens    [batch]                                    int32, >= 0
@@ -132,7 +144,8 @@ typedef struct mla_shape {
   int32_t num_blocks;         /* pages in the pool, >= 1                    */
   int32_t max_blocks_per_seq; /* block_table row stride in entries, >= 1    */
   int32_t q_dtype;            /* mla_dtype: MLA_BF16                        */
-  int32_t kv_dtype;           /* mla_dtype: MLA_BF16 or MLA_FP8_E4M3        */
+  int32_t kv_dtype;           /* mla_dtype: MLA_BF16, MLA_FP8_E4M3 or
+                                 MLA_FP8_E4M3_PER_TOKEN                     */
   int32_t o_dtype;            /* mla_dtype: MLA_BF16 or MLA_FP32            */
 } mla_shape;
 
@@ -170,8 +183,8 @@ size_t mla_workspace_size(const mla_shape* shape, int32_t split_mode, int32_t nu
  *   q, kv_cache, block_table, seq_lens   inputs, layouts as in mla_shape
  *   scale          softmax scale applied to q.K (e.g. 192^-0.5), finite > 0
  *   page_size      must equal shape->page_size
- *   k_scale        per-layer dequantisation scale of an fp8 cache (finite > 0);
- *                  ignored for a bf16 cache
+ *   k_scale        per-layer dequantisation scale of an MLA_FP8_E4M3 cache
+ *                  (finite > 0); ignored for bf16 and per-token caches
  *   num_kv_splits, split_mode   as returned by mla_plan (or chosen freely)
  *   o, lse         outputs, every [b, h] entry is overwritten; a sequence
  *                  with seq_lens[b] == 0 gets o = 0 and lse = -inf

@@ -42,7 +42,12 @@ HeadTiling head_tiling(int32_t heads);
 // (1 KB per step and wave), as many as the remaining LDS holds, up to 12.
 constexpr int kLdsBytes = 160 * 1024;
 
-constexpr int stage1_ring_depth(int hpw, int waves, int d, bool fp8) {
+// Per-token fp8 caches (rows of D codes + a 16-byte inline scale pad) run
+// the plain fp8 loop with a ring of 2 and keep each tile's 32 scales in LDS:
+// two staging slots of 2 x 256 B and a ring of 128 B slots.
+constexpr int kPerTokenPad = 16;
+constexpr int stage1_ring_depth(int hpw, int waves, int d, bool fp8, bool pt = false) {
+  if (pt) return 2;
   if (fp8) return (hpw == 32 && waves == 4) ? 3 : 2;
   if (d != 576) return 4;
   // 32-head waves at D = 576: three tiles, so that 12 of Q's 36 k-steps fit
@@ -51,15 +56,20 @@ constexpr int stage1_ring_depth(int hpw, int waves, int d, bool fp8) {
   return waves == 4 ? 4 : 2;
 }
 constexpr int stage1_staging_bytes(int d, bool fp8) { return fp8 ? 2 * kTile * d : 0; }
-constexpr int stage1_qlds_steps(int hpw, int waves, int d, bool fp8) {
+constexpr int stage1_scale_bytes(int hpw, int waves, int d, bool fp8, bool pt) {
+  return pt ? 2 * 512 + stage1_ring_depth(hpw, waves, d, fp8, pt) * 128 : 0;
+}
+constexpr int stage1_qlds_steps(int hpw, int waves, int d, bool fp8, bool pt = false) {
   if (!(hpw == 32 && d == 576)) return 0;
-  const int room = (kLdsBytes - stage1_ring_depth(hpw, waves, d, fp8) * kTile * d * 2 -
-                    stage1_staging_bytes(d, fp8)) / (waves * 1024);
+  const int room = (kLdsBytes - stage1_ring_depth(hpw, waves, d, fp8, pt) * kTile * d * 2 -
+                    stage1_staging_bytes(d, fp8) - stage1_scale_bytes(hpw, waves, d, fp8, pt)) /
+                   (waves * 1024);
   return room < 12 ? room : 12;
 }
-constexpr int stage1_lds_bytes(int hpw, int waves, int d, bool fp8) {
-  return stage1_ring_depth(hpw, waves, d, fp8) * kTile * d * 2 + stage1_staging_bytes(d, fp8) +
-         stage1_qlds_steps(hpw, waves, d, fp8) * waves * 1024;
+constexpr int stage1_lds_bytes(int hpw, int waves, int d, bool fp8, bool pt = false) {
+  return stage1_ring_depth(hpw, waves, d, fp8, pt) * kTile * d * 2 + stage1_staging_bytes(d, fp8) +
+         stage1_qlds_steps(hpw, waves, d, fp8, pt) * waves * 1024 +
+         stage1_scale_bytes(hpw, waves, d, fp8, pt);
 }
 
 struct DecodeArgs {
@@ -79,6 +89,7 @@ struct DecodeArgs {
   int32_t page_size;
   int32_t bt_stride;
   int32_t kv_fp8;
+  int32_t kv_pt;  // per-token fp8 rows: D codes + an inline fp32 scale (16-byte pad)
   int32_t o_f32;
   int32_t split_mode;
   int32_t num_splits;

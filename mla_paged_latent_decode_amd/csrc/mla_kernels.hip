@@ -128,6 +128,11 @@ __device__ __forceinline__ void lds_wait(u32x2& x) {
   static_assert(N >= 0 && N < 16, "lgkmcnt is a 4-bit counter");
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
 }
+template <int N>
+__device__ __forceinline__ void lds_wait(uint32_t& x) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt is a 4-bit counter");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
+}
 // Plain LDS read / write from asm, for the fp8 widening step: the compiler
 // would otherwise order them after every in-flight tile load (the loads
 // write LDS), and it does not count them, so every use of a read comes after
@@ -140,6 +145,19 @@ __device__ __forceinline__ u32x2 ds_read_b64_asm(uint32_t addr) {
 }
 __device__ __forceinline__ void ds_write_b128_asm(uint32_t addr, u32x4 v) {
   asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ uint32_t ds_read_b32_asm(uint32_t addr) {
+  uint32_t r;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+__device__ __forceinline__ void ds_write_b32_asm(uint32_t addr, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ u32x4 ds_read_b128_asm(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
 }
 
 // Eight OCP e4m3fn values (one per byte, lowest byte first) to eight bf16.
@@ -293,7 +311,7 @@ __device__ __forceinline__ int64_t total_cost(const int32_t* seq_lens, int B, in
 
 // ---------------------------------------------------------------- stage 1
 
-template <int HPW, int W, int D, int DV, int NBUF, bool F8>
+template <int HPW, int W, int D, int DV, int NBUF, bool F8, bool PT = false>
 struct Cfg {
   static constexpr int NKQ = D / 32;                       // 32-wide d groups per row
   static constexpr int NBLK = 2 * NKQ;                     // 1 KB LDS blocks per tile
@@ -301,14 +319,14 @@ struct Cfg {
   // With 32 heads per wave and D = 576, the O accumulators (256 registers)
   // and all 36 Q fragments (144) leave too few registers for the rest of the
   // loop; the last QLDS k-steps of Q then live in LDS (1 KB per step/wave).
-  static constexpr int QLDS = stage1_qlds_steps(HPW, W, D, F8);
+  static constexpr int QLDS = stage1_qlds_steps(HPW, W, D, F8, PT);
   static constexpr int NQR = NKS - QLDS;                   // Q k-steps held in VGPRs
   static constexpr int QLDS_BYTES = W * QLDS * 1024;
   static constexpr int LPW = NBLK / W;                     // bf16 blocks per wave per tile
   static constexpr int TILE_BYTES = NBLK * 1024;
   static constexpr int NVB = HPW == 32 ? DV / 32 : DV / 16;  // PV output blocks
   static constexpr int HEADS_PER_WG = HPW * W;
-  static constexpr int SRC_ROW = F8 ? D : 2 * D;           // bytes of one cache row
+  static constexpr int SRC_ROW = F8 ? (PT ? D + kPerTokenPad : D) : 2 * D;  // cache row bytes
   // fp8: a 16-row half tile (16*D contiguous bytes of one page) is copied to
   // a staging tile with G-byte LDS DMA per lane (consecutive lanes write
   // consecutive G bytes), G = 16 when every wave then issues the same number
@@ -319,6 +337,7 @@ struct Cfg {
   static constexpr int NIW = 2 * NIH / W;                   // DMA copies per wave per tile
   static constexpr int STG_TILE = F8 ? kTile * D : 0;       // fp8 staging tile bytes
   static constexpr int STG_BYTES = 2 * STG_TILE;
+  static constexpr int SCL_BYTES = stage1_scale_bytes(HPW, W, D, F8, PT);
   // Pipelined bf16 loop: the k-th of a wave's NIW tile loads goes out at step
   // dma_step(k) of the iteration's NKS QK^T + 2*NVB PV MFMA steps.  Spread
   // evenly, the loads leave the memory pipeline at about the rate HBM drains
@@ -335,14 +354,15 @@ struct Cfg {
   // within one wave gfx950 does not overlap VALU work with an executing
   // MFMA, so the interleaving buys nothing, while the plain loop needs no
   // second score buffer and can spread a tile's loads over two iterations.
-  static constexpr bool PIPE = HPW == 32 && (F8 ? W == 4 : NBUF >= 4);
-  static_assert(NBUF == stage1_ring_depth(HPW, W, D, F8), "ring depth");
+  static constexpr bool PIPE = HPW == 32 && !PT && (F8 ? W == 4 : NBUF >= 4);
+  static_assert(NBUF == stage1_ring_depth(HPW, W, D, F8, PT), "ring depth");
+  static_assert(!PT || F8, "per-token rows hold fp8 codes");
   static_assert(NBLK * 1024 == kTile * D * 2, "tile bytes");
   static_assert(NBLK % W == 0, "each wave loads or widens the same number of blocks");
   static_assert(!F8 || ((16 * D) % (64 * G) == 0 && (2 * NIH) % W == 0), "fp8 copy split");
   static_assert(F8 ? NIW <= 63 : (NBUF - 1) * LPW <= 63,
                 "outstanding loads must fit the vmcnt counter");
-  static_assert(NBUF * TILE_BYTES + STG_BYTES + QLDS_BYTES <= kLdsBytes, "LDS budget");
+  static_assert(NBUF * TILE_BYTES + STG_BYTES + QLDS_BYTES + SCL_BYTES <= kLdsBytes, "LDS budget");
   static_assert(D % 32 == 0 && DV % 32 == 0, "");
 };
 
@@ -357,15 +377,20 @@ __device__ __forceinline__ int tile_slot(int t16, int c4) {
   return (t16 ^ (8 * (c4 & 1) + 4 * (c4 >> 1))) + 16 * c4;
 }
 
-template <int HPW, int W, int D, int DV, int NBUF, bool F8, bool SP>
+template <int HPW, int W, int D, int DV, int NBUF, bool F8, bool SP, bool PT>
 __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
-  using C = Cfg<HPW, W, D, DV, NBUF, F8>;
+  using C = Cfg<HPW, W, D, DV, NBUF, F8, PT>;
   static_assert(!SP || (!F8 && NBUF == 3),
                 "the index-driven gather is built for the bf16 loop with a ring of 3");
   // [bf16 ring: NBUF tiles][fp8 staging: 2 tiles][Q k-steps of each wave]
+  // [per-token scales: 2 staging slots of 2 x 256 B, NBUF ring slots of 128 B]
   __shared__ __attribute__((aligned(1024)))
-  uint8_t ring[NBUF * C::TILE_BYTES + C::STG_BYTES + C::QLDS_BYTES];
+  uint8_t ring[NBUF * C::TILE_BYTES + C::STG_BYTES + C::QLDS_BYTES + C::SCL_BYTES];
   uint8_t* const stg = ring + NBUF * C::TILE_BYTES;
+  // LDS addresses (32-bit) of the per-token scale areas
+  constexpr int kSclOff = NBUF * C::TILE_BYTES + C::STG_BYTES + C::QLDS_BYTES;
+  const uint32_t scl_stage = (uint32_t)(uintptr_t)((LDS_AS uint8_t*)ring + kSclOff);
+  const uint32_t scl_ring = scl_stage + 2 * 512;
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -485,11 +510,13 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       int bytes[2];
       uint32_t off[2];  // sparse: this lane's row offset in each half
       uint8_t* dst;
+      int sslot;        // fp8: staging slot (per-token scales go to the same slot)
     };
     // Resources of the next tile to load (ring slot i % NBUF); advances the cursor.
     auto prepare = [&](int i) __attribute__((always_inline)) {
       TileLoad tl;
       tl.dst = F8 ? stg + (i & 1) * C::STG_TILE : ring + (i % NBUF) * C::TILE_BYTES;
+      tl.sslot = i & 1;
       if constexpr (SP) {
         tl.off[0] = sp_offset(spA0, spG0);
         tl.off[1] = sp_offset(spA1, spG1);
@@ -551,7 +578,30 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           0x00020000);
       if constexpr (F8) {
         LDS_AS void* dst = (LDS_AS void*)(tl.dst + th * 16 * D + r * 64 * C::G);
-        const int voff = C::G * lane + sgpr_here(r * 64 * C::G);
+        int voff;
+        if constexpr (PT) {
+          // the codes of a half tile are contiguous in staging, but in the
+          // cache each row is followed by its 16-byte scale pad
+          // (formed here from an SGPR constant, not hoisted into a VGPR per copy)
+          const uint32_t c = (uint32_t)(C::G * lane) + (uint32_t)sgpr_here(r * 64 * C::G);
+          voff = (int)(c + (c / D) * kPerTokenPad);  // c: code byte within the half tile
+          if (k == 0 && wave == 0) {
+            // the 16 inline scales of each half: lane l < 16 reads row l's
+            // scale into slot l of a 256-byte area; rows past the segment
+            // (and lanes >= 16) read as 0 through the range check
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const __amdgpu_buffer_rsrc_t rsh = __builtin_amdgcn_make_buffer_rsrc(
+                  (void*)tl.base[h2], (short)0, tl.bytes[h2], 0x00020000);
+              const int soff = lane < 16 ? lane * C::SRC_ROW + D : tl.bytes[h2];
+              __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                  rsh, (LDS_AS uint8_t*)ring + kSclOff + tl.sslot * 512 + h2 * 256, 4, soff, 0, 0,
+                  0);
+            }
+          }
+        } else {
+          voff = C::G * lane + sgpr_here(r * 64 * C::G);
+        }
         // the size operand is spelled as a literal: given as a template
         // constant, the host pass drops the kernel's launch stub
         if constexpr (C::G == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, 0, 0, 0);
@@ -593,6 +643,20 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           ds_write_b128_asm(widen_dst(x, k0 + i), e4m3x8_to_bf16x8(v[i]));
         });
       });
+      if constexpr (PT) {
+        // the tile's 32 token scales: staging slot x % 2 (two 256-byte
+        // halves, row l of a half at float l) -> ring slot x % NBUF (float t)
+        if (wave == 0 && lane < 32) {
+          uint32_t sc = ds_read_b32_asm(scl_stage + (x & 1) * 512 + (lane >> 4) * 256 +
+                                        (lane & 15) * 4);
+          lds_wait<0>(sc);
+          ds_write_b32_asm(scl_ring + (x % NBUF) * 128 + lane * 4, sc);
+        }
+      }
+    };
+    // per-token scales of the four consecutive positions t .. t+3 of ring tile x
+    auto token_scales4 = [&](int x, int t) __attribute__((always_inline)) {
+      return ds_read_b128_asm(scl_ring + (x % NBUF) * 128 + t * 4);
     };
 
     // Q fragments of this wave's heads (B operand of S^T = K Q^T): the first
@@ -927,7 +991,9 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       // not read before iteration i+NBUF-1, so the loads may be spread over
       // the whole iteration and leave the memory pipeline at about the rate
       // it drains instead of blocking the wave in a burst).
-      constexpr int TOT_STEPS = HPW == 32 ? C::NKS + 2 * C::NVB : C::NKS;
+      // fp8: the staged tile is waited for at the top of the next iteration,
+      // so its loads go out over the QK^T steps only and land during PV.
+      constexpr int TOT_STEPS = (HPW == 32 && !F8) ? C::NKS + 2 * C::NVB : C::NKS;
       auto dma_at = [&](int step) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < C::NIW; ++k)
@@ -975,8 +1041,22 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
             q1 = q2;
           });
         }
-        // position of s[r] is 8*(r/4) + 4*(lane/32) + r%4; mask past the
-        // segment and past the row's causal limit (multi-token decode)
+        // position of s[r] is 8*(r/4) + 4*(lane/32) + r%4.  Per-token caches:
+        // scores and PV weights are multiplied by the scales of those
+        // positions (read twice from LDS rather than held in 16 registers)
+        auto scale_by_tokens = [&](f32x16& x) __attribute__((always_inline)) {
+          u32x4 g[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) g[q] = token_scales4(i, 8 * q + 4 * (lane >> 5));
+          static_for<4>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
+            lds_wait<3 - q>(g[q]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[4 * q + r] *= __uint_as_float(g[q][r]);
+          });
+        };
+        if constexpr (PT) scale_by_tokens(s);  // before the mask: zero rows have scale 0
+        // mask past the segment and past the row's causal limit (multi-token decode)
         const int t0 = ts + i * kTile;
         if (nvalid < kTile || t0 + kTile > vis_n) {
           const int lim = min(nvalid, row_end - t0);
@@ -1011,13 +1091,25 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
                           (f32x8){pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]};
           l_part += ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
         }
+        if constexpr (PT) {
+          // per-token caches: the PV weights are bf16(p_t * scale_t) and o is
+          // normalised by the sum of the bf16(p_t), so a lone position gives
+          // its row exactly when its scale is exact in bf16
+          const f32x8 r01 =
+              __builtin_convertvector(__builtin_convertvector(
+                  (f32x8){pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]}, bf16x8), f32x8) +
+              __builtin_convertvector(__builtin_convertvector(
+                  (f32x8){pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]}, bf16x8), f32x8);
+          lr_part += ((r01[0] + r01[1]) + (r01[2] + r01[3])) + ((r01[4] + r01[5]) + (r01[6] + r01[7]));
+          scale_by_tokens(pr);
+        }
         const bf16x8 p0 = __builtin_convertvector(
             (f32x8){pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]}, bf16x8);
         const bf16x8 p1 = __builtin_convertvector(
             (f32x8){pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]}, bf16x8);
         // the running sum that normalises o adds the bf16 weights the MFMA
         // uses, so o is an exact convex combination of V rows with them
-        {
+        if constexpr (!PT) {
           const f32x8 r01 = __builtin_convertvector(p0, f32x8) + __builtin_convertvector(p1, f32x8);
           lr_part += ((r01[0] + r01[1]) + (r01[2] + r01[3])) + ((r01[4] + r01[5]) + (r01[6] + r01[7]));
         }
@@ -1063,8 +1155,22 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks], s1, 0, 0, 0);
           dma_at(ks);
         });
-        // position of s_th[r] is 16*th + 4*(lane/16) + r; mask past the
-        // segment and past the row's causal limit (multi-token decode)
+        // position of s_th[r] is 16*th + 4*(lane/16) + r
+        f32x8 tsc;  // per-token caches: the scale of each of those positions
+        if constexpr (PT) {
+          u32x4 g0 = token_scales4(i, 4 * (lane >> 4));
+          u32x4 g1 = token_scales4(i, 16 + 4 * (lane >> 4));
+          lds_wait<0>(g1);
+          lds_wait<0>(g0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            tsc[r] = __uint_as_float(g0[r]);
+            tsc[4 + r] = __uint_as_float(g1[r]);
+            s0[r] *= tsc[r];  // before the mask: zero rows have scale 0
+            s1[r] *= tsc[4 + r];
+          }
+        }
+        // mask past the segment and past the row's causal limit (multi-token decode)
         const int t0 = ts + i * kTile;
         if (nvalid < kTile || t0 + kTile > vis_n) {
           const int lim = min(nvalid, row_end - t0);
@@ -1097,12 +1203,15 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], p.score_log2, -m_exp));
           pr[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.score_log2, -m_exp));
         }
-        const bf16x8 pb = __builtin_convertvector(pr, bf16x8);
         l_part += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
         {
-          const f32x8 r = __builtin_convertvector(pb, f32x8);
+          // the sum of the bf16 weights normalises o (per-token caches: the
+          // weights of P V are bf16(p_t * scale_t), the sum that of bf16(p_t))
+          const f32x8 r = __builtin_convertvector(__builtin_convertvector(pr, bf16x8), f32x8);
           lr_part += ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
         }
+        if constexpr (PT) pr *= tsc;
+        const bf16x8 pb = __builtin_convertvector(pr, bf16x8);
         {
           const uint32_t vbase0 = (uint32_t)(uintptr_t)tile + v_off0;
           const uint32_t vbase1 = (uint32_t)(uintptr_t)tile + v_off1;
@@ -1472,26 +1581,26 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
 
 // ---------------------------------------------------------------- dispatch
 
-template <int HPW, int W, int D, int DV, bool F8, bool SP = false>
+template <int HPW, int W, int D, int DV, bool F8, bool SP = false, bool PT = false>
 int launch_stage1(const Stage1Params& sp, int grid, hipStream_t st) {
-  constexpr int NBUF = stage1_ring_depth(HPW, W, D, F8);
-  hipLaunchKernelGGL((mla_stage1<HPW, W, D, DV, NBUF, F8, SP>), dim3(grid), dim3(64 * W), 0, st,
-                     sp);
+  constexpr int NBUF = stage1_ring_depth(HPW, W, D, F8, PT);
+  hipLaunchKernelGGL((mla_stage1<HPW, W, D, DV, NBUF, F8, SP, PT>), dim3(grid), dim3(64 * W), 0,
+                     st, sp);
   return (int)hipGetLastError();
 }
 
-template <int D, int DV, bool F8>
+template <int D, int DV, bool F8, bool PT = false>
 int launch_stage1_for(const HeadTiling& ht, const Stage1Params& sp, int grid, hipStream_t st) {
   if (ht.heads_per_wave == 32) {
     switch (ht.waves) {
-      case 4: return launch_stage1<32, 4, D, DV, F8>(sp, grid, st);
-      case 2: return launch_stage1<32, 2, D, DV, F8>(sp, grid, st);
-      default: return launch_stage1<32, 1, D, DV, F8>(sp, grid, st);
+      case 4: return launch_stage1<32, 4, D, DV, F8, false, PT>(sp, grid, st);
+      case 2: return launch_stage1<32, 2, D, DV, F8, false, PT>(sp, grid, st);
+      default: return launch_stage1<32, 1, D, DV, F8, false, PT>(sp, grid, st);
     }
   }
   // 16-head waves only arise for an odd number of 16-head groups (H % 32 != 0),
   // which always gives one wave per workgroup
-  return launch_stage1<16, 1, D, DV, F8>(sp, grid, st);
+  return launch_stage1<16, 1, D, DV, F8, false, PT>(sp, grid, st);
 }
 
 }  // namespace
@@ -1535,8 +1644,11 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   sp.page_shift = -1;
   for (int sh = 0; sh < 31; ++sh)
     if ((1 << sh) == a.page_size) sp.page_shift = sh;
-  sp.score_log2 = a.scale * kLog2e * (a.kv_fp8 ? a.k_scale : 1.f);
-  sp.out_scale = a.kv_fp8 ? a.k_scale : 1.f;
+  // a per-tensor fp8 scale multiplies every score and o; per-token scales
+  // are applied inside the kernel, position by position
+  const bool tensor_scale = a.kv_fp8 && !a.kv_pt;
+  sp.score_log2 = a.scale * kLog2e * (tensor_scale ? a.k_scale : 1.f);
+  sp.out_scale = tensor_scale ? a.k_scale : 1.f;
 
   const int units = a.split_mode == 0 ? a.batch * a.num_splits : a.num_splits;
   const int grid1 = (units + 7) / 8 * 8 * ht.head_chunks;
@@ -1546,7 +1658,10 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
       // the host admits the sparse gather only for this configuration
       if (a.kv_fp8 || a.head_size != 576 || ht.heads_per_wave != 32 || ht.waves != 4) return -1;
       err = launch_stage1<32, 4, 576, 512, false, true>(sp, grid1, st);
-    } else if (a.kv_fp8)
+    } else if (a.kv_pt)
+      err = a.head_size == 576 ? launch_stage1_for<576, 512, true, true>(ht, sp, grid1, st)
+                               : launch_stage1_for<320, 256, true, true>(ht, sp, grid1, st);
+    else if (a.kv_fp8)
       err = a.head_size == 576 ? launch_stage1_for<576, 512, true>(ht, sp, grid1, st)
                                : launch_stage1_for<320, 256, true>(ht, sp, grid1, st);
     else

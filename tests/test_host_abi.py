@@ -133,3 +133,42 @@ def test_fp8_query_is_refused():
     with pytest.raises(NotImplementedError):
         mla.mla_plan(shape(q_dtype=mla.MLA_FP8_E4M3), 100, 0, 256)
     assert _decode_raw(shape(q_dtype=mla.MLA_FP8_E4M3)) == mla.MLA_ERR_DTYPE
+
+
+# ---------------------------------------------------------------- per-token fp8 cache
+
+def test_per_token_cache_is_planned_like_the_others():
+    s, pt = shape(), shape(kv_dtype=mla.MLA_FP8_E4M3_PER_TOKEN)
+    assert mla.mla_plan(pt, 8192, 64 * 4608, 256) == mla.mla_plan(s, 8192, 64 * 4608, 256)
+    assert mla.mla_workspace_size(pt, mla.SPLIT_BALANCED, 64) == \
+        mla.mla_workspace_size(s, mla.SPLIT_BALANCED, 64)
+    with pytest.raises(NotImplementedError):  # MLA_ERR_DTYPE
+        mla.mla_plan(shape(kv_dtype=4), 1024, 0, 256)
+
+
+def test_per_token_cache_argument_checks():
+    pt = shape(kv_dtype=mla.MLA_FP8_E4M3_PER_TOKEN)
+    # k_scale is not read for a per-token cache, so 0 passes this check and
+    # the call is stopped by the next one (a missing workspace)
+    assert _decode_raw(pt, k_scale=0.0, splits=16) == mla.MLA_ERR_WORKSPACE
+    assert _decode_raw(pt, q=258) == mla.MLA_ERR_ARGUMENT
+    # the sparse gather is built for bf16 caches only
+    lib = mla.load_library()
+    st = lib.mla_decode_sparse(ctypes.byref(pt), 2048, 256, 256, 256, 256, 256, 0.07,
+                               pt.page_size, 1.0, 1, 0, 256, 256, None, 0, None)
+    assert st == mla.MLA_ERR_DTYPE
+
+
+def test_shape_of_checks_cache_row_width():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(2, 16, 576, dtype=torch.bfloat16)
+    bt = torch.zeros(2, 4, dtype=torch.int32)
+    pt = torch.zeros(8, 16, 576 + mla.MLA_PER_TOKEN_PAD, dtype=torch.uint8)
+    s = mla.shape_of(q, pt, bt, kv_dtype="fp8_per_token")
+    assert s.kv_dtype == mla.MLA_FP8_E4M3_PER_TOKEN and s.head_size == 576
+    with pytest.raises(ValueError):
+        mla.shape_of(q, pt, bt, kv_dtype="fp8_e4m3")  # rows 16 bytes too wide
+    with pytest.raises(ValueError):
+        mla.shape_of(q, torch.zeros(8, 16, 576, dtype=torch.uint8), bt, kv_dtype="fp8_per_token")
+    with pytest.raises(ValueError):
+        mla.shape_of(q, torch.zeros(8, 16, 576, dtype=torch.bfloat16), bt, kv_dtype="fp8_e4m3")
