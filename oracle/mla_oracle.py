@@ -25,6 +25,9 @@ What it computes (decode attention of one latent query per head):
 * For an fp8 cache one per-layer scale multiplies both K and V
   (Triton MLA page, data flow: ``k_scale = v_scale = layer._k_scale``); for a
   bf16 cache it has no effect (same listing's comment on the fp8 check).
+* A per-token-head cache (Triton MLA page, key files: fp8 and int8 modes
+  whose rows are padded to hold an inline scale) stores each token's codes
+  followed by its float32 scale; the token's K and V are code * scale.
 
 The online softmax (lshu.cn article, section 7) and the split-KV merge
 (section 12) are exact rewrites of this plain softmax, so ``decode`` is the
@@ -75,30 +78,39 @@ def e4m3fn_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 PER_TOKEN_PAD = 16  # bytes after the codes of a per-token row: fp32 scale + 12 unused
+PER_TOKEN_DTYPES = ("fp8_per_token", "int8_per_token")
+
+
+def int8_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Two's-complement signed bytes."""
+    return np.asarray(bits, dtype=np.uint8).view(np.int8).astype(np.float64)
 
 
 def row_width(kv_dtype: str, head_size: int) -> int:
-    """Stored elements (bytes for fp8) per cache row: the head_size values, and
-    for the per-token layout the padding that holds the inline scale (Triton
-    MLA page, key files: in per-token-head modes the cache shape pads head_dim
-    to hold an inline scale)."""
-    return head_size + PER_TOKEN_PAD if kv_dtype == "fp8_per_token" else head_size
+    """Stored elements (bytes for fp8 / int8) per cache row: the head_size
+    values, and for the per-token layouts the padding that holds the inline
+    scale (Triton MLA page, key files: in the per-token-head modes, fp8 and
+    int8 among them, the cache shape pads head_dim to hold an inline scale)."""
+    return head_size + PER_TOKEN_PAD if kv_dtype in PER_TOKEN_DTYPES else head_size
 
 
 def decode_kv(kv_bits: np.ndarray, kv_dtype: str, k_scale: float) -> np.ndarray:
     """Cache rows as float64.  fp8 values are multiplied by the fp32-rounded
     k_scale (exact in float64); bf16 rows ignore k_scale.  Per-token rows
-    ``[e4m3fn codes (D) | fp32 scale | pad]`` decode to code * scale of that
-    token (exact in float64); k_scale does not apply to them."""
+    ``[codes (D) | fp32 scale | pad]``, codes e4m3fn or signed int8, decode
+    to code * scale of that token (exact in float64); k_scale does not apply
+    to them."""
     if kv_dtype == "bf16":
         return bf16_bits_to_f64(kv_bits)
     if kv_dtype == "fp8_e4m3":
         return e4m3fn_bits_to_f64(kv_bits) * float(np.float32(k_scale))
-    if kv_dtype == "fp8_per_token":
+    if kv_dtype in PER_TOKEN_DTYPES:
         rows = np.ascontiguousarray(kv_bits, dtype=np.uint8)
         D = rows.shape[-1] - PER_TOKEN_PAD
         scale = rows[..., D:D + 4].copy().view("<f4")[..., 0].astype(np.float64)
-        return e4m3fn_bits_to_f64(rows[..., :D]) * scale[..., None]
+        codes = (e4m3fn_bits_to_f64 if kv_dtype == "fp8_per_token" else int8_bits_to_f64)(
+            rows[..., :D])
+        return codes * scale[..., None]
     raise ValueError(f"unknown kv dtype {kv_dtype!r}")
 
 
@@ -341,4 +353,5 @@ __all__ = [
     "physical_slot", "gather_rows", "attend", "decode", "segment_bounds", "merge_partials",
     "merge_normalised", "segment_partial", "decode_split", "pages_split_count",
     "visible_keys", "decode_mtp", "decode_sparse", "row_width", "PER_TOKEN_PAD",
+    "PER_TOKEN_DTYPES", "int8_bits_to_f64",
 ]

@@ -53,9 +53,10 @@ def dense_keys(inp, b):
     if w.kv_dtype == "bf16":
         t = torch.from_numpy(flat.view(np.int16).copy()).view(torch.bfloat16)
         return t.to(torch.float64)
-    if w.kv_dtype == "fp8_per_token":
+    if w.kv_dtype in ("fp8_per_token", "int8_per_token"):
         D = w.head_size
-        codes = torch.from_numpy(flat[:, :D].copy()).view(torch.float8_e4m3fn).to(torch.float64)
+        code_t = torch.float8_e4m3fn if w.kv_dtype == "fp8_per_token" else torch.int8
+        codes = torch.from_numpy(flat[:, :D].copy()).view(code_t).to(torch.float64)
         scale = torch.from_numpy(flat[:, D:D + 4].copy()).view(torch.float32).to(torch.float64)
         return codes * scale
     t = torch.from_numpy(flat.copy()).view(torch.float8_e4m3fn)
@@ -696,4 +697,83 @@ def test_planted_per_token_mistakes_are_caught(monkeypatch):
         monkeypatch.setattr(OM, "decode_kv", fake)
         with pytest.raises(AssertionError):
             test_per_token_cache_matches_torch_sdpa(576)
+        monkeypatch.undo()
+
+
+# ---------------------------------------------------------------- per-token int8 cache
+# (the same pages list int8 among the per-token-head modes; rows here are
+# [signed int8 codes (D) | fp32 scale | 12 pad bytes], value = code * scale)
+
+def test_int8_rows_decode_like_torch_times_their_scale():
+    inp = W.small_case(seed=71, batch=2, num_heads=16, head_size=576, kv_lora_rank=512,
+                       page_size=16, seq_lens=(40, 7), kv_dtype=W.INT8_PER_TOKEN)
+    rows = inp.kv_bits.reshape(-1, inp.kv_bits.shape[-1])
+    D = 576
+    mine = O.decode_kv(rows, "int8_per_token", 1.0)
+    codes = torch.from_numpy(rows[:, :D].copy()).view(torch.int8).to(torch.float64)
+    scale = torch.from_numpy(rows[:, D:D + 4].copy()).view(torch.float32).to(torch.float64)
+    assert np.array_equal(mine, (codes * scale).numpy())
+    assert O.row_width("int8_per_token", D) == D + 16
+
+
+def test_int8_every_code_decodes_to_itself():
+    """All 256 byte values with scale 1 give -128..127 (two's complement):
+    a reading of the bytes as unsigned, or as sign-magnitude, fails."""
+    rows = np.zeros((1, 256 + 16), dtype=np.uint8)
+    rows[0, :256] = np.arange(256, dtype=np.uint8)
+    rows[0, 256:260] = np.array([1.0], dtype="<f4").view(np.uint8)
+    got = O.decode_kv(rows, "int8_per_token", 1.0)[0]
+    want = np.array([b if b < 128 else b - 256 for b in range(256)], dtype=np.float64)
+    assert np.array_equal(got, want)
+
+
+def test_int8_quantisation_round_trips_within_half_a_step():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((64, 320), dtype=np.float32) * rng.uniform(0.01, 100, (64, 1)).astype(
+        np.float32)
+    rows = W.per_token_int8_rows(x)
+    dec = O.decode_kv(rows, "int8_per_token", 1.0)
+    amax = np.abs(x).max(axis=1).astype(np.float64)
+    step = amax / 127.0
+    assert np.all(np.abs(np.abs(dec).max(axis=1) - amax) <= amax * 2.0 ** -22)
+    assert np.all(np.abs(dec - x) <= step[:, None] * (0.5 + 2.0 ** -20))
+
+
+@pytest.mark.parametrize("D", [576, 320])
+def test_int8_cache_matches_torch_sdpa(D):
+    inp = W.small_case(seed=72, batch=3, num_heads=16, head_size=D, kv_lora_rank=D - 64,
+                       page_size=16, seq_lens=(37, 100, 1), kv_dtype=W.INT8_PER_TOKEN)
+    w = inp.workload
+    o, lse = run(inp)
+    sc = float(np.float32(w.scale))
+    for b in range(3):
+        K = dense_keys(inp, b)
+        q = q_of(inp, b)
+        ref = torch.nn.functional.scaled_dot_product_attention(q[None], K[None],
+                                                               K[None, :, :D - 64], scale=sc)[0]
+        ref_lse = torch.logsumexp((q @ K.T) * sc, dim=1)
+        assert np.abs(o[b] - ref.numpy()).max() < 1e-12
+        assert np.abs(lse[b] - ref_lse.numpy()).max() < 1e-12
+
+
+def test_planted_int8_mistakes_are_caught(monkeypatch):
+    """Reading the int8 codes as unsigned bytes, or as fp8 codes, fails the
+    SDPA pin."""
+    real = OM.decode_kv
+
+    def unsigned(bits, dt, ks):
+        if dt != "int8_per_token":
+            return real(bits, dt, ks)
+        b = np.asarray(bits)
+        D = b.shape[-1] - 16
+        scale = b[..., D:D + 4].copy().view("<f4")[..., 0].astype(np.float64)
+        return b[..., :D].astype(np.float64) * scale[..., None]
+
+    def as_fp8(bits, dt, ks):
+        return real(bits, "fp8_per_token" if dt == "int8_per_token" else dt, ks)
+
+    for fake in (unsigned, as_fp8):
+        monkeypatch.setattr(OM, "decode_kv", fake)
+        with pytest.raises(AssertionError):
+            test_int8_cache_matches_torch_sdpa(576)
         monkeypatch.undo()

@@ -30,6 +30,7 @@ FP8_E4M3 = "fp8_e4m3"
 # per-token quantised fp8: each row [e4m3fn codes (D) | fp32 scale | 12 zero
 # bytes], scale = max|row| / 448 of the token's fp32 row
 FP8_PER_TOKEN = "fp8_per_token"
+INT8_PER_TOKEN = "int8_per_token"
 PER_TOKEN_PAD = 16
 
 # fp32(192 ** -0.5): the softmax scale of a DeepSeek-V3 style head
@@ -47,7 +48,7 @@ class Workload:
     kv_lora_rank: int       # D_v
     page_size: int
     num_blocks: int
-    kv_dtype: str           # BF16 or FP8_E4M3
+    kv_dtype: str           # BF16, FP8_E4M3, FP8_PER_TOKEN or INT8_PER_TOKEN
     k_scale: float
     scale: float
     seq_lens_fixed: Optional[Sequence[int]] = None
@@ -117,6 +118,12 @@ WORKLOADS: Dict[str, Workload] = {
             scale=DSV3_SCALE, seq_len_range=(1024, 8192), parity_splits=(16, 1),
             description="B=64 H=128 D=576/512 per-token fp8 cache (inline fp32 scale, rows of "
                         "592 B), page 64, 8192 pages, seq_lens U[1024,8192]"),
+        Workload(
+            name="int8_pt", seed=9, batch=64, num_heads=128, head_size=576, kv_lora_rank=512,
+            page_size=64, num_blocks=8192, kv_dtype=INT8_PER_TOKEN, k_scale=1.0,
+            scale=DSV3_SCALE, seq_len_range=(1024, 8192), parity_splits=(16, 1),
+            description="B=64 H=128 D=576/512 per-token int8 cache (inline fp32 scale, rows of "
+                        "592 B), page 64, 8192 pages, seq_lens U[1024,8192]"),
     ]
 }
 
@@ -161,6 +168,19 @@ def per_token_fp8_rows(pool: np.ndarray) -> np.ndarray:
     codes = f32_to_e4m3fn_bits(pool / s)
     out = np.zeros(pool.shape[:-1] + (pool.shape[-1] + PER_TOKEN_PAD,), dtype=np.uint8)
     out[..., :pool.shape[-1]] = codes
+    out[..., pool.shape[-1]:pool.shape[-1] + 4] = s.view(np.uint8)
+    return out
+
+
+def per_token_int8_rows(pool: np.ndarray) -> np.ndarray:
+    """fp32 rows [..., D] -> per-token quantised rows [..., D + 16] bytes:
+    int8 codes round(row / s) (symmetric, in [-127, 127]), then s as fp32,
+    then zeros, with s = fp32(max|row| / 127) (1 for an all-zero row)."""
+    amax = np.abs(pool).max(axis=-1, keepdims=True).astype(np.float32)
+    s = np.where(amax > 0, amax / np.float32(127.0), np.float32(1.0)).astype(np.float32)
+    codes = np.clip(np.rint(pool / s), -127, 127).astype(np.int8)
+    out = np.zeros(pool.shape[:-1] + (pool.shape[-1] + PER_TOKEN_PAD,), dtype=np.uint8)
+    out[..., :pool.shape[-1]] = codes.view(np.uint8)
     out[..., pool.shape[-1]:pool.shape[-1] + 4] = s.view(np.uint8)
     return out
 
@@ -218,6 +238,8 @@ def generate(workload: Workload | str, *, seq_lens: Optional[Sequence[int]] = No
         kv_bits = f32_to_bf16_bits(pool)
     elif w.kv_dtype == FP8_PER_TOKEN:
         kv_bits = per_token_fp8_rows(pool)
+    elif w.kv_dtype == INT8_PER_TOKEN:
+        kv_bits = per_token_int8_rows(pool)
     else:
         kv_bits = f32_to_e4m3fn_bits(pool / np.float32(w.k_scale))
     inp = DecodeInputs(workload=w, q_bits=q_bits, kv_bits=kv_bits, block_table=table,
