@@ -58,7 +58,7 @@ def algorithmic(inp):
     B, H, D, DV, P = w.batch, w.num_heads, w.head_size, w.kv_lora_rank, w.page_size
     # bytes of one cache row the method needs: bf16 values, fp8 codes, or fp8
     # codes and the token's fp32 scale (the rest of the per-token pad is unused)
-    row = {"bf16": 2 * D, "fp8_per_token": D + 4}.get(w.kv_dtype, D)
+    row = {"bf16": 2 * D, "fp8_per_token": D + 4, "int8_per_token": D + 4}.get(w.kv_dtype, D)
     ql = w.q_len
     if w.topk:
         # sparse decode: the selected rows, the index lists and one table entry each
@@ -208,7 +208,7 @@ def main():
     q = torch.from_numpy(inp.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     if w.kv_dtype == "bf16":
         kv = torch.from_numpy(inp.kv_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    elif w.kv_dtype == "fp8_per_token":
+    elif w.kv_dtype in ("fp8_per_token", "int8_per_token"):
         kv = torch.from_numpy(inp.kv_bits).to(dev)  # uint8 rows: codes | fp32 scale | pad
     else:
         kv = torch.from_numpy(inp.kv_bits).view(torch.float8_e4m3fn).to(dev)

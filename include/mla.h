@@ -65,7 +65,7 @@ typedef enum mla_status {
                             page, Limites et échecs: block sizes are multiples of 16)   */
   MLA_ERR_DTYPE = 4,     /* q not bf16 (an fp8 query is refused: "Triton と MLA" page,
                             境界と失敗), kv not bf16 / fp8 e4m3fn (per-tensor or
-                            per-token scale), o not bf16/fp32                            */
+                            per-token scale) / per-token int8, o not bf16/fp32           */
   MLA_ERR_SHAPE = 5,     /* batch < 1, num_heads not a positive multiple of 16,
                             num_blocks < 1 (empty cache), max_blocks_per_seq < 1, or a
                             size whose byte count overflows                              */
@@ -89,7 +89,11 @@ typedef enum mla_dtype {
    * page, 主要ファイル: in the per-token-head modes the cache's head_dim is
    * padded to hold an inline scale).  k_scale does not apply.  Rows start on
    * 16-byte boundaries (head_size + 16 is a multiple of 16). */
-  MLA_FP8_E4M3_PER_TOKEN = 3
+  MLA_FP8_E4M3_PER_TOKEN = 3,
+  /* Cache only: as MLA_FP8_E4M3_PER_TOKEN with signed (two's-complement)
+   * int8 codes; value = code * scale (the same page lists int8 among the
+   * per-token-head modes). */
+  MLA_INT8_PER_TOKEN = 4
 } mla_dtype;
 
 #define MLA_PER_TOKEN_PAD 16 /* bytes after the codes of a per-token cache row */
@@ -127,7 +131,7 @@ typedef enum mla_split_mode {
 /* Problem shape.  Layouts (all row-major, densely packed unless noted):
  *   q           [batch, num_heads, head_size]              q_dtype (bf16)
  *   kv_cache    [num_blocks, page_size, head_size]         kv_dtype; row =
- *               [kv_c (kv_lora_rank) | k_pe (64)]; with MLA_FP8_E4M3_PER_TOKEN
+ *               [kv_c (kv_lora_rank) | k_pe (64)]; per-token caches are
  *               [num_blocks, page_size, head_size + MLA_PER_TOKEN_PAD] bytes
  *   block_table [batch, max_blocks_per_seq]                int32; entries at
  *               index >= ceil(seq_lens[b] / page_size) are never read
@@ -144,8 +148,8 @@ typedef struct mla_shape {
   int32_t num_blocks;         /* pages in the pool, >= 1                    */
   int32_t max_blocks_per_seq; /* block_table row stride in entries, >= 1    */
   int32_t q_dtype;            /* mla_dtype: MLA_BF16                        */
-  int32_t kv_dtype;           /* mla_dtype: MLA_BF16, MLA_FP8_E4M3 or
-                                 MLA_FP8_E4M3_PER_TOKEN                     */
+  int32_t kv_dtype;           /* mla_dtype: MLA_BF16, MLA_FP8_E4M3,
+                                 MLA_FP8_E4M3_PER_TOKEN or MLA_INT8_PER_TOKEN */
   int32_t o_dtype;            /* mla_dtype: MLA_BF16 or MLA_FP32            */
 } mla_shape;
 

@@ -48,7 +48,8 @@ HeadTiling head_tiling(int32_t heads) {
 static int64_t stage1_lds(const mla_shape& s) {
   const HeadTiling t = head_tiling(s.num_heads);
   return stage1_lds_bytes(t.heads_per_wave, t.waves, s.head_size,
-                          s.kv_dtype != MLA_BF16, s.kv_dtype == MLA_FP8_E4M3_PER_TOKEN);
+                          s.kv_dtype != MLA_BF16,
+                          s.kv_dtype == MLA_FP8_E4M3_PER_TOKEN || s.kv_dtype == MLA_INT8_PER_TOKEN);
 }
 
 }  // namespace mla
@@ -63,7 +64,7 @@ static mla_status check_shape(const mla_shape* s) {
   if (s->page_size <= 0 || s->page_size % 16 != 0) return MLA_ERR_PAGE_SIZE;
   if (s->q_dtype != MLA_BF16) return MLA_ERR_DTYPE;
   if (s->kv_dtype != MLA_BF16 && s->kv_dtype != MLA_FP8_E4M3 &&
-      s->kv_dtype != MLA_FP8_E4M3_PER_TOKEN)
+      s->kv_dtype != MLA_FP8_E4M3_PER_TOKEN && s->kv_dtype != MLA_INT8_PER_TOKEN)
     return MLA_ERR_DTYPE;
   if (s->o_dtype != MLA_BF16 && s->o_dtype != MLA_FP32) return MLA_ERR_DTYPE;
   if (s->batch < 1 || s->num_heads < 16 || s->num_heads % 16 != 0 || s->num_blocks < 1 ||
@@ -184,7 +185,8 @@ static mla_status decode_stages(const mla_shape* shape, int32_t q_len, const voi
     return MLA_ERR_SPLITS;
   if (!(isfinite(scale) && scale > 0.f)) return MLA_ERR_ARGUMENT;
   const bool fp8 = shape->kv_dtype != MLA_BF16;
-  const bool per_token = shape->kv_dtype == MLA_FP8_E4M3_PER_TOKEN;
+  const bool per_token =
+      shape->kv_dtype == MLA_FP8_E4M3_PER_TOKEN || shape->kv_dtype == MLA_INT8_PER_TOKEN;
   if (fp8 && !per_token && !(isfinite(k_scale) && k_scale > 0.f)) return MLA_ERR_ARGUMENT;
   if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
       !aligned(block_table, 4) || !aligned(seq_lens, 4))
@@ -213,7 +215,9 @@ static mla_status decode_stages(const mla_shape* shape, int32_t q_len, const voi
   a.page_size = shape->page_size;
   a.bt_stride = shape->max_blocks_per_seq;
   a.kv_fp8 = fp8 ? 1 : 0;
-  a.kv_pt = per_token ? 1 : 0;
+  a.kv_pt = shape->kv_dtype == MLA_FP8_E4M3_PER_TOKEN ? 1
+            : shape->kv_dtype == MLA_INT8_PER_TOKEN   ? 2
+                                                      : 0;
   a.o_f32 = shape->o_dtype == MLA_FP32 ? 1 : 0;
   a.split_mode = split_mode;
   a.num_splits = num_kv_splits;
@@ -328,7 +332,7 @@ const char* mla_status_string(int32_t status) {
     case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
     case MLA_ERR_HEAD_SIZE: return "MLA_ERR_HEAD_SIZE: head_size must be 576 or 320 with kv_lora_rank = head_size - 64";
     case MLA_ERR_PAGE_SIZE: return "MLA_ERR_PAGE_SIZE: page_size must be a positive multiple of 16 and match the shape";
-    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: q must be bf16, kv bf16 or fp8 e4m3fn (per-tensor or per-token scale; bf16 only for sparse decode), o bf16 or fp32";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: q must be bf16, kv bf16, fp8 e4m3fn (per-tensor or per-token scale) or per-token int8 (bf16 only for sparse decode), o bf16 or fp32";
     case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: batch, heads (multiple of 16), num_blocks or table width out of range";
     case MLA_ERR_SPLITS: return "MLA_ERR_SPLITS: num_kv_splits or split_mode out of range";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";

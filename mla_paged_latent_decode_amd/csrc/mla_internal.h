@@ -42,7 +42,7 @@ HeadTiling head_tiling(int32_t heads);
 // (1 KB per step and wave), as many as the remaining LDS holds, up to 12.
 constexpr int kLdsBytes = 160 * 1024;
 
-// Per-token fp8 caches (rows of D codes + a 16-byte inline scale pad) run
+// Per-token caches (rows of D fp8 or int8 codes + a 16-byte inline scale pad) run
 // the plain fp8 loop with a ring of 2 and keep each tile's 32 scales in LDS:
 // two staging slots of 2 x 256 B and a ring of 128 B slots.
 constexpr int kPerTokenPad = 16;
@@ -89,7 +89,7 @@ struct DecodeArgs {
   int32_t page_size;
   int32_t bt_stride;
   int32_t kv_fp8;
-  int32_t kv_pt;  // per-token fp8 rows: D codes + an inline fp32 scale (16-byte pad)
+  int32_t kv_pt;  // per-token rows (D codes + an inline fp32 scale): 1 e4m3fn, 2 int8
   int32_t o_f32;
   int32_t split_mode;
   int32_t num_splits;

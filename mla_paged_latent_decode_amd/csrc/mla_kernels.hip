@@ -172,6 +172,21 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 v) {
   return r;
 }
 
+// Eight signed int8 codes (one per byte, lowest byte first) to eight bf16:
+// every value in [-128, 127] is exact in bf16.
+__device__ __forceinline__ u32x4 i8x8_to_bf16x8(u32x2 v) {
+  u32x4 r;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const int x = (int)v[w];
+    const f32x2 lo = {(float)((x << 24) >> 24), (float)((x << 16) >> 24)};
+    const f32x2 hi = {(float)((x << 8) >> 24), (float)(x >> 24)};
+    r[2 * w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+    r[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+  }
+  return r;
+}
+
 // LDS operation schedule of one P V^T pass: step s issues the two
 // transposed V reads of step s+3, then (fp8 caches) the staging read of
 // widened block k at s = 3k, or the write of block k at s = 3k+2, then waits
@@ -311,7 +326,8 @@ __device__ __forceinline__ int64_t total_cost(const int32_t* seq_lens, int B, in
 
 // ---------------------------------------------------------------- stage 1
 
-template <int HPW, int W, int D, int DV, int NBUF, bool F8, bool PT = false>
+// PT: 0 = no per-token scales, 1 = per-token e4m3fn codes, 2 = per-token int8 codes
+template <int HPW, int W, int D, int DV, int NBUF, bool F8, int PT = 0>
 struct Cfg {
   static constexpr int NKQ = D / 32;                       // 32-wide d groups per row
   static constexpr int NBLK = 2 * NKQ;                     // 1 KB LDS blocks per tile
@@ -377,7 +393,7 @@ __device__ __forceinline__ int tile_slot(int t16, int c4) {
   return (t16 ^ (8 * (c4 & 1) + 4 * (c4 >> 1))) + 16 * c4;
 }
 
-template <int HPW, int W, int D, int DV, int NBUF, bool F8, bool SP, bool PT>
+template <int HPW, int W, int D, int DV, int NBUF, bool F8, bool SP, int PT>
 __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   using C = Cfg<HPW, W, D, DV, NBUF, F8, PT>;
   static_assert(!SP || (!F8 && NBUF == 3),
@@ -640,7 +656,8 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           constexpr int i = decltype(ic)::value;
           // issued after read i: the other nb-1-i reads and i writes
           lds_wait<nb - 1>(v[i]);
-          ds_write_b128_asm(widen_dst(x, k0 + i), e4m3x8_to_bf16x8(v[i]));
+          ds_write_b128_asm(widen_dst(x, k0 + i),
+                            PT == 2 ? i8x8_to_bf16x8(v[i]) : e4m3x8_to_bf16x8(v[i]));
         });
       });
       if constexpr (PT) {
@@ -1581,7 +1598,7 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
 
 // ---------------------------------------------------------------- dispatch
 
-template <int HPW, int W, int D, int DV, bool F8, bool SP = false, bool PT = false>
+template <int HPW, int W, int D, int DV, bool F8, bool SP = false, int PT = 0>
 int launch_stage1(const Stage1Params& sp, int grid, hipStream_t st) {
   constexpr int NBUF = stage1_ring_depth(HPW, W, D, F8, PT);
   hipLaunchKernelGGL((mla_stage1<HPW, W, D, DV, NBUF, F8, SP, PT>), dim3(grid), dim3(64 * W), 0,
@@ -1589,7 +1606,7 @@ int launch_stage1(const Stage1Params& sp, int grid, hipStream_t st) {
   return (int)hipGetLastError();
 }
 
-template <int D, int DV, bool F8, bool PT = false>
+template <int D, int DV, bool F8, int PT = 0>
 int launch_stage1_for(const HeadTiling& ht, const Stage1Params& sp, int grid, hipStream_t st) {
   if (ht.heads_per_wave == 32) {
     switch (ht.waves) {
@@ -1658,9 +1675,12 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
       // the host admits the sparse gather only for this configuration
       if (a.kv_fp8 || a.head_size != 576 || ht.heads_per_wave != 32 || ht.waves != 4) return -1;
       err = launch_stage1<32, 4, 576, 512, false, true>(sp, grid1, st);
-    } else if (a.kv_pt)
-      err = a.head_size == 576 ? launch_stage1_for<576, 512, true, true>(ht, sp, grid1, st)
-                               : launch_stage1_for<320, 256, true, true>(ht, sp, grid1, st);
+    } else if (a.kv_pt == 1)
+      err = a.head_size == 576 ? launch_stage1_for<576, 512, true, 1>(ht, sp, grid1, st)
+                               : launch_stage1_for<320, 256, true, 1>(ht, sp, grid1, st);
+    else if (a.kv_pt == 2)
+      err = a.head_size == 576 ? launch_stage1_for<576, 512, true, 2>(ht, sp, grid1, st)
+                               : launch_stage1_for<320, 256, true, 2>(ht, sp, grid1, st);
     else if (a.kv_fp8)
       err = a.head_size == 576 ? launch_stage1_for<576, 512, true>(ht, sp, grid1, st)
                                : launch_stage1_for<320, 256, true>(ht, sp, grid1, st);

@@ -1,9 +1,10 @@
-"""GPU parity of decode over a per-token quantised fp8 cache: each row holds
-head_size e4m3fn codes and its own float32 scale inline in a 16-byte pad
-(Triton MLA page, key files: the per-token-head modes pad the cache's head_dim
-to hold an inline scale).  The HIP path runs through the C ABI (ctypes
-binding, kv dtype MLA_FP8_E4M3_PER_TOKEN) and is compared with the float64
-oracle, which decodes every row to code * scale of that token.
+"""GPU parity of decode over per-token quantised caches: each row holds
+head_size codes (e4m3fn or signed int8) and its own float32 scale inline in a
+16-byte pad (Triton MLA page, key files: the per-token-head modes, fp8 and
+int8 among them, pad the cache's head_dim to hold an inline scale).  The HIP
+path runs through the C ABI (ctypes binding, kv dtype MLA_FP8_E4M3_PER_TOKEN
+or MLA_INT8_PER_TOKEN) and is compared with the float64 oracle, which decodes
+every row to code * scale of that token.
 
 Tolerances (max-abs) are those of the per-tensor fp8 cache: o 3e-2, lse 3e-3.
 Where the scale of each row is exact in bf16 and a sequence has a single
@@ -20,6 +21,7 @@ pytestmark = pytest.mark.gpu
 
 TOL_O, TOL_LSE = 3e-2, 3e-3
 PAD = W.PER_TOKEN_PAD
+DTYPES = [W.FP8_PER_TOKEN, W.INT8_PER_TOKEN]
 
 
 @pytest.fixture(scope="module")
@@ -43,11 +45,11 @@ def to_dev(inp):
 def run_gpu(mla, inp, splits, mode, o_dtype=None, dev_inputs=None, k_scale=1.0):
     w = inp.workload
     q, kv, bt, sl = dev_inputs or to_dev(inp)
-    print(f"[per-token] B={w.batch} H={w.num_heads} D={w.head_size} P={w.page_size} "
-          f"q_len={w.q_len} mode={mode} S={splits}", flush=True)
+    print(f"[per-token] {w.kv_dtype} B={w.batch} H={w.num_heads} D={w.head_size} "
+          f"P={w.page_size} q_len={w.q_len} mode={mode} S={splits}", flush=True)
     o, lse = mla.mla_decode(q, kv, bt, sl, w.scale, w.page_size, k_scale, splits,
                             split_mode=mode, o_dtype=o_dtype or torch.bfloat16,
-                            kv_dtype="fp8_per_token")
+                            kv_dtype=w.kv_dtype)
     torch.cuda.synchronize()
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
@@ -79,9 +81,9 @@ def assert_close(o, lse, ro, rl, empty, label, rounding_slack=False):
     assert do <= TOL_O and dl <= TOL_LSE, (label, do, dl)
 
 
-def case(seed, H, D, P, sl, **kw):
+def case(seed, H, D, P, sl, dt=W.FP8_PER_TOKEN, **kw):
     return W.small_case(seed=seed, batch=len(sl), num_heads=H, head_size=D, kv_lora_rank=D - 64,
-                        page_size=P, seq_lens=sl, kv_dtype=W.FP8_PER_TOKEN, **kw)
+                        page_size=P, seq_lens=sl, kv_dtype=dt, **kw)
 
 
 def set_scales(inp, scales):
@@ -107,28 +109,30 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("dt", DTYPES)
 @pytest.mark.parametrize("c", range(len(CASES)))
 @pytest.mark.parametrize("mode,splits", [(0, 1), (0, 3), (1, 4), (1, 37)])
-def test_ragged_cases(mla, c, mode, splits):
+def test_ragged_cases(mla, c, mode, splits, dt):
     H, D, P, sl = CASES[c]
-    inp = case(300 + c, H, D, P, sl, table_pad=1)
+    inp = case(300 + c, H, D, P, sl, dt, table_pad=1)
     ro, rl = ref(inp)
     empty = np.asarray(inp.seq_lens) == 0
-    label = f"pt case{c} H={H} D={D} P={P} mode={mode} S={splits}"
+    label = f"{dt} case{c} H={H} D={D} P={P} mode={mode} S={splits}"
     o, lse = run_gpu(mla, inp, splits, mode, o_dtype=torch.float32)
     assert_close(o, lse, ro, rl, empty, label + " o=f32")
     o, lse = run_gpu(mla, inp, splits, mode)
     assert_close(o, lse, ro, rl, empty, label + " o=bf16", rounding_slack=True)
 
 
+@pytest.mark.parametrize("dt", DTYPES)
 @pytest.mark.parametrize("H,D", [(16, 576), (128, 576), (32, 320), (48, 320)])
 @pytest.mark.parametrize("mode,splits", [(0, 1), (1, 5)])
-def test_scales_differ_from_token_to_token(mla, H, D, mode, splits):
+def test_scales_differ_from_token_to_token(mla, H, D, mode, splits, dt):
     """Rows of one page carry scales 2^k apart (k in -2..1, seeded): a scale
     applied to the wrong position, or one scale for a whole tile, moves the
     scores by factors of 2 and fails the tolerance."""
     sl = (45, 200, 33)
-    inp = case(41, H, D, 16, sl, extra_pages=2)
+    inp = case(41, H, D, 16, sl, dt, extra_pages=2)
     rng = np.random.default_rng(42)
     D2 = D + PAD
     base = inp.kv_bits[..., D:D + 4].copy().view("<f4")[..., 0]
@@ -137,19 +141,23 @@ def test_scales_differ_from_token_to_token(mla, H, D, mode, splits):
     assert inp.kv_bits.shape[-1] == D2
     ro, rl = ref(inp)
     o, lse = run_gpu(mla, inp, splits, mode, o_dtype=torch.float32)
-    assert_close(o, lse, ro, rl, np.zeros(len(sl), bool), f"pt scales H={H} D={D} S={splits}")
+    assert_close(o, lse, ro, rl, np.zeros(len(sl), bool), f"{dt} scales H={H} D={D} S={splits}")
 
 
+@pytest.mark.parametrize("dt", DTYPES)
 @pytest.mark.parametrize("H,D", [(16, 576), (32, 576), (128, 576), (48, 320), (128, 320)])
 @pytest.mark.parametrize("mode,splits", [(0, 1), (1, 2)])
-def test_one_position_returns_the_scaled_row(mla, H, D, mode, splits):
+def test_one_position_returns_the_scaled_row(mla, H, D, mode, splits, dt):
     """A single position has softmax weight 1, so o is its kv_c codes times
-    its scale.  Each sequence's row runs through all finite e4m3fn codes and
-    has its own scale with at most 3 significant bits (exact in bf16), so
-    every product is exact in fp32 and must come back bit for bit."""
+    its scale.  Each sequence's row runs through all finite codes (254 e4m3fn
+    or 256 int8) and has its own scale with 2 significant bits (exact in
+    bf16), so every product is exact in fp32 and must come back bit for bit."""
     Dv, P, B = D - 64, 16, 3
     rng = np.random.default_rng(51)
-    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    if dt == W.FP8_PER_TOKEN:
+        finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    else:
+        finite = np.arange(256, dtype=np.uint8)
     nb = B + 2
     kv = np.zeros((nb, P, D + PAD), dtype=np.uint8)
     kv[..., :D] = rng.choice(finite, size=(nb, P, D))
@@ -160,7 +168,7 @@ def test_one_position_returns_the_scaled_row(mla, H, D, mode, splits):
     table = np.array([[b + 1, 0] for b in range(B)], dtype=np.int32)
     q = W.f32_to_bf16_bits(rng.standard_normal((B, H, D), dtype=np.float32) * 0.1)
     w = W.Workload(name="pt-codes", seed=51, batch=B, num_heads=H, head_size=D,
-                   kv_lora_rank=Dv, page_size=P, num_blocks=nb, kv_dtype=W.FP8_PER_TOKEN,
+                   kv_lora_rank=Dv, page_size=P, num_blocks=nb, kv_dtype=dt,
                    k_scale=1.0, scale=W.DSV3_SCALE, seq_lens_fixed=(1,) * B)
     inp = W.DecodeInputs(workload=w, q_bits=q, kv_bits=kv, block_table=table,
                          seq_lens=np.ones(B, dtype=np.int32))
@@ -170,45 +178,50 @@ def test_one_position_returns_the_scaled_row(mla, H, D, mode, splits):
     assert np.abs(l32 - rl).max() <= 1e-4 * max(1.0, np.abs(rl).max())
 
 
-def test_k_scale_does_not_apply(mla):
-    inp = case(61, 128, 576, 64, (100, 513))
+@pytest.mark.parametrize("dt", DTYPES)
+def test_k_scale_does_not_apply(mla, dt):
+    inp = case(61, 128, 576, 64, (100, 513), dt)
     a = run_gpu(mla, inp, 3, 1, k_scale=1.0)
     b = run_gpu(mla, inp, 3, 1, k_scale=7.0)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("dt", DTYPES)
 @pytest.mark.parametrize("mode,splits", [(0, 1), (0, 4), (1, 3)])
-def test_empty_sequences(mla, mode, splits):
-    inp = case(63, 16, 576, 16, (0, 50, 0, 1, 0))
+def test_empty_sequences(mla, mode, splits, dt):
+    inp = case(63, 16, 576, 16, (0, 50, 0, 1, 0), dt)
     o, lse = run_gpu(mla, inp, splits, mode)
     ro, rl = ref(inp)
     assert_close(o, lse, ro, rl, np.asarray(inp.seq_lens) == 0, f"pt empty S={splits}",
                  rounding_slack=True)
 
 
+@pytest.mark.parametrize("dt", DTYPES)
 @pytest.mark.parametrize("mode,splits", [(0, 1), (0, 4), (1, 6)])
-def test_page_permutation_is_bitwise_invariant(mla, mode, splits):
-    inp = case(65, 128, 576, 16, (37, 100, 64, 257), extra_pages=9)
+def test_page_permutation_is_bitwise_invariant(mla, mode, splits, dt):
+    inp = case(65, 128, 576, 16, (37, 100, 64, 257), dt, extra_pages=9)
     o, lse = run_gpu(mla, inp, splits, mode)
     o2, lse2 = run_gpu(mla, W.permute_pages(inp, seed=5), splits, mode)
     assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
 
 
+@pytest.mark.parametrize("dt", DTYPES)
 @pytest.mark.parametrize("mode,splits", [(0, 1), (1, 3)])
 @pytest.mark.parametrize("H,P,D", [(128, 64, 576), (16, 16, 576), (32, 16, 320)])
-def test_poisoned_unreferenced_slots(mla, mode, splits, H, P, D):
-    """Unreferenced rows get NaN codes and a NaN scale; the output must not
-    change by a bit."""
-    inp = case(67, H, D, P, (37, 100, 5), extra_pages=4, table_pad=3)
+def test_poisoned_unreferenced_slots(mla, mode, splits, H, P, D, dt):
+    """Unreferenced rows get 0x7F bytes: NaN codes (fp8) and a NaN scale; the
+    output must not change by a bit."""
+    inp = case(67, H, D, P, (37, 100, 5), dt, extra_pages=4, table_pad=3)
     o, lse = run_gpu(mla, inp, splits, mode)
     o2, lse2 = run_gpu(mla, W.poison_unreferenced(inp), splits, mode)
     assert np.all(np.isfinite(o2)) and np.array_equal(o, o2) and np.array_equal(lse, lse2)
 
 
+@pytest.mark.parametrize("dt", DTYPES)
 @pytest.mark.parametrize("q_len", [2, 5])
-def test_multi_token_decode(mla, q_len):
+def test_multi_token_decode(mla, q_len, dt):
     sl = (1, 3, 40, 300)
-    inp = case(69, 128, 576, 64, sl, q_len=q_len)
+    inp = case(69, 128, 576, 64, sl, dt, q_len=q_len)
     ro, rl = ref(inp)
     o, lse = run_gpu(mla, inp, 4, 1, o_dtype=torch.float32)
     vis = np.array([[oracle.visible_keys(int(n), q_len, i) for i in range(q_len)] for n in sl])
@@ -216,11 +229,12 @@ def test_multi_token_decode(mla, q_len):
     assert_close(o, lse, ro, rl, empty, f"pt mtp q_len={q_len}")
 
 
-def test_full_size_fp8_pt(mla):
-    """The fp8_pt workload (B=64, H=128, D=576, P=64, lengths 1024..8192) at
-    the planner's launch configuration and at per-sequence splits, checked on
-    sampled sequences."""
-    inp = W.generate("fp8_pt")
+@pytest.mark.parametrize("name", ["fp8_pt", "int8_pt"])
+def test_full_size_per_token(mla, name):
+    """The fp8_pt / int8_pt workloads (B=64, H=128, D=576, P=64, lengths
+    1024..8192) at the planner's launch configuration and at per-sequence
+    splits, checked on sampled sequences."""
+    inp = W.generate(name)
     w = inp.workload
     dev_inputs = to_dev(inp)
     sl = np.asarray(inp.seq_lens)
@@ -228,10 +242,10 @@ def test_full_size_fp8_pt(mla):
     picks = sorted({int(np.argmax(sl)), int(np.argmin(sl)), 0, len(sl) - 1} |
                    set(rng.choice(len(sl), size=6, replace=False).tolist()))
     ro, rl = ref(inp, picks)
-    shape = mla.shape_of(dev_inputs[0], dev_inputs[1], dev_inputs[2], kv_dtype="fp8_per_token")
+    shape = mla.shape_of(dev_inputs[0], dev_inputs[1], dev_inputs[2], kv_dtype=w.kv_dtype)
     mode, units, _ = mla.mla_plan(shape, int(sl.max()), int(sl.sum()), 256)
     for mode, splits in [(mode, units)] + [(0, s) for s in w.parity_splits]:
         o, lse = run_gpu(mla, inp, splits, mode, dev_inputs=dev_inputs)
         assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
         assert_close(o[picks], lse[picks], ro, rl, np.zeros(len(picks), bool),
-                     f"fp8_pt mode={mode} S={splits}", rounding_slack=True)
+                     f"{name} mode={mode} S={splits}", rounding_slack=True)

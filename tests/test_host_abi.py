@@ -137,17 +137,20 @@ def test_fp8_query_is_refused():
 
 # ---------------------------------------------------------------- per-token fp8 cache
 
-def test_per_token_cache_is_planned_like_the_others():
-    s, pt = shape(), shape(kv_dtype=mla.MLA_FP8_E4M3_PER_TOKEN)
+@pytest.mark.parametrize("code", [3, 4])
+def test_per_token_cache_is_planned_like_the_others(code):
+    assert code in (mla.MLA_FP8_E4M3_PER_TOKEN, mla.MLA_INT8_PER_TOKEN)
+    s, pt = shape(), shape(kv_dtype=code)
     assert mla.mla_plan(pt, 8192, 64 * 4608, 256) == mla.mla_plan(s, 8192, 64 * 4608, 256)
     assert mla.mla_workspace_size(pt, mla.SPLIT_BALANCED, 64) == \
         mla.mla_workspace_size(s, mla.SPLIT_BALANCED, 64)
     with pytest.raises(NotImplementedError):  # MLA_ERR_DTYPE
-        mla.mla_plan(shape(kv_dtype=4), 1024, 0, 256)
+        mla.mla_plan(shape(kv_dtype=5), 1024, 0, 256)
 
 
-def test_per_token_cache_argument_checks():
-    pt = shape(kv_dtype=mla.MLA_FP8_E4M3_PER_TOKEN)
+@pytest.mark.parametrize("code", [3, 4])
+def test_per_token_cache_argument_checks(code):
+    pt = shape(kv_dtype=code)
     # k_scale is not read for a per-token cache, so 0 passes this check and
     # the call is stopped by the next one (a missing workspace)
     assert _decode_raw(pt, k_scale=0.0, splits=16) == mla.MLA_ERR_WORKSPACE
