@@ -39,6 +39,7 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, public spec
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, public spec
 KERNEL_SRC = os.path.join(ROOT, "mla_paged_latent_decode_amd", "csrc", "mla_kernels.hip")
 COPY_BYTES = 1 << 30
+EVENT_EVERY = 4           # per-kernel events on every 4th timed step (see the timed loop)
 
 
 def kernel_hash():
@@ -171,7 +172,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # the first ~200 steps run up to 10 % slower while the GPU settles into
+    # its steady clocks, so the default warm-up is that long (≈ 30 ms)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--split", default="plan", choices=["plan", "pages", "single"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -254,25 +257,34 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    # Per-kernel HIP events bracket the two launches of every EVENT_EVERY-th
+    # step: each event recorded between two kernels adds a gap of a few
+    # microseconds that a caller's back-to-back launches do not have, so
+    # instrumenting every step would inflate the step time by ~4 %.
+    sampled = [i for i in range(K) if i % EVENT_EVERY == 0]
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(K):
         c = calls[i % 2]
-        evs[i][0].record(stream)
+        e = evs.get(i)
+        if e:
+            e[0].record(stream)
         c("stage1")
-        evs[i][1].record(stream)
+        if e:
+            e[1].record(stream)
         c("stage2")
-        evs[i][2].record(stream)
+        if e:
+            e[2].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / K
-    s1 = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    s2 = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    s1 = np.array([e[0].elapsed_time(e[1]) for e in evs.values()])
+    s2 = np.array([e[1].elapsed_time(e[2]) for e in evs.values()])
 
     if args.copy_calibration:
         a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)

@@ -28,9 +28,11 @@ WorkspaceLayout workspace_layout(int32_t batch, int32_t heads, int32_t d_v, int3
   }
   const int64_t o_bytes = w.slots * heads * (int64_t)d_v * 2;
   const int64_t lse_off = align_up(o_bytes, 256);
-  const int64_t total = lse_off + align_up(w.slots * heads * 8, 256);
+  const int64_t seg_off = lse_off + align_up(w.slots * heads * 8, 256);
+  const int64_t total = seg_off + align_up((int64_t)batch * 8, 256);
   w.o_bytes = (size_t)o_bytes;
   w.lse_offset = (size_t)lse_off;
+  w.seg_offset = (size_t)seg_off;
   w.total = (size_t)total;
   return w;
 }
@@ -207,6 +209,7 @@ static mla_status decode_stages(const mla_shape* shape, int32_t q_len, const voi
   a.lse = lse;
   a.ws_o = wl.total ? workspace : nullptr;
   a.ws_ls = wl.total ? reinterpret_cast<char*>(workspace) + wl.lse_offset : nullptr;
+  a.ws_seg = wl.total ? reinterpret_cast<char*>(workspace) + wl.seg_offset : nullptr;
   a.batch = shape->batch;
   a.heads = shape->num_heads;  // rows: q_len tokens x heads
   a.q_len = q_len;

@@ -13,11 +13,14 @@ constexpr int kTile = 32;  // context positions per stage-1 tile
 //   ws_o  [slots][H][D_v]  fp16, the segment's normalised output o_s stored
 //                          as o_s * 2^-e (e per row, see ws_ls)
 //   ws_ls [slots][H][2]    float32 {lse_s (natural log), 2^e}
-// ws_ls starts at the first 256-byte boundary after ws_o.
+//   ws_seg [B][2]          int32 {first slot, partial count} of each sequence
+//                          (balanced mode; written by stage 1 for stage 2)
+// ws_ls and ws_seg each start at the next 256-byte boundary.
 struct WorkspaceLayout {
   int64_t slots = 0;
   size_t o_bytes = 0;
   size_t lse_offset = 0;
+  size_t seg_offset = 0;
   size_t total = 0;
 };
 
@@ -81,6 +84,7 @@ struct DecodeArgs {
   float* lse;
   void* ws_o;
   void* ws_ls;
+  void* ws_seg;
   int32_t batch;
   int32_t heads;  // rows: q_len query tokens x heads per token
   int32_t q_len;  // query tokens per sequence (1: plain decode)

@@ -261,6 +261,7 @@ struct Stage1Params {
   float* lse;
   _Float16* ws_o;  // partial outputs, fp16, each row scaled by a power of two
   f32x2* ws_ls;    // per partial row: {lse (natural log), that power of two}
+  int32_t* ws_seg; // balanced mode, per sequence: {first slot, partial count or -1}
   int32_t batch, heads, page_size, bt_stride;
   int32_t o_f32, split_mode, num_splits, head_chunks;
   int32_t seg_cost;  // balanced mode: virtual tiles charged per sequence start
@@ -1359,6 +1360,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   int b = 0, ts = 0, te = 0, slot = 0, vis_n = 0;
   bool fin = false;
   int64_t st = 0, a0 = 0, a1 = 0;  // balanced mode: tile cursor and unit range
+  int64_t TC = 0;                   // balanced mode: length of the cost stream
   if (p.split_mode == 0) {
     const int S = p.num_splits;
     b = unit / S;
@@ -1386,7 +1388,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   } else {
     // the unit covers positions [a0, a1) of the batch's cost stream
     const int U = p.num_splits;
-    const int64_t TC = uniform64(total_cost(p.seq_lens, p.batch, p.seg_cost, lane));
+    TC = uniform64(total_cost(p.seq_lens, p.batch, p.seg_cost, lane));
     if (TC == 0) return;
     a0 = (int64_t)unit * TC / U;
     a1 = (int64_t)(unit + 1) * TC / U;
@@ -1420,6 +1422,14 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       fin = lo == 0 && hi == nt;
       slot = unit + b;
       vis_n = n - (p.q_len - 1);
+      if (lo == 0 && hi > 0 && hc == 0 && threadIdx.x == 0) {
+        // this unit owns tile 0 of sequence b: record the slots of its partials for
+        // stage 2 (count 1: the result is final; -1: some unit of the run
+        // owns no tile, and stage 2 works the range out itself)
+        const int ul = unit_of_tile(rs + nt - 1, TC, p.num_splits);
+        p.ws_seg[2 * b] = slot;
+        p.ws_seg[2 * b + 1] = p.num_splits <= TC ? ul - unit + 1 : -1;
+      }
       st += cost_of(n, p.seg_cost);
     }
     if (te > ts) process(b, ts, te, fin, slot, vis_n);
@@ -1435,6 +1445,7 @@ struct Stage2Params {
   const int32_t* seq_lens;
   const _Float16* ws_o;
   const f32x2* ws_ls;
+  const int32_t* ws_seg;
   void* o;
   float* lse;
   int32_t batch, heads, o_f32, split_mode, num_splits, head_groups, kgroups;
@@ -1493,6 +1504,11 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
     if (nseg <= 1) return;  // stage 1 wrote the final result
     first = b * S;
     count = nseg;
+  } else if (n > 0 && p.ws_seg[2 * b + 1] > 0) {
+    // the partial range stage 1 recorded for this sequence
+    count = p.ws_seg[2 * b + 1];
+    if (count == 1) return;  // stage 1 wrote the final result
+    first = p.ws_seg[2 * b];
   } else {
     const int U = p.num_splits;
     // cost before sequence b, and in total
@@ -1644,6 +1660,7 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   sp.lse = a.lse;
   sp.ws_o = reinterpret_cast<_Float16*>(a.ws_o);
   sp.ws_ls = reinterpret_cast<f32x2*>(a.ws_ls);
+  sp.ws_seg = reinterpret_cast<int32_t*>(a.ws_seg);
   sp.batch = a.batch;
   sp.heads = a.heads;
   sp.page_size = a.page_size;
@@ -1695,6 +1712,7 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   s2.seq_lens = a.seq_lens;
   s2.ws_o = reinterpret_cast<const _Float16*>(a.ws_o);
   s2.ws_ls = reinterpret_cast<const f32x2*>(a.ws_ls);
+  s2.ws_seg = reinterpret_cast<const int32_t*>(a.ws_seg);
   s2.o = a.o;
   s2.lse = a.lse;
   s2.batch = a.batch;

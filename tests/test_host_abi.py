@@ -55,13 +55,15 @@ def shape(**kw):
 def test_workspace_sizes():
     s = shape()
     assert mla.mla_workspace_size(s, mla.SPLIT_PER_SEQUENCE, 1) == 0
-    # fp16 partial rows plus an {lse, row scale} float pair per row
+    # fp16 partial rows, an {lse, row scale} float pair per row, then one
+    # {first slot, count} int pair per sequence (rounded up to 256 bytes)
     per = 64 * 16 * 128 * 512 * 2
     got = mla.mla_workspace_size(s, mla.SPLIT_PER_SEQUENCE, 16)
     ls_bytes = 64 * 16 * 128 * 8
-    assert got == per + ls_bytes  # both parts are 256-byte multiples here
+    seg_bytes = 512  # 64 * 8
+    assert got == per + ls_bytes + seg_bytes  # every part a 256-byte multiple here
     bal = mla.mla_workspace_size(s, mla.SPLIT_BALANCED, 256)
-    assert bal == (256 + 64) * 128 * (512 * 2 + 8)
+    assert bal == (256 + 64) * 128 * (512 * 2 + 8) + seg_bytes
     assert mla.mla_workspace_size(s, 7, 4) == 0
     assert mla.mla_workspace_size(s, mla.SPLIT_BALANCED, 0) == 0
     assert mla.mla_workspace_size(shape(head_size=400), mla.SPLIT_BALANCED, 4) == 0
