@@ -339,6 +339,41 @@ def decode_split(q_bits: np.ndarray, kv_bits: np.ndarray, block_table: np.ndarra
     return np.stack(outs), np.stack(lses)
 
 
+# ---------------------------------------------------------------- cross-shard merge
+
+def merge_shards(o_parts: np.ndarray, lse_parts: np.ndarray, lse_base: str = "ln"
+                 ) -> Tuple[np.ndarray, np.ndarray]:
+    """Merge of the results of G context shards (decode context parallelism:
+    Triton MLA page, design motivation, and AttentionBackend page, limits:
+    shards are combined through their LSE, which must be read in the base it
+    was written in).  o_parts [G, ..., D_v] holds each shard's normalised
+    output over its own keys and lse_parts [G, ...] its log-sum-exp, in
+    natural log (``lse_base="ln"``) or base 2 (``"log2"``).  Per row:
+    lse = ln sum_g e^lse_g and o = sum_g e^(lse_g - lse) o_g; a shard with
+    lse_g = -inf (no keys) has weight 0, and a row no shard saw gets o = 0,
+    lse = -inf.  Returns (o, lse) with lse in natural log."""
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse = np.asarray(lse_parts, dtype=np.float64)
+    if lse_base == "log2":
+        lse = lse * math.log(2.0)
+    elif lse_base != "ln":
+        raise ValueError(f"unknown lse base {lse_base!r}")
+    G = lse.shape[0]
+    out_o = np.zeros(o_parts.shape[1:])
+    out_l = np.full(lse.shape[1:], -np.inf)
+    for idx in np.ndindex(*lse.shape[1:]):
+        ls = [lse[(g,) + idx] for g in range(G)]
+        live = [g for g in range(G) if ls[g] != -np.inf]
+        if not live:
+            continue
+        M = max(ls[g] for g in live)
+        w = {g: math.exp(ls[g] - M) for g in live}
+        tot = math.fsum(w.values())
+        out_o[idx] = sum(w[g] * o_parts[(g,) + idx] for g in live) / tot
+        out_l[idx] = M + math.log(tot)
+    return out_o, out_l
+
+
 # ---------------------------------------------------------------- split count rule
 
 def pages_split_count(max_seq_len: int, num_sms: int) -> int:
@@ -353,5 +388,5 @@ __all__ = [
     "physical_slot", "gather_rows", "attend", "decode", "segment_bounds", "merge_partials",
     "merge_normalised", "segment_partial", "decode_split", "pages_split_count",
     "visible_keys", "decode_mtp", "decode_sparse", "row_width", "PER_TOKEN_PAD",
-    "PER_TOKEN_DTYPES", "int8_bits_to_f64",
+    "PER_TOKEN_DTYPES", "int8_bits_to_f64", "merge_shards",
 ]

@@ -777,3 +777,68 @@ def test_planted_int8_mistakes_are_caught(monkeypatch):
         with pytest.raises(AssertionError):
             test_int8_cache_matches_torch_sdpa(576)
         monkeypatch.undo()
+
+
+# ---------------------------------------------------------------- cross-shard (DCP) merge
+# (Triton MLA page, design motivation: decode always returns lse because the
+# shards of a context-parallel decode are merged through it; AttentionBackend
+# page, limits: reading an lse in the wrong base corrupts that merge)
+
+def shard_results(inp, G):
+    """Oracle decode of each round-robin page shard of the batch."""
+    outs = [run(W.shard_pages(inp, G, r)) for r in range(G)]
+    return np.stack([o for o, _ in outs]), np.stack([l for _, l in outs])
+
+
+@pytest.mark.parametrize("G", [2, 3, 4, 8])
+def test_shard_merge_equals_unsharded_decode(G):
+    """Every key lies in exactly one shard, so merging the shards' (o, lse)
+    must give the single-pass decode of the whole batch (to rounding)."""
+    inp = small(seed=81, seq_lens=(1, 15, 16, 17, 100, 257), P=16)
+    o_p, l_p = shard_results(inp, G)
+    o, lse = O.merge_shards(o_p, l_p)
+    ro, rl = run(inp)
+    assert np.abs(o - ro).max() < 1e-12 and np.abs(lse - rl).max() < 1e-12
+
+
+def test_shard_pages_cover_every_position_once():
+    inp = small(seed=82, seq_lens=(1, 16, 33, 100), P=16)
+    for G in (2, 3, 5):
+        seen = {b: [] for b in range(4)}
+        for r in range(G):
+            sh = W.shard_pages(inp, G, r)
+            for b in range(4):
+                n = int(sh.seq_lens[b])
+                pos_pages = [int(sh.block_table[b, t // 16]) * 16 + t % 16 for t in range(n)]
+                seen[b] += pos_pages
+        for b in range(4):
+            n = int(inp.seq_lens[b])
+            full = [int(inp.block_table[b, t // 16]) * 16 + t % 16 for t in range(n)]
+            assert sorted(seen[b]) == sorted(full)
+
+
+def test_shard_merge_log2_base_and_empty_shards():
+    """A sequence shorter than a page lives in shard 0 only: the other shards
+    carry lse = -inf and must get weight 0.  The same lse given in base 2
+    merges to the same result when declared as such, and to a wrong one when
+    declared as natural log."""
+    inp = small(seed=83, seq_lens=(5, 40, 16), P=16)
+    o_p, l_p = shard_results(inp, 4)
+    assert np.all(np.isneginf(l_p[1:, 0]))  # sequence 0: one page, shard 0 only
+    ro, rl = run(inp)
+    o, lse = O.merge_shards(o_p, l_p / math.log(2.0), lse_base="log2")
+    assert np.abs(o - ro).max() < 1e-12 and np.abs(lse - rl).max() < 1e-12
+    o_bad, _ = O.merge_shards(o_p, l_p / math.log(2.0), lse_base="ln")
+    assert np.abs(o_bad - ro).max() > 1e-3
+    # no shard saw anything: o = 0, lse = -inf
+    o0, l0 = O.merge_shards(np.ones((3, 2, 4)), np.full((3, 2), -np.inf))
+    assert np.all(o0 == 0) and np.all(np.isneginf(l0))
+
+
+def test_shard_merge_closed_form():
+    """Two shards with lse a and b: weights e^a / (e^a + e^b) exactly."""
+    o_p = np.array([[[1.0, 0.0]], [[0.0, 1.0]]])
+    l_p = np.array([[math.log(3.0)], [math.log(1.0)]])
+    o, lse = O.merge_shards(o_p, l_p)
+    assert np.allclose(o[0], [0.75, 0.25], atol=1e-15, rtol=0)
+    assert abs(lse[0] - math.log(4.0)) < 1e-15

@@ -318,6 +318,28 @@ def permute_pages(inp: DecodeInputs, seed: int) -> DecodeInputs:
     return dataclasses.replace(inp, kv_bits=kv, block_table=table.astype(np.int32))
 
 
+def shard_pages(inp: DecodeInputs, shards: int, rank: int) -> DecodeInputs:
+    """The same pool as seen by one of ``shards`` context shards: rank r owns
+    every sequence's logical pages j with j % shards == r (round robin).  Its
+    block table lists those pages in order and its sequence length counts
+    their positions (a sequence's last, possibly partial, page stays last).
+    The pool itself is shared, so no value moves."""
+    P = inp.workload.page_size
+    B = len(inp.seq_lens)
+    tables, lens = [], []
+    for b in range(B):
+        n = int(inp.seq_lens[b])
+        pages = (n + P - 1) // P
+        mine = list(range(rank, pages, shards))
+        tables.append([int(inp.block_table[b, j]) for j in mine])
+        lens.append(sum(min(P, n - j * P) for j in mine))
+    width = max(1, max(len(t) for t in tables))
+    table = np.zeros((B, width), dtype=np.int32)
+    for b, t in enumerate(tables):
+        table[b, :len(t)] = t
+    return dataclasses.replace(inp, block_table=table, seq_lens=np.asarray(lens, dtype=np.int32))
+
+
 def subset(inp: DecodeInputs, batches: Sequence[int]) -> DecodeInputs:
     """The same pool with only the chosen sequences, in the given order."""
     idx = np.asarray(batches, dtype=np.int64)
@@ -339,4 +361,5 @@ __all__ = [
     "BF16", "FP8_E4M3", "DSV3_SCALE", "Workload", "WORKLOADS", "DecodeInputs", "generate",
     "small_case", "f32_to_bf16_bits", "f32_to_e4m3fn_bits", "make_block_table",
     "referenced_slots", "poison_unreferenced", "permute_pages", "subset", "expected_tokens",
+    "shard_pages",
 ]
