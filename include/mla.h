@@ -303,6 +303,36 @@ mla_status mla_decode_sparse_stage2(const mla_shape* shape, int32_t topk, const 
                                     float* lse, void* workspace, size_t workspace_bytes,
                                     void* hip_stream);
 
+/* Merge the results of a context-parallel decode ("Triton と MLA" page,
+ * 設計動機: decode always returns lse because the context shards are merged
+ * through it; "AttentionBackend" page, Limites et échecs: an lse taken in the
+ * wrong base silently corrupts the merge, so the base is stated here).
+ *
+ * Each of num_shards shards has decoded the same rows (a row = one sequence
+ * and query head, or one query token and head) over its own share of the
+ * keys, e.g. the pages j % num_shards == shard of every sequence, each with
+ * this library.  Per row:
+ *   lse = ln sum_g e^lse_g,   o = sum_g e^(lse_g - lse) o_g;
+ * a shard with lse_g = -inf (it held no key of the row) has weight 0 whatever
+ * its o_g holds; a row with no live shard gets o = 0 and lse = -inf.
+ *   o_parts    device, [num_shards][rows][d_v], parts_dtype MLA_BF16 or
+ *              MLA_FP32, 16-byte aligned
+ *   lse_parts  device, [num_shards][rows] float32, natural log
+ *              (lse_base MLA_LSE_LN) or base 2 (MLA_LSE_LOG2)
+ *   o          device, [rows][d_v], o_dtype MLA_BF16 or MLA_FP32, 16-byte
+ *              aligned; lse device [rows] float32, natural log
+ *   d_v        512 or 256 (kv_lora_rank); rows >= 1; 1 <= num_shards <=
+ *              MLA_MAX_SHARDS
+ * Buffers are caller-owned and may not overlap the outputs; one kernel is
+ * enqueued on hip_stream; nothing is allocated.  Errors (nothing enqueued):
+ * MLA_ERR_NULL, MLA_ERR_ARGUMENT (shard count, base or alignment),
+ * MLA_ERR_SHAPE (rows), MLA_ERR_HEAD_SIZE (d_v), MLA_ERR_DTYPE. */
+typedef enum mla_lse_base { MLA_LSE_LN = 0, MLA_LSE_LOG2 = 1 } mla_lse_base;
+#define MLA_MAX_SHARDS 65536
+mla_status mla_merge_shards(int32_t num_shards, int64_t rows, int32_t d_v, const void* o_parts,
+                            int32_t parts_dtype, const float* lse_parts, int32_t lse_base,
+                            void* o, int32_t o_dtype, float* lse, void* hip_stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char* mla_status_string(int32_t status);
 

@@ -30,7 +30,7 @@ __all__ = [
     "MlaError", "mla_decode", "mla_decode_sparse", "mla_plan", "mla_workspace_size", "mla_pages_split_count",
     "mla_status_string", "SPLIT_PER_SEQUENCE", "SPLIT_BALANCED", "library_path", "load_library",
     "MLA_BF16", "MLA_FP8_E4M3", "MLA_FP32", "MLA_FP8_E4M3_PER_TOKEN", "MLA_INT8_PER_TOKEN",
-    "MLA_PER_TOKEN_PAD",
+    "MLA_PER_TOKEN_PAD", "mla_merge_shards", "MLA_LSE_LN", "MLA_LSE_LOG2",
 ]
 
 MLA_OK, MLA_ERR_NULL, MLA_ERR_HEAD_SIZE, MLA_ERR_PAGE_SIZE, MLA_ERR_DTYPE = 0, 1, 2, 3, 4
@@ -38,6 +38,8 @@ MLA_ERR_SHAPE, MLA_ERR_SPLITS, MLA_ERR_WORKSPACE, MLA_ERR_LAUNCH, MLA_ERR_ARGUME
 MLA_BF16, MLA_FP8_E4M3, MLA_FP32, MLA_FP8_E4M3_PER_TOKEN, MLA_INT8_PER_TOKEN = 0, 1, 2, 3, 4
 MLA_PER_TOKEN_PAD = 16  # bytes after the codes of a per-token cache row (fp32 scale first)
 SPLIT_PER_SEQUENCE, SPLIT_BALANCED = 0, 1
+MLA_LSE_LN, MLA_LSE_LOG2 = 0, 1
+MLA_MAX_SHARDS = 65536
 MLA_MAX_KV_SPLITS = 65536
 MLA_MAX_Q_LEN = 16
 
@@ -94,6 +96,8 @@ def load_library():
             fn.argtypes = [shp, i32, vp, vp, vp, vp, vp, ctypes.c_float, i32, ctypes.c_float,
                            i32, i32, vp, vp, vp, sz, vp]
             fn.restype = i32
+        lib.mla_merge_shards.argtypes = [i32, i64, i32, vp, i32, vp, i32, vp, i32, vp, vp]
+        lib.mla_merge_shards.restype = i32
         lib.mla_status_string.argtypes = [i32]
         lib.mla_status_string.restype = ctypes.c_char_p
         _LIB = lib
@@ -310,6 +314,48 @@ def mla_decode_sparse(q, kv_cache, block_table, topk_indices, topk_lens, scale: 
             workspace.numel() * workspace.element_size() if workspace is not None else 0, stream)
     if st != MLA_OK:
         _raise(st, "mla_decode_sparse")
+    return o, lse
+
+
+def mla_merge_shards(o_parts, lse_parts, lse_base: str = "ln", o=None, lse=None, *,
+                     o_dtype=None, stream=None):
+    """Merge G context shards' decode results through their LSE (the C ABI's
+    mla_merge_shards).  o_parts [G, ..., D_v] (bf16 or fp32) and lse_parts
+    [G, ...] float32 are device tensors; lse_base is "ln" or "log2".
+    Returns (o [..., D_v], lse [...]) with lse in natural log."""
+    torch = _torch()
+    lib = load_library()
+    if not (o_parts.is_cuda and lse_parts.is_cuda):
+        raise ValueError("mla_merge_shards needs device tensors (HIP)")
+    if o_parts.dim() < 2 or tuple(lse_parts.shape) != tuple(o_parts.shape[:-1]):
+        raise ValueError("o_parts must be [G, ..., D_v] and lse_parts [G, ...]")
+    if not (o_parts.is_contiguous() and lse_parts.is_contiguous()):
+        raise ValueError("o_parts and lse_parts must be contiguous")
+    if lse_parts.dtype != torch.float32:
+        raise ValueError("lse_parts must be float32")
+    G, d_v = o_parts.shape[0], o_parts.shape[-1]
+    rows_shape = tuple(o_parts.shape[1:-1])
+    rows = 1
+    for r in rows_shape:
+        rows *= int(r)
+    if o is None:
+        o = torch.empty(rows_shape + (d_v,), dtype=o_dtype or torch.bfloat16,
+                        device=o_parts.device)
+    if lse is None:
+        lse = torch.empty(rows_shape, dtype=torch.float32, device=o_parts.device)
+    if (tuple(o.shape) != rows_shape + (d_v,) or tuple(lse.shape) != rows_shape
+            or not o.is_contiguous() or not lse.is_contiguous() or lse.dtype != torch.float32):
+        raise ValueError("o must be [..., D_v] and lse [...] float32, contiguous")
+    base = {"ln": MLA_LSE_LN, "log2": MLA_LSE_LOG2}[lse_base]
+    if stream is None:
+        stream = torch.cuda.current_stream(o_parts.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    st = lib.mla_merge_shards(int(G), int(rows), int(d_v), o_parts.data_ptr(),
+                              _dtype_code(o_parts.dtype), lse_parts.data_ptr(), base,
+                              o.data_ptr(), _dtype_code(o.dtype), lse.data_ptr(), stream)
+    if st != MLA_OK:
+        _raise(st, "mla_merge_shards")
     return o, lse
 
 

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libmla.so")
-SOURCES = [os.path.join(CSRC, "mla_api.cpp"), os.path.join(CSRC, "mla_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "mla_api.cpp"), os.path.join(CSRC, "mla_kernels.hip"),
+           os.path.join(CSRC, "mla_merge.hip")]
 ARCH = "gfx950"
 
 

@@ -329,6 +329,33 @@ MLA_SPARSE_ENTRY(mla_decode_sparse_stage1, kStage1)
 MLA_SPARSE_ENTRY(mla_decode_sparse_stage2, kStage2)
 #undef MLA_SPARSE_ENTRY
 
+mla_status mla_merge_shards(int32_t num_shards, int64_t rows, int32_t d_v, const void* o_parts,
+                            int32_t parts_dtype, const float* lse_parts, int32_t lse_base,
+                            void* o, int32_t o_dtype, float* lse, void* hip_stream) {
+  if (!o_parts || !lse_parts || !o || !lse) return MLA_ERR_NULL;
+  if (num_shards < 1 || num_shards > MLA_MAX_SHARDS) return MLA_ERR_ARGUMENT;
+  if (rows < 1 || rows > ((int64_t)1 << 33)) return MLA_ERR_SHAPE;
+  if (d_v != 512 && d_v != 256) return MLA_ERR_HEAD_SIZE;
+  if ((parts_dtype != MLA_BF16 && parts_dtype != MLA_FP32) ||
+      (o_dtype != MLA_BF16 && o_dtype != MLA_FP32))
+    return MLA_ERR_DTYPE;
+  if (lse_base != MLA_LSE_LN && lse_base != MLA_LSE_LOG2) return MLA_ERR_ARGUMENT;
+  if (!aligned(o_parts, 16) || !aligned(o, 16) || !aligned(lse_parts, 4) || !aligned(lse, 4))
+    return MLA_ERR_ARGUMENT;
+  MergeArgs a;
+  a.o_parts = o_parts;
+  a.lse_parts = lse_parts;
+  a.o = o;
+  a.lse = lse;
+  a.rows = rows;
+  a.shards = num_shards;
+  a.d_v = d_v;
+  a.parts_f32 = parts_dtype == MLA_FP32 ? 1 : 0;
+  a.o_f32 = o_dtype == MLA_FP32 ? 1 : 0;
+  a.lse_log2 = lse_base == MLA_LSE_LOG2 ? 1 : 0;
+  return launch_merge_shards(a, hip_stream) == 0 ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
 const char* mla_status_string(int32_t status) {
   switch (status) {
     case MLA_OK: return "MLA_OK";

@@ -112,4 +112,17 @@ enum Stages { kStage1 = 1, kStage2 = 2, kBothStages = 3 };
 // a merge).  Returns 0 or a HIP error code.
 int launch_decode(const DecodeArgs& a, void* stream, int stages);
 
+// Cross-shard merge (mla_merge.hip).
+struct MergeArgs {
+  const void* o_parts;     // [shards][rows][d_v]
+  const float* lse_parts;  // [shards][rows]
+  void* o;                 // [rows][d_v]
+  float* lse;              // [rows]
+  int64_t rows;
+  int32_t shards, d_v;
+  int32_t parts_f32, o_f32, lse_log2;
+};
+
+int launch_merge_shards(const MergeArgs& a, void* stream);
+
 }  // namespace mla

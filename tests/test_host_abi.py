@@ -177,3 +177,24 @@ def test_shape_of_checks_cache_row_width():
         mla.shape_of(q, torch.zeros(8, 16, 576, dtype=torch.uint8), bt, kv_dtype="fp8_per_token")
     with pytest.raises(ValueError):
         mla.shape_of(q, torch.zeros(8, 16, 576, dtype=torch.bfloat16), bt, kv_dtype="fp8_e4m3")
+
+
+# ---------------------------------------------------------------- cross-shard merge
+
+def _merge_raw(G=2, rows=4, d_v=512, op=256, pd=mla.MLA_BF16, lp=256, base=0, o=256,
+               od=mla.MLA_BF16, lse=256):
+    return mla.load_library().mla_merge_shards(G, rows, d_v, op, pd, lp, base, o, od, lse, None)
+
+
+def test_merge_argument_checks_fail_before_launch():
+    assert _merge_raw(op=None) == mla.MLA_ERR_NULL
+    assert _merge_raw(lse=None) == mla.MLA_ERR_NULL
+    assert _merge_raw(G=0) == mla.MLA_ERR_ARGUMENT
+    assert _merge_raw(G=mla.MLA_MAX_SHARDS + 1) == mla.MLA_ERR_ARGUMENT
+    assert _merge_raw(rows=0) == mla.MLA_ERR_SHAPE
+    assert _merge_raw(d_v=320) == mla.MLA_ERR_HEAD_SIZE
+    assert _merge_raw(pd=mla.MLA_FP8_E4M3) == mla.MLA_ERR_DTYPE
+    assert _merge_raw(od=mla.MLA_FP8_E4M3) == mla.MLA_ERR_DTYPE
+    assert _merge_raw(base=2) == mla.MLA_ERR_ARGUMENT
+    assert _merge_raw(op=264) == mla.MLA_ERR_ARGUMENT  # misaligned
+    assert _merge_raw(lse=258) == mla.MLA_ERR_ARGUMENT
