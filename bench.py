@@ -168,6 +168,99 @@ def ingest_pmc(fetch_csv, write_csv, workload):
     print(json.dumps(out))
 
 
+def run_dcp(args, G):
+    """Context-parallel decode on one GPU: the workload's batch is cut into G
+    round-robin page shards, each decoded by the library (untimed, bf16 o and
+    fp32 lse, as a serving stack would exchange them), and the timed step is
+    the merge of the G shard results into the final (o, lse).  On G GPUs each
+    would decode its own shard; the merge is the one step the context split
+    adds (after the exchange of the shard results, which one GPU cannot show)."""
+    import numpy as np
+    import torch
+
+    import mla_paged_latent_decode_amd as mla
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    inp = W.generate(args.workload)
+    w = inp.workload
+    if w.kv_dtype != "bf16" or w.q_len != 1 or w.topk:
+        print("--dcp runs on the bf16 single-token workloads", file=sys.stderr)
+        return 2
+    q = torch.from_numpy(inp.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    kv = torch.from_numpy(inp.kv_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    o_parts, l_parts = [], []
+    for r in range(G):
+        sh = W.shard_pages(inp, G, r)
+        bt = torch.from_numpy(sh.block_table).to(dev)
+        sl = torch.from_numpy(sh.seq_lens).to(dev)
+        o, lse = mla.mla_decode(q, kv, bt, sl, w.scale, w.page_size, w.k_scale, num_cus=cus)
+        o_parts.append(o)
+        l_parts.append(lse)
+    o_p = torch.stack(o_parts).contiguous()
+    l_p = torch.stack(l_parts).contiguous()
+    del kv
+    o = torch.empty((w.batch, w.num_heads, w.kv_lora_rank), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, w.num_heads), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        mla.mla_merge_shards(o_p, l_p, "ln", o, lse, stream=stream)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        evs[i][0].record(stream)
+        mla.mla_merge_shards(o_p, l_p, "ln", o, lse, stream=stream)
+        evs[i][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / K
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    rows = w.batch * w.num_heads
+    # every shard row (bf16) and lse read once, the merged row and lse written once
+    nbytes = G * rows * (w.kv_lora_rank * 2 + 4) + rows * (w.kv_lora_rank * 2 + 4)
+    ach = nbytes / (launch_ms * 1e-3) / 1e9
+    out = {
+        "metric": "MLA context-parallel shard merge GB/s (% of HBM peak)",
+        "value": round(nbytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} merge of {G} round-robin page shards: {w.description}",
+                   "batch": w.batch, "heads": w.num_heads, "kv_lora_rank": w.kv_lora_rank,
+                   "shards": G, "seed": w.seed},
+        "wall_s": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "mla_merge_shards_kernel", "avg_launch_ms": round(launch_ms, 5)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        op = o_p.float().cpu().numpy().astype(np.float64)
+        lp = l_p.cpu().numpy().astype(np.float64)
+        done = 0
+        t1 = time.perf_counter()
+        for b in range(w.batch):
+            oracle.merge_shards(op[:, b], lp[:, b])
+            done += 1
+            if time.perf_counter() - t1 > 20.0:
+                break
+        dt = time.perf_counter() - t1
+        out["cpu_baseline"] = {
+            "value": round(done * w.num_heads * (G + 1) * (w.kv_lora_rank * 2 + 4) / dt / 1e9, 4),
+            "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {w.batch} sequences' rows merged by oracle.merge_shards "
+                      f"(python loop per row, float64), {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +273,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--dcp", type=int, default=0, metavar="G",
+                    help="time the cross-shard merge of G round-robin page shards of the "
+                         "workload instead of the decode (the shards are decoded untimed)")
     args = ap.parse_args()
 
     if args.ingest_pmc:
@@ -200,6 +296,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.dcp:
+        return run_dcp(args, args.dcp)
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
     inp = W.generate(args.workload)
