@@ -303,9 +303,7 @@ static mla_status check_sparse(const mla_shape* shape, int32_t topk, const int32
   if (st != MLA_OK) return st;
   if (!topk_indices || !topk_lens) return MLA_ERR_NULL;
   if (topk < 1) return MLA_ERR_ARGUMENT;
-  if (shape->head_size != 576) return MLA_ERR_HEAD_SIZE;
   if (shape->kv_dtype != MLA_BF16) return MLA_ERR_DTYPE;
-  if (shape->num_heads % 128 != 0) return MLA_ERR_SHAPE;
   const uint64_t pool = (uint64_t)shape->num_blocks * shape->page_size * shape->head_size * 2;
   if (pool + 65536 >= ((uint64_t)1 << 32)) return MLA_ERR_SHAPE;
   if (!aligned(topk_indices, 4)) return MLA_ERR_ARGUMENT;

@@ -397,8 +397,7 @@ __device__ __forceinline__ int tile_slot(int t16, int c4) {
 template <int HPW, int W, int D, int DV, int NBUF, bool F8, bool SP, int PT>
 __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   using C = Cfg<HPW, W, D, DV, NBUF, F8, PT>;
-  static_assert(!SP || (!F8 && NBUF == 3),
-                "the index-driven gather is built for the bf16 loop with a ring of 3");
+  static_assert(!SP || !F8, "the index-driven gather reads bf16 cache rows");
   // [bf16 ring: NBUF tiles][fp8 staging: 2 tiles][Q k-steps of each wave]
   // [per-token scales: 2 staging slots of 2 x 256 B, NBUF ring slots of 128 B]
   __shared__ __attribute__((aligned(1024)))
@@ -1622,18 +1621,18 @@ int launch_stage1(const Stage1Params& sp, int grid, hipStream_t st) {
   return (int)hipGetLastError();
 }
 
-template <int D, int DV, bool F8, int PT = 0>
+template <int D, int DV, bool F8, int PT = 0, bool SP = false>
 int launch_stage1_for(const HeadTiling& ht, const Stage1Params& sp, int grid, hipStream_t st) {
   if (ht.heads_per_wave == 32) {
     switch (ht.waves) {
-      case 4: return launch_stage1<32, 4, D, DV, F8, false, PT>(sp, grid, st);
-      case 2: return launch_stage1<32, 2, D, DV, F8, false, PT>(sp, grid, st);
-      default: return launch_stage1<32, 1, D, DV, F8, false, PT>(sp, grid, st);
+      case 4: return launch_stage1<32, 4, D, DV, F8, SP, PT>(sp, grid, st);
+      case 2: return launch_stage1<32, 2, D, DV, F8, SP, PT>(sp, grid, st);
+      default: return launch_stage1<32, 1, D, DV, F8, SP, PT>(sp, grid, st);
     }
   }
   // 16-head waves only arise for an odd number of 16-head groups (H % 32 != 0),
   // which always gives one wave per workgroup
-  return launch_stage1<16, 1, D, DV, F8, false, PT>(sp, grid, st);
+  return launch_stage1<16, 1, D, DV, F8, SP, PT>(sp, grid, st);
 }
 
 }  // namespace
@@ -1689,9 +1688,10 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   if (stages & kStage1) {
     int err;
     if (a.topk_idx) {
-      // the host admits the sparse gather only for this configuration
-      if (a.kv_fp8 || a.head_size != 576 || ht.heads_per_wave != 32 || ht.waves != 4) return -1;
-      err = launch_stage1<32, 4, 576, 512, false, true>(sp, grid1, st);
+      // the host admits the sparse gather for bf16 caches only
+      if (a.kv_fp8) return -1;
+      err = a.head_size == 576 ? launch_stage1_for<576, 512, false, 0, true>(ht, sp, grid1, st)
+                               : launch_stage1_for<320, 256, false, 0, true>(ht, sp, grid1, st);
     } else if (a.kv_pt == 1)
       err = a.head_size == 576 ? launch_stage1_for<576, 512, true, 1>(ht, sp, grid1, st)
                                : launch_stage1_for<320, 256, true, 1>(ht, sp, grid1, st);

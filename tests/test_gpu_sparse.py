@@ -70,28 +70,36 @@ def check(o, lse, ro, rl, lens, label):
 
 
 SPARSE_CASES = [
-    # (H, P, seq_lens, topk)
-    (128, 64, (300, 2000, 40, 1031), 256),
-    (128, 16, (1, 33, 64, 100), 48),
-    (256, 64, (700, 129), 100),
+    # (H, D, P, seq_lens, topk): every head tiling (16-head waves, 1/2/4 waves
+    # of 32 heads, several head chunks) and both head sizes
+    (128, 576, 64, (300, 2000, 40, 1031), 256),
+    (128, 576, 16, (1, 33, 64, 100), 48),
+    (256, 576, 64, (700, 129), 100),
+    (16, 576, 16, (1, 33, 64, 100), 48),
+    (32, 576, 32, (500, 97), 80),
+    (48, 576, 16, (3, 129, 40), 40),
+    (64, 576, 64, (300, 2000), 200),
+    (16, 320, 16, (1, 31, 33, 250, 513), 64),
+    (128, 320, 32, (17, 95, 333), 72),
 ]
 
 
 @pytest.mark.parametrize("case", range(len(SPARSE_CASES)))
 @pytest.mark.parametrize("mode,splits", [(0, 1), (0, 3), (1, 1), (1, 5), (1, 37)])
 def test_sparse_cases(mla, case, mode, splits):
-    H, P, sl, k = SPARSE_CASES[case]
-    inp = W.small_case(seed=400 + case, batch=len(sl), num_heads=H, head_size=576,
-                       kv_lora_rank=512, page_size=P, seq_lens=sl, topk=k)
+    H, D, P, sl, k = SPARSE_CASES[case]
+    inp = W.small_case(seed=400 + case, batch=len(sl), num_heads=H, head_size=D,
+                       kv_lora_rank=D - 64, page_size=P, seq_lens=sl, topk=k)
     ro, rl = ref(inp)
     o, lse = run_sparse(mla, inp, splits, mode, o_dtype=torch.float32)
     check(o, lse, ro, rl, inp.topk_lens, f"sparse case{case} mode={mode} S={splits}")
 
 
+@pytest.mark.parametrize("H,D", [(128, 576), (16, 576), (64, 576), (128, 320), (16, 320)])
 @pytest.mark.parametrize("mode,splits", [(0, 1), (0, 4), (1, 7)])
-def test_sparse_over_every_position_is_dense_decode_bitwise(mla, mode, splits):
+def test_sparse_over_every_position_is_dense_decode_bitwise(mla, mode, splits, H, D):
     sl = (37, 100, 1, 700)
-    inp = W.small_case(seed=410, batch=len(sl), num_heads=128, head_size=576, kv_lora_rank=512,
+    inp = W.small_case(seed=410, batch=len(sl), num_heads=H, head_size=D, kv_lora_rank=D - 64,
                        page_size=64, seq_lens=sl)
     idx = np.zeros((len(sl), 704), np.int32)
     for b, n in enumerate(sl):
@@ -129,15 +137,16 @@ def test_sparse_ignores_unlisted_slots(mla, mode, splits):
     assert np.array_equal(a[0], b_[0]) and np.array_equal(a[1], b_[1])
 
 
-def test_sparse_rejects_configurations_it_is_not_built_for(mla):
+def test_sparse_rejects_quantised_caches(mla):
     inp = W.small_case(seed=412, batch=1, num_heads=16, head_size=576, kv_lora_rank=512,
-                       page_size=16, seq_lens=(40,), topk=8)
-    with pytest.raises(mla.MlaError):  # 16 heads: not a multiple of 128
-        run_sparse(mla, inp, 1, 0)
-    inp = W.small_case(seed=413, batch=1, num_heads=128, head_size=320, kv_lora_rank=256,
-                       page_size=16, seq_lens=(40,), topk=8)
-    with pytest.raises(ValueError):  # head size 320
-        run_sparse(mla, inp, 1, 0)
+                       page_size=16, seq_lens=(40,), topk=8, kv_dtype=W.FP8_E4M3, k_scale=0.05)
+    w = inp.workload
+    q = dev(inp.q_bits.view(np.int16)).view(torch.bfloat16)
+    kv = dev(inp.kv_bits).view(torch.float8_e4m3fn)
+    with pytest.raises(NotImplementedError):  # MLA_ERR_DTYPE: the gather reads bf16 rows
+        mla.mla_decode_sparse(q, kv, dev(inp.block_table), dev(inp.topk_indices),
+                              dev(inp.topk_lens), w.scale, w.page_size, w.k_scale, 1,
+                              split_mode=0)
 
 
 def test_sparse_full_size(mla):
