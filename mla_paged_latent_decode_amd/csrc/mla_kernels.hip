@@ -17,6 +17,13 @@
 //   XOR swizzle, so that both the QK^T read (ds_read_b128) and the
 //   transposed V read (ds_read_b64_tr_b16) hit distinct banks.
 //
+//   Variants of the same kernel: 1-byte caches (e4m3fn with a per-tensor
+//   scale, or e4m3fn / int8 codes with a per-token inline scale, "Triton と
+//   MLA" page, 主要ファイル) are staged in LDS and widened to bf16 there;
+//   multi-token decode gives each query-token row its own causal limit
+//   (article above, section 十); sparse decode takes its rows from a list of
+//   logical positions (section 十三) through an index-driven gather.
+//
 // Stage 2 (merge).  Partials (o_s, lse_s) of a sequence are combined with the
 //   log-sum-exp rule of the same article, section 十二:
 //   lse = M + ln sum_s e^(lse_s - M),  o = sum_s e^(lse_s - lse) o_s.
@@ -277,8 +284,8 @@ struct Stage1Params {
   const int32_t* topk_idx;
   int32_t topk_stride, page_shift;
   uint32_t pool_bytes;
-  float score_log2;  // scale * log2(e) (* k_scale for fp8 caches)
-  float out_scale;   // 1, or k_scale for fp8 caches
+  float score_log2;  // scale * log2(e) (* k_scale for per-tensor fp8 caches)
+  float out_scale;   // 1, or k_scale for per-tensor fp8 caches
 };
 
 // ---------------------------------------------------------------- work units
@@ -373,7 +380,7 @@ struct Cfg {
   // second score buffer and can spread a tile's loads over two iterations.
   static constexpr bool PIPE = HPW == 32 && !PT && (F8 ? W == 4 : NBUF >= 4);
   static_assert(NBUF == stage1_ring_depth(HPW, W, D, F8, PT), "ring depth");
-  static_assert(!PT || F8, "per-token rows hold fp8 codes");
+  static_assert(!PT || F8, "per-token rows hold 1-byte codes (e4m3fn or int8)");
   static_assert(NBLK * 1024 == kTile * D * 2, "tile bytes");
   static_assert(NBLK % W == 0, "each wave loads or widens the same number of blocks");
   static_assert(!F8 || ((16 * D) % (64 * G) == 0 && (2 * NIH) % W == 0), "fp8 copy split");
@@ -1004,12 +1011,12 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       TileLoad tl;
       if (more) tl = prepare(F8 ? i + 2 : i + NBUF - 1);
       // Load k goes after step floor(k * TOT / NIW) of the tile's TOT MFMA
-      // steps (32-head waves: the QK^T and the PV steps; the loaded tile is
-      // not read before iteration i+NBUF-1, so the loads may be spread over
-      // the whole iteration and leave the memory pipeline at about the rate
-      // it drains instead of blocking the wave in a burst).
-      // fp8: the staged tile is waited for at the top of the next iteration,
-      // so its loads go out over the QK^T steps only and land during PV.
+      // steps.  bf16, 32-head waves: the QK^T and the PV steps (the loaded
+      // tile is not read before iteration i+NBUF-1, so the loads may be
+      // spread over the whole iteration and leave the memory pipeline at
+      // about the rate it drains instead of blocking the wave in a burst).
+      // fp8 and 16-head waves: the QK^T steps only (an fp8 staging tile is
+      // waited for at the top of the next iteration, so it lands during PV).
       constexpr int TOT_STEPS = (HPW == 32 && !F8) ? C::NKS + 2 * C::NVB : C::NKS;
       auto dma_at = [&](int step) __attribute__((always_inline)) {
 #pragma unroll
