@@ -19,9 +19,14 @@ CPU oracle timed on the host as a baseline.
 Extra modes:
   --copy-calibration   also runs a plain 1 GiB device copy (for scaling
                        rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
-  --ingest-pmc F W     turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE,
-                       WRITE_SIZE runs of this script with --copy-calibration)
-                       into profiles/<kernel>_<workload>_traffic.json
+  --ingest-pmc F W [M] turn rocprofv3 --pmc counter CSVs (FETCH_SIZE,
+                       WRITE_SIZE runs of this script with --copy-calibration,
+                       optionally an MFMA pass: SQ_VALU_MFMA_BUSY_CYCLES,
+                       SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE) into
+                       profiles/<kernel>_<workload>_traffic.json
+  --peaks              measured peaks next to the spec ones: a 1 GiB device
+                       copy (HBM) and a bf16 8192^3 GEMM (hipBLASLt, MFMA)
+  --dcp G              time the cross-shard merge of G page shards
 """
 import argparse
 import csv
@@ -118,7 +123,9 @@ def cpu_baseline(inp, alg, budget_s=25.0):
             "tokens_heads_per_s": round(tok * w.num_heads / dt, 1)}
 
 
-def load_traffic(workload):
+def load_counters(workload):
+    """The stage-1 counter figures of profiles/mla_stage1_<workload>_traffic.json,
+    or None when they were taken on another version of the kernel source."""
     path = os.path.join(ROOT, "profiles", f"mla_stage1_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
@@ -126,10 +133,15 @@ def load_traffic(workload):
         t = json.load(f)
     if t.get("kernel_sha256_16") != kernel_hash():
         return None  # counters were taken on another version of the kernel
-    return t.get("bytes_per_launch")
+    return t
 
 
-def ingest_pmc(fetch_csv, write_csv, workload):
+def load_traffic(workload):
+    t = load_counters(workload)
+    return t.get("bytes_per_launch") if t else None
+
+
+def ingest_pmc(fetch_csv, write_csv, workload, mfma_csv=None):
     """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the stage-1
     kernel, scaled by what the same counters read for the 1 GiB copy."""
     def per_kernel(path, counter):
@@ -162,10 +174,64 @@ def ingest_pmc(fetch_csv, write_csv, workload):
            "copy_fetch_kib": fc, "copy_write_kib": wc, "fetch_scale": ffac, "write_scale": wfac,
            "bytes_per_launch": (f1 * 1024 * ffac + w1 * 1024 * wfac) if f1 and w1 else None,
            "sources": [os.path.basename(fetch_csv), os.path.basename(write_csv)]}
+    if mfma_csv:
+        # the MFMA work the hardware counted (SQ_INSTS_VALU_MFMA_MOPS_BF16 is
+        # in units of 512 FLOP), per dispatch; the raw busy-cycle and GPU-busy
+        # counters are kept as read
+        mops = pick(per_kernel(mfma_csv, "SQ_INSTS_VALU_MFMA_MOPS_BF16"), "mla_stage1")
+        out["mfma_flops_counted"] = mops * 512 if mops else None
+        out["sq_valu_mfma_busy_cycles"] = pick(per_kernel(mfma_csv, "SQ_VALU_MFMA_BUSY_CYCLES"),
+                                               "mla_stage1")
+        out["grbm_gui_active"] = pick(per_kernel(mfma_csv, "GRBM_GUI_ACTIVE"), "mla_stage1")
+        out["sources"].append(os.path.basename(mfma_csv))
     path = os.path.join(ROOT, "profiles", f"mla_stage1_{workload}_traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
+
+
+def run_peaks(args):
+    """Measured peaks next to the spec ones: HBM from a 1 GiB device-to-device
+    copy (2 GiB moved per copy), MFMA from a bf16 8192^3 GEMM (hipBLASLt),
+    each the median of 20 timed runs after 5 warm-ups."""
+    import numpy as np
+    import torch
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, n=20):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e-3
+
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src))
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    t_mm = timed(lambda: torch.mm(a, b))
+    copy_gbs = 2 * COPY_BYTES / t_copy / 1e9
+    mm_tflops = 2 * n ** 3 / t_mm / 1e12
+    print(json.dumps({
+        "metric": "measured peaks (one MI355X)",
+        "copy_GBps": round(copy_gbs, 1), "copy_frac_of_spec": round(copy_gbs / HBM_PEAK_GBS, 4),
+        "gemm_bf16_TFLOPs": round(mm_tflops, 1),
+        "gemm_frac_of_spec": round(mm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "spec": {"hbm_GBps": HBM_PEAK_GBS, "mfma_bf16_TFLOPs": MFMA_BF16_PEAK_TFLOPS},
+        "how": "median of 20 HIP-event-timed runs: torch copy_ of 1 GiB (read + write), "
+               "torch.mm bf16 8192x8192x8192"}), flush=True)
+    return 0
 
 
 def run_dcp(args, G):
@@ -272,14 +338,18 @@ def main():
     ap.add_argument("--split", default="plan", choices=["plan", "pages", "single"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--ingest-pmc", nargs="+", metavar="CSV")
+    ap.add_argument("--peaks", action="store_true")
     ap.add_argument("--dcp", type=int, default=0, metavar="G",
                     help="time the cross-shard merge of G round-robin page shards of the "
                          "workload instead of the decode (the shards are decoded untimed)")
     args = ap.parse_args()
 
     if args.ingest_pmc:
-        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload)
+        if len(args.ingest_pmc) not in (2, 3):
+            ap.error("--ingest-pmc takes FETCH_CSV WRITE_CSV [MFMA_CSV]")
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload,
+                   args.ingest_pmc[2] if len(args.ingest_pmc) == 3 else None)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -298,6 +368,8 @@ def main():
         return 2
     if args.dcp:
         return run_dcp(args, args.dcp)
+    if args.peaks:
+        return run_peaks(args)
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
     inp = W.generate(args.workload)
@@ -405,6 +477,13 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
     roof["traffic"] = load_traffic(args.workload)
+    counters = load_counters(args.workload)
+    if counters and counters.get("mfma_flops_counted"):
+        # MFMA work counted by the hardware for one launch, over the measured
+        # launch time: the MFMA rate from counters rather than from the method
+        rate = counters["mfma_flops_counted"] / (s1_ms * 1e-3) / 1e12
+        roof["mfma_tflops_counted"] = round(rate, 1)
+        roof["mfma_frac_counted"] = round(rate / MFMA_BF16_PEAK_TFLOPS, 4)
     roof["kernel"] = "mla_stage1"
     roof["avg_launch_ms"] = round(s1_ms, 5)
     roof["mfma_tflops"] = round(alg["flops"] / (s1_ms * 1e-3) / 1e12, 1)
@@ -428,6 +507,9 @@ def main():
         "roofline_frac_total": round(max(alg["total_bytes"] / (HBM_PEAK_GBS * 1e9), t_mfma)
                                      / (ms_step * 1e-3), 4),
         "stage2_avg_ms": round(float(s2.mean()), 5),
+        "stage1_ms_p10_p50_p90": [round(float(np.percentile(s1, q)), 5) for q in (10, 50, 90)],
+        "sampled_step_ms_p10_p50_p90": [round(float(np.percentile(s1 + s2, q)), 5)
+                                        for q in (10, 50, 90)],
         "wall_s": round(wall, 4),
         "roofline": roof,
     }
