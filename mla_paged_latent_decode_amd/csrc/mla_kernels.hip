@@ -194,34 +194,16 @@ __device__ __forceinline__ u32x4 i8x8_to_bf16x8(u32x2 v) {
   return r;
 }
 
-// LDS operation schedule of one P V^T pass: step s issues the two
-// transposed V reads of step s+3, then (fp8 caches) the staging read of
-// widened block k at s = 3k, or the write of block k at s = 3k+2, then waits
-// for its own V reads and runs its MFMA.  The functions give how many LDS
-// operations were issued after the one a wait is for, which is the lgkmcnt
-// to wait for (LDS operations complete in order).
-template <int NST, int NCV>
-struct PvSched {
-  static constexpr bool has_r(int s) { return s >= 0 && s % 3 == 0 && s / 3 < NCV; }
-  static constexpr bool has_w(int s) { return s >= 0 && s % 3 == 2 && s / 3 < NCV; }
-  static constexpr int nv(int s) { return s + 3 < NST ? 2 : 0; }
-  static constexpr int ops(int s) { return nv(s) + (has_r(s) ? 1 : 0) + (has_w(s) ? 1 : 0); }
-  // after the V reads of step st (issued in step st-3, or before step 0)
-  static constexpr int after_v(int st) {
-    int n = 0;
-    if (st >= 3) {
-      n += (has_r(st - 3) ? 1 : 0) + (has_w(st - 3) ? 1 : 0);
-      for (int s = st - 2; s <= st; ++s) n += ops(s);
-    } else {
-      n += 2 * (2 - st);
-      for (int s = 0; s <= st; ++s) n += ops(s);
-    }
-    return n;
-  }
-  // after the staging read of block k, at the write of step 3k+2
-  static constexpr int after_r(int k) { return nv(3 * k + 1) + nv(3 * k + 2); }
-  static_assert(NCV == 0 || 3 * NCV - 1 < NST, "widening must end inside the pass");
-};
+// LDS reads of one P V^T pass of the pipelined loop: step s issues the two
+// transposed V reads of step s+3, then waits for its own (issued three steps
+// earlier, or before step 0) and runs its MFMA.  The lgkmcnt to wait for is
+// the number of LDS reads issued after them (LDS operations complete in order).
+template <int NST>
+constexpr int pv_reads_after(int st) {
+  int n = st >= 3 ? 0 : 2 * (2 - st);  // pre-issued reads of steps st+1 .. 2
+  for (int s = st >= 3 ? st - 2 : 0; s <= st; ++s) n += s + 3 < NST ? 2 : 0;
+  return n;
+}
 
 // Multiply an MFMA accumulator held in AGPRs by s in place.  The "+a"
 // constraints keep the accumulator in the AGPR file, so this (rare) rescale
@@ -373,12 +355,13 @@ struct Cfg {
     return NBUF >= 4 ? k * (NKS + 2 * NVB) / NIW : k * (NKS / 2) / NIW;
   }
   // Software-pipelined loop (softmax of tile j interleaved with the QK^T of
-  // tile j+1): kept for fp8 caches and the 4-tile ring (D = 320).  With the
-  // 3-tile ring the plain loop is as fast with loads and faster without:
-  // within one wave gfx950 does not overlap VALU work with an executing
-  // MFMA, so the interleaving buys nothing, while the plain loop needs no
-  // second score buffer and can spread a tile's loads over two iterations.
-  static constexpr bool PIPE = HPW == 32 && !PT && (F8 ? W == 4 : NBUF >= 4);
+  // tile j+1): kept for the bf16 4-tile ring (D = 320).  At D = 576 the
+  // plain loop is as fast or faster (bf16: as fast with loads and faster
+  // without; fp8: 8 % faster per decode step): within one wave gfx950 does
+  // not overlap VALU work with an executing MFMA, so the interleaving buys
+  // nothing, while the plain loop needs no second score buffer and can
+  // spread a tile's loads over two iterations.
+  static constexpr bool PIPE = HPW == 32 && !F8 && NBUF >= 4;
   static_assert(NBUF == stage1_ring_depth(HPW, W, D, F8, PT), "ring depth");
   static_assert(!PT || F8, "per-token rows hold 1-byte codes (e4m3fn or int8)");
   static_assert(NBLK * 1024 == kTile * D * 2, "tile bytes");
@@ -688,7 +671,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     // In the pipelined bf16 loop the LDS part is held in registers until the
     // first tiles' loads are issued, so that the query, the block-table
     // window and the first tiles are all in flight together.
-    constexpr bool kEarlyRing = C::PIPE && !F8;
+    constexpr bool kEarlyRing = C::PIPE;
     bf16x8 qf[C::NQR];
     bf16x8 qtmp[kEarlyRing ? (C::QLDS > 0 ? C::QLDS : 1) : 1];
     LDS_AS uint8_t* qlds =
@@ -723,47 +706,30 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     for (int vb = 0; vb < C::NVB; ++vb) oacc[vb] = acc_t{};
 
     if constexpr (C::PIPE) {
-      // ---- software-pipelined loop (32-head waves).  Iteration j runs the
-      // softmax of tile j interleaved with the QK^T MFMAs of tile j+1, then
-      // the PV MFMAs of tile j.  The ring holds tiles j (V) and j+1 (K).
-      // bf16: the loads of tile j+NBUF-1 go straight into the ring, spread
-      // over the PV MFMAs, with NBUF-2 tiles in flight.  fp8: the loads of
-      // tile j+3 go to staging slot (j+3) % 2 early in the iteration (over
-      // the QK^T MFMAs); tile j+2, loaded during the previous iteration, is
-      // widened into ring slot (j+2) % 3 over the PV MFMAs.  Past the
-      // segment, loads are issued with an empty resource (they write zeros
-      // into a free slot), so every iteration issues the same number of
-      // loads and the waits are constants.
-      constexpr int AHEAD = F8 ? 3 : NBUF - 1;  // tile whose loads iteration j issues: j + AHEAD
-      if constexpr (!F8) {
-        // every wave is done with the ring of a previous segment; the first
-        // tiles go out behind the query loads, then the query's LDS part is
-        // stored (asm: no compiler wait for the ring loads it cannot alias)
-        __builtin_amdgcn_s_barrier();
-#pragma unroll
-        for (int i = 0; i < NBUF - 1; ++i) issue(i);
-#pragma unroll
-        for (int k = 0; k < C::QLDS; ++k)
-          ds_write_b128_asm((uint32_t)(uintptr_t)(qlds + k * 1024 + lane * 16),
-                            __builtin_bit_cast(u32x4, qtmp[k]));
-        wait_vmcnt<(NBUF - 2) * C::LPW>();
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the query's LDS part is written
-        __builtin_amdgcn_s_barrier();
-      } else {
-      wait_vmcnt<0>();
+      // ---- software-pipelined loop (bf16, 32-head waves, ring of 4: the
+      // D = 320 shapes).  Iteration j runs the softmax of tile j interleaved
+      // with the QK^T MFMAs of tile j+1, then the PV MFMAs of tile j.  The
+      // ring holds tiles j (V) and j+1 (K); the loads of tile j+NBUF-1 go
+      // straight into the ring, spread over the MFMA steps, with NBUF-2 tiles
+      // in flight.  Past the segment, loads are issued with an empty resource
+      // (they write zeros into a free slot), so every iteration issues the
+      // same number of loads and the waits are constants.  (Measured on the
+      // D = 576 shapes, bf16 and fp8, the plain loop below is faster.)
+      static_assert(!F8, "1-byte caches take the plain loop");
+      constexpr int AHEAD = NBUF - 1;  // tile whose loads iteration j issues: j + AHEAD
+      // every wave is done with the ring of a previous segment; the first
+      // tiles go out behind the query loads, then the query's LDS part is
+      // stored (asm: no compiler wait for the ring loads it cannot alias)
       __builtin_amdgcn_s_barrier();
-      }
-      if constexpr (F8) {
-        issue(0);
-        issue(1);
-        wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();  // staging tiles 0 and 1 complete
-        widen_tile(0);
-        widen_tile(1);
-        wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();  // ring tiles 0, 1 written; staging slot 0 free
-        issue(2);
-      }
+#pragma unroll
+      for (int i = 0; i < NBUF - 1; ++i) issue(i);
+#pragma unroll
+      for (int k = 0; k < C::QLDS; ++k)
+        ds_write_b128_asm((uint32_t)(uintptr_t)(qlds + k * 1024 + lane * 16),
+                          __builtin_bit_cast(u32x4, qtmp[k]));
+      wait_vmcnt<(NBUF - 2) * C::LPW>();
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the query's LDS part is written
+      __builtin_amdgcn_s_barrier();
 
       auto kread = [&](const LDS_AS uint8_t* t, int ks) __attribute__((always_inline)) {
         return *reinterpret_cast<const LDS_AS bf16x8*>(t + (ks >> 1) * 1024 +
@@ -812,10 +778,8 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
         s_cur = s0.e + s0.o;
       }
       for (int j = 0; j < n_tiles; ++j) {
-        // tile j+1 is in the ring (fp8: its widening is written and tile
-        // j+2's staging copy complete) for every wave; tile j-1's slot is free
-        if constexpr (F8) wait_vmcnt<0>();
-        else wait_vmcnt<(NBUF - 3) * C::LPW>();
+        // tile j+1 is in the ring for every wave; tile j-1's slot is free
+        wait_vmcnt<(NBUF - 3) * C::LPW>();
         __builtin_amdgcn_s_barrier();
         const LDS_AS uint8_t* tcur = (const LDS_AS uint8_t*)ring + (j % NBUF) * C::TILE_BYTES;
         const LDS_AS uint8_t* tnext =
@@ -839,13 +803,10 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
         static_assert(E >= 1 && L >= 1, "too few QK^T steps to hide the softmax");
         auto hook = [&](auto ksc) __attribute__((always_inline)) {
           constexpr int ks = decltype(ksc)::value;
-          if constexpr (F8 && ks < C::NIW) dma(tl, ks);  // fp8: staging loads of tile j+3
-          // bf16: the loads of tile j+NBUF-1, spread evenly over the QK^T and PV steps
-          if constexpr (!F8) {
-            static_for<C::NIW>([&](auto kc) __attribute__((always_inline)) {
-              if constexpr (C::dma_step(decltype(kc)::value) == ks) dma(tl, decltype(kc)::value);
-            });
-          }
+          // the loads of tile j+NBUF-1, spread evenly over the QK^T and PV steps
+          static_for<C::NIW>([&](auto kc) __attribute__((always_inline)) {
+            if constexpr (C::dma_step(decltype(kc)::value) == ks) dma(tl, decltype(kc)::value);
+          });
           if constexpr (ks < 4) {
             mt = fmaxf(mt, fmaxf(fmaxf(sv[4 * ks], sv[4 * ks + 1]), fmaxf(sv[4 * ks + 2], sv[4 * ks + 3])));
           } else if constexpr (ks == 4) {
@@ -926,7 +887,6 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           const uint32_t vbase0 = (uint32_t)(uintptr_t)tcur + v_off0;
           const uint32_t vbase1 = (uint32_t)(uintptr_t)tcur + v_off1;
           constexpr int NST = 2 * C::NVB;
-          using Sched = PvSched<NST, F8 ? C::LPW : 0>;
           auto vread = [&](auto stc) __attribute__((always_inline)) {
             constexpr int st = decltype(stc)::value;
             constexpr int kk = st / C::NVB, vb = st % C::NVB;
@@ -938,20 +898,12 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           u32x4 a0 = vread(std::integral_constant<int, 0>{});
           u32x4 a1 = vread(std::integral_constant<int, 1>{});
           u32x4 a2 = vread(std::integral_constant<int, 2>{});
-          u32x2 wv = {};  // fp8: staging chunk being widened
           static_for<NST>([&](auto stc) __attribute__((always_inline)) {
             constexpr int st = decltype(stc)::value;
             constexpr int kk = st / C::NVB, vb = st % C::NVB;
             u32x4 a3 = a2;
             if constexpr (st + 3 < NST) a3 = vread(std::integral_constant<int, st + 3>{});
-            if constexpr (F8) {  // widen block st/3 of tile j+2
-              if constexpr (Sched::has_r(st)) wv = ds_read_b64_asm(widen_src(j + 2, st / 3));
-              if constexpr (Sched::has_w(st)) {
-                lds_wait<Sched::after_r(st / 3)>(wv);
-                ds_write_b128_asm(widen_dst(j + 2, st / 3), e4m3x8_to_bf16x8(wv));
-              }
-            }
-            lds_wait<Sched::after_v(st)>(a0);
+            lds_wait<pv_reads_after<NST>(st)>(a0);
             oacc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0),
                                                               kk ? p1 : p0, oacc[vb], 0, 0, 0);
             // scores of tile j+1: sum of its two QK^T chains
@@ -959,13 +911,11 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
 #pragma unroll
               for (int r = 4 * st; r < 4 * st + 4; ++r) s_cur[r] = s_next.e[r] + s_next.o[r];
             }
-            // bf16: the rest of the loads of tile j+NBUF-1
-            if constexpr (!F8) {
-              static_for<C::NIW>([&](auto kc) __attribute__((always_inline)) {
-                if constexpr (C::dma_step(decltype(kc)::value) == C::NKS + st)
-                  dma(tl, decltype(kc)::value);
-              });
-            }
+            // the rest of the loads of tile j+NBUF-1
+            static_for<C::NIW>([&](auto kc) __attribute__((always_inline)) {
+              if constexpr (C::dma_step(decltype(kc)::value) == C::NKS + st)
+                dma(tl, decltype(kc)::value);
+            });
             __builtin_amdgcn_sched_barrier(0);
             a0 = a1;
             a1 = a2;
