@@ -278,9 +278,9 @@ mla_status mla_decode_mtp_stage2(const mla_shape* shape, int32_t q_len, const vo
  *   topk_indices  [batch, topk] int32, device; entries and topk_lens[b] <= topk
  *                 are trusted like block_table entries
  *   topk_lens     [batch] int32, device; 0 gives o = 0, lse = -inf
- * The index-driven gather reads bf16 caches of at most 4 GB (else
- * MLA_ERR_DTYPE / MLA_ERR_SHAPE), for both head sizes and every head count
- * mla_decode takes; topk < 1 is MLA_ERR_ARGUMENT, NULL lists MLA_ERR_NULL. */
+ * The index-driven gather takes every cache dtype, head size and head count
+ * mla_decode takes, for pools of at most 4 GB (else MLA_ERR_SHAPE); topk < 1
+ * is MLA_ERR_ARGUMENT, NULL lists MLA_ERR_NULL. */
 mla_status mla_decode_sparse(const mla_shape* shape, int32_t topk, const void* q,
                              const void* kv_cache, const int32_t* block_table,
                              const int32_t* topk_indices, const int32_t* topk_lens, float scale,

@@ -270,7 +270,8 @@ def mla_decode_sparse(q, kv_cache, block_table, topk_indices, topk_lens, scale: 
                       page_size: int, k_scale: float = 1.0,
                       num_kv_splits: Optional[int] = None, o=None, lse=None, *,
                       split_mode: Optional[int] = None, workspace=None, o_dtype=None,
-                      num_cus: Optional[int] = None, stream=None, stages: str = "both"):
+                      num_cus: Optional[int] = None, stream=None, stages: str = "both",
+                      kv_dtype=None):
     """Sparse (top-k) MLA decode: sequence b attends to the cache rows of the
     logical positions ``topk_indices[b, :topk_lens[b]]`` (int32 [B, topk] and
     [B]).  Other arguments as in ``mla_decode``; the split plan counts list
@@ -285,7 +286,7 @@ def mla_decode_sparse(q, kv_cache, block_table, topk_indices, topk_lens, scale: 
         raise ValueError("topk_indices and topk_lens must be int32")
     if o is not None:
         o_dtype = o.dtype
-    shape = shape_of(q, kv_cache, block_table, o_dtype=o_dtype)
+    shape = shape_of(q, kv_cache, block_table, kv_dtype=kv_dtype, o_dtype=o_dtype)
     B, H = shape.batch, shape.num_heads
     topk = int(topk_indices.shape[1])
     if num_kv_splits is None:

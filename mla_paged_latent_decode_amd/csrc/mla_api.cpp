@@ -303,8 +303,11 @@ static mla_status check_sparse(const mla_shape* shape, int32_t topk, const int32
   if (st != MLA_OK) return st;
   if (!topk_indices || !topk_lens) return MLA_ERR_NULL;
   if (topk < 1) return MLA_ERR_ARGUMENT;
-  if (shape->kv_dtype != MLA_BF16) return MLA_ERR_DTYPE;
-  const uint64_t pool = (uint64_t)shape->num_blocks * shape->page_size * shape->head_size * 2;
+  const bool per_token =
+      shape->kv_dtype == MLA_FP8_E4M3_PER_TOKEN || shape->kv_dtype == MLA_INT8_PER_TOKEN;
+  const uint64_t row = per_token ? shape->head_size + MLA_PER_TOKEN_PAD
+                                 : (uint64_t)shape->head_size * (shape->kv_dtype == MLA_BF16 ? 2 : 1);
+  const uint64_t pool = (uint64_t)shape->num_blocks * shape->page_size * row;
   if (pool + 65536 >= ((uint64_t)1 << 32)) return MLA_ERR_SHAPE;
   if (!aligned(topk_indices, 4)) return MLA_ERR_ARGUMENT;
   return MLA_OK;
@@ -360,7 +363,7 @@ const char* mla_status_string(int32_t status) {
     case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
     case MLA_ERR_HEAD_SIZE: return "MLA_ERR_HEAD_SIZE: head_size must be 576 or 320 with kv_lora_rank = head_size - 64";
     case MLA_ERR_PAGE_SIZE: return "MLA_ERR_PAGE_SIZE: page_size must be a positive multiple of 16 and match the shape";
-    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: q must be bf16, kv bf16, fp8 e4m3fn (per-tensor or per-token scale) or per-token int8 (bf16 only for sparse decode), o bf16 or fp32";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: q must be bf16, kv bf16, fp8 e4m3fn (per-tensor or per-token scale) or per-token int8, o bf16 or fp32";
     case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: batch, heads (multiple of 16), num_blocks or table width out of range";
     case MLA_ERR_SPLITS: return "MLA_ERR_SPLITS: num_kv_splits or split_mode out of range";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";

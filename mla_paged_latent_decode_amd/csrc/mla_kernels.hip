@@ -387,7 +387,6 @@ __device__ __forceinline__ int tile_slot(int t16, int c4) {
 template <int HPW, int W, int D, int DV, int NBUF, bool F8, bool SP, int PT>
 __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   using C = Cfg<HPW, W, D, DV, NBUF, F8, PT>;
-  static_assert(!SP || !F8, "the index-driven gather reads bf16 cache rows");
   // [bf16 ring: NBUF tiles][fp8 staging: 2 tiles][Q k-steps of each wave]
   // [per-token scales: 2 staging slots of 2 x 256 B, NBUF ring slots of 128 B]
   __shared__ __attribute__((aligned(1024)))
@@ -573,10 +572,38 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       if constexpr (SP) {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)p.kv, (short)0, (int)p.pool_bytes, 0x00020000);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(tl.dst + j * 1024), 16,
-                                                 (int)((th ? tl.off[1] : tl.off[0]) +
-                                                       16 * dma_c4) + sgpr_here(64 * r),
-                                                 0, 0, 0);
+        if constexpr (F8) {
+          // 1-byte codes: the r-th 64*G bytes of half th go to the row-major
+          // staging tile as in dense decode, but each row comes from its own
+          // slot; lane t < 16 holds the offset of row t of the half
+          // (dma_t16 = lane there), read here with a lane shuffle
+          const int c = C::G * lane + sgpr_here(r * 64 * C::G);  // code byte in the half
+          const int row = c / D;
+          const uint32_t roff = (uint32_t)__shfl((int)(th ? tl.off[1] : tl.off[0]), row, 64);
+          LDS_AS void* dst = (LDS_AS void*)(tl.dst + th * 16 * D + r * 64 * C::G);
+          const int voff = (int)(roff + (uint32_t)(c - row * D));
+          if constexpr (C::G == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, 0, 0, 0);
+          else __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, voff, 0, 0, 0);
+          if constexpr (PT) {
+            if (k == 0 && wave == 0) {
+              // the 16 inline scales of each half: lane l < 16 reads row l's
+              // (rows past the segment, and lanes >= 16, read 0)
+#pragma unroll
+              for (int h2 = 0; h2 < 2; ++h2) {
+                const int soff = lane < 16 ? (int)((h2 ? tl.off[1] : tl.off[0]) + D)
+                                           : (int)p.pool_bytes;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (LDS_AS uint8_t*)ring + kSclOff + tl.sslot * 512 + h2 * 256, 4, soff,
+                    0, 0, 0);
+              }
+            }
+          }
+        } else {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(tl.dst + j * 1024), 16,
+                                                   (int)((th ? tl.off[1] : tl.off[0]) +
+                                                         16 * dma_c4) + sgpr_here(64 * r),
+                                                   0, 0, 0);
+        }
         return;
       }
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -1645,10 +1672,18 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   if (stages & kStage1) {
     int err;
     if (a.topk_idx) {
-      // the host admits the sparse gather for bf16 caches only
-      if (a.kv_fp8) return -1;
-      err = a.head_size == 576 ? launch_stage1_for<576, 512, false, 0, true>(ht, sp, grid1, st)
-                               : launch_stage1_for<320, 256, false, 0, true>(ht, sp, grid1, st);
+      if (a.kv_pt == 1)
+        err = a.head_size == 576 ? launch_stage1_for<576, 512, true, 1, true>(ht, sp, grid1, st)
+                                 : launch_stage1_for<320, 256, true, 1, true>(ht, sp, grid1, st);
+      else if (a.kv_pt == 2)
+        err = a.head_size == 576 ? launch_stage1_for<576, 512, true, 2, true>(ht, sp, grid1, st)
+                                 : launch_stage1_for<320, 256, true, 2, true>(ht, sp, grid1, st);
+      else if (a.kv_fp8)
+        err = a.head_size == 576 ? launch_stage1_for<576, 512, true, 0, true>(ht, sp, grid1, st)
+                                 : launch_stage1_for<320, 256, true, 0, true>(ht, sp, grid1, st);
+      else
+        err = a.head_size == 576 ? launch_stage1_for<576, 512, false, 0, true>(ht, sp, grid1, st)
+                                 : launch_stage1_for<320, 256, false, 0, true>(ht, sp, grid1, st);
     } else if (a.kv_pt == 1)
       err = a.head_size == 576 ? launch_stage1_for<576, 512, true, 1>(ht, sp, grid1, st)
                                : launch_stage1_for<320, 256, true, 1>(ht, sp, grid1, st);

@@ -34,15 +34,24 @@ def dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).to(torch.device("cuda:0"))
 
 
+def kv_dev(inp):
+    if inp.kv_dtype == W.BF16:
+        return dev(inp.kv_bits.view(np.int16)).view(torch.bfloat16)
+    if inp.kv_dtype == W.FP8_E4M3:
+        return dev(inp.kv_bits).view(torch.float8_e4m3fn)
+    return dev(inp.kv_bits)  # per-token rows: uint8
+
+
 def run_sparse(mla, inp, splits, mode, idx=None, lens=None, o_dtype=None):
     w = inp.workload
     q = dev(inp.q_bits.view(np.int16)).view(torch.bfloat16)
-    kv = dev(inp.kv_bits.view(np.int16)).view(torch.bfloat16)
-    o, lse = mla.mla_decode_sparse(q, kv, dev(inp.block_table),
+    print(f"[sparse] {w.kv_dtype} B={len(inp.seq_lens)} H={w.num_heads} D={w.head_size} "
+          f"P={w.page_size} mode={mode} S={splits}", flush=True)
+    o, lse = mla.mla_decode_sparse(q, kv_dev(inp), dev(inp.block_table),
                                    dev(inp.topk_indices if idx is None else idx),
                                    dev(inp.topk_lens if lens is None else lens), w.scale,
                                    w.page_size, w.k_scale, splits, split_mode=mode,
-                                   o_dtype=o_dtype or torch.bfloat16)
+                                   o_dtype=o_dtype or torch.bfloat16, kv_dtype=w.kv_dtype)
     torch.cuda.synchronize()
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
@@ -137,16 +146,58 @@ def test_sparse_ignores_unlisted_slots(mla, mode, splits):
     assert np.array_equal(a[0], b_[0]) and np.array_equal(a[1], b_[1])
 
 
-def test_sparse_rejects_quantised_caches(mla):
-    inp = W.small_case(seed=412, batch=1, num_heads=16, head_size=576, kv_lora_rank=512,
-                       page_size=16, seq_lens=(40,), topk=8, kv_dtype=W.FP8_E4M3, k_scale=0.05)
+QUANT_CASES = [
+    # (H, D, P, seq_lens, topk): 1-byte caches through the same gather
+    (128, 576, 64, (300, 2000, 40, 1031), 256),
+    (16, 576, 16, (1, 33, 64, 100), 48),
+    (64, 576, 64, (300, 2000), 200),
+    (128, 320, 32, (17, 95, 333), 72),
+]
+
+
+@pytest.mark.parametrize("dt", [W.FP8_E4M3, W.FP8_PER_TOKEN, W.INT8_PER_TOKEN])
+@pytest.mark.parametrize("case", range(len(QUANT_CASES)))
+@pytest.mark.parametrize("mode,splits", [(0, 1), (0, 3), (1, 5), (1, 37)])
+def test_sparse_quantised_caches(mla, case, mode, splits, dt):
+    """Quantised caches (per-tensor fp8; per-token fp8 / int8 with inline
+    scales) gathered by the index lists; tolerances of the fp8 cache."""
+    H, D, P, sl, k = QUANT_CASES[case]
+    inp = W.small_case(seed=420 + case, batch=len(sl), num_heads=H, head_size=D,
+                       kv_lora_rank=D - 64, page_size=P, seq_lens=sl, topk=k, kv_dtype=dt,
+                       k_scale=0.05 if dt == W.FP8_E4M3 else 1.0)
+    ro, rl = ref(inp)
+    o, lse = run_sparse(mla, inp, splits, mode, o_dtype=torch.float32)
+    lens = np.asarray(inp.topk_lens)
+    empty = lens == 0
+    live = ~empty
+    assert np.all(o[empty] == 0) and np.all(np.isneginf(lse[empty]))
+    do = np.abs(o[live] - ro[live]).max()
+    dl = np.abs(lse[live] - rl[live]).max()
+    print(f"sparse {dt} case{case} mode={mode} S={splits}: max|do|={do:.3e} max|dlse|={dl:.3e}",
+          flush=True)
+    assert np.all(np.isfinite(o[live])) and do <= 3e-2 and dl <= 3e-3
+
+
+@pytest.mark.parametrize("dt", [W.FP8_E4M3, W.FP8_PER_TOKEN, W.INT8_PER_TOKEN])
+@pytest.mark.parametrize("mode,splits", [(0, 1), (1, 7)])
+def test_sparse_quantised_over_every_position_is_dense_bitwise(mla, mode, splits, dt):
+    sl = (37, 100, 1, 700)
+    inp = W.small_case(seed=430, batch=len(sl), num_heads=128, head_size=576, kv_lora_rank=512,
+                       page_size=64, seq_lens=sl, kv_dtype=dt,
+                       k_scale=0.05 if dt == W.FP8_E4M3 else 1.0)
+    idx = np.zeros((len(sl), 704), np.int32)
+    for b, n in enumerate(sl):
+        idx[b, :n] = np.arange(n)
     w = inp.workload
     q = dev(inp.q_bits.view(np.int16)).view(torch.bfloat16)
-    kv = dev(inp.kv_bits).view(torch.float8_e4m3fn)
-    with pytest.raises(NotImplementedError):  # MLA_ERR_DTYPE: the gather reads bf16 rows
-        mla.mla_decode_sparse(q, kv, dev(inp.block_table), dev(inp.topk_indices),
-                              dev(inp.topk_lens), w.scale, w.page_size, w.k_scale, 1,
-                              split_mode=0)
+    kv = kv_dev(inp)
+    bt, lens = dev(inp.block_table), dev(np.asarray(sl, np.int32))
+    od, ld = mla.mla_decode(q, kv, bt, lens, w.scale, w.page_size, w.k_scale, splits,
+                            split_mode=mode, kv_dtype=w.kv_dtype)
+    os_, ls_ = mla.mla_decode_sparse(q, kv, bt, dev(idx), lens, w.scale, w.page_size,
+                                     w.k_scale, splits, split_mode=mode, kv_dtype=w.kv_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(od, os_) and torch.equal(ld, ls_)
 
 
 def test_sparse_full_size(mla):

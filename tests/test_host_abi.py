@@ -157,11 +157,16 @@ def test_per_token_cache_argument_checks(code):
     # the call is stopped by the next one (a missing workspace)
     assert _decode_raw(pt, k_scale=0.0, splits=16) == mla.MLA_ERR_WORKSPACE
     assert _decode_raw(pt, q=258) == mla.MLA_ERR_ARGUMENT
-    # the sparse gather is built for bf16 caches only
+    # the sparse gather addresses the pool with 32-bit offsets: pools past
+    # 4 GB (here 200000 pages of 64 rows of 592 bytes) are refused
     lib = mla.load_library()
-    st = lib.mla_decode_sparse(ctypes.byref(pt), 2048, 256, 256, 256, 256, 256, 0.07,
+    big = shape(kv_dtype=code, num_blocks=200000)
+    st = lib.mla_decode_sparse(ctypes.byref(big), 2048, 256, 256, 256, 256, 256, 0.07,
+                               big.page_size, 1.0, 1, 0, 256, 256, None, 0, None)
+    assert st == mla.MLA_ERR_SHAPE
+    st = lib.mla_decode_sparse(ctypes.byref(pt), 0, 256, 256, 256, 256, 256, 0.07,
                                pt.page_size, 1.0, 1, 0, 256, 256, None, 0, None)
-    assert st == mla.MLA_ERR_DTYPE
+    assert st == mla.MLA_ERR_ARGUMENT  # topk < 1
 
 
 def test_shape_of_checks_cache_row_width():
