@@ -3,21 +3,31 @@
 ``build()`` always recompiles; ``ensure_built()`` builds only when the shared
 library is missing.  The library is a plain C-ABI shared object (no torch
 types), loaded by the ctypes binding in this package.
+
+The stage-1 kernel source is compiled once per group of template instances
+(MLA_STAGE1_GROUP 0..7) and once for the rest (MLA_MAIN); the translation
+units build in parallel and are linked into one library.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libmla.so")
-SOURCES = [os.path.join(CSRC, "mla_api.cpp"), os.path.join(CSRC, "mla_kernels.hip"),
-           os.path.join(CSRC, "mla_merge.hip")]
+KERNELS = os.path.join(CSRC, "mla_kernels.hip")
+# (source, extra defines) of every translation unit
+UNITS = ([(os.path.join(CSRC, "mla_api.cpp"), []), (os.path.join(CSRC, "mla_merge.hip"), []),
+          (KERNELS, ["-DMLA_MAIN"])] +
+         [(KERNELS, [f"-DMLA_STAGE1_GROUP={g}"]) for g in range(8)])
+SOURCES = sorted({u[0] for u in UNITS})
 ARCH = "gfx950"
 
 
@@ -28,30 +38,51 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmla)")
 
 
-def compile_command(out: str = LIB_PATH) -> list:
-    return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        f"-I{INCLUDE}", f"-I{CSRC}",
-        # packed fp32 VALU ops stay disabled in every HIP translation unit
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wno-unused-command-line-argument", "-Wl,--no-undefined",
-        *SOURCES, "-o", out,
-    ]
+def _flags() -> list:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}",
+            # packed fp32 VALU ops stay disabled in every HIP translation unit
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wno-unused-command-line-argument"]
 
 
-def build(verbose: bool = True) -> str:
-    tmp = LIB_PATH + ".tmp"
-    cmd = compile_command(tmp)
-    if verbose:
-        print("[libmla] " + " ".join(cmd), flush=True)
+def compile_commands(obj_dir: str) -> list:
+    cmds = []
+    for i, (src, defs) in enumerate(UNITS):
+        obj = os.path.join(obj_dir, f"unit{i}.o")
+        cmds.append(([hipcc(), *_flags(), *defs, "-c", src, "-o", obj], obj))
+    return cmds
+
+
+def _run(cmd):
     res = subprocess.run(cmd, cwd=PKG_DIR, capture_output=True, text=True)
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines()
             if ln.strip() and "packed-fp32-ops" not in ln]
-    if res.returncode != 0:
-        raise RuntimeError("libmla build failed:\n" + "\n".join(msgs))
-    if verbose and msgs:
-        print("\n".join(msgs), file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
+    return res.returncode, msgs
+
+
+def build(verbose: bool = True) -> str:
+    with tempfile.TemporaryDirectory(prefix="libmla_build_") as tmp:
+        cmds = compile_commands(tmp)
+        if verbose:
+            for cmd, _ in cmds:
+                print("[libmla] " + " ".join(cmd), flush=True)
+        jobs = max(1, min(len(cmds), os.cpu_count() or 1))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as pool:
+            results = list(pool.map(_run, [c for c, _ in cmds]))
+        msgs = [m for _, ms in results for m in ms]
+        if any(rc != 0 for rc, _ in results):
+            raise RuntimeError("libmla build failed:\n" + "\n".join(msgs))
+        tmp_lib = LIB_PATH + ".tmp"
+        link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined",
+                *[o for _, o in cmds], "-o", tmp_lib]
+        if verbose:
+            print("[libmla] " + " ".join(link), flush=True)
+        rc, lmsgs = _run(link)
+        if rc != 0:
+            raise RuntimeError("libmla link failed:\n" + "\n".join(lmsgs))
+        if verbose and (msgs or lmsgs):
+            print("\n".join(msgs + lmsgs), file=sys.stderr)
+        os.replace(tmp_lib, LIB_PATH)
     return LIB_PATH
 
 
@@ -59,7 +90,3 @@ def ensure_built() -> str:
     if not os.path.exists(LIB_PATH):
         build()
     return LIB_PATH
-
-
-if __name__ == "__main__":
-    build()

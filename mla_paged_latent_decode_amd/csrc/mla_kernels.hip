@@ -241,6 +241,10 @@ __device__ __forceinline__ void store_out4(void* o, int o_f32, size_t idx, f32x4
   }
 }
 
+}  // namespace
+
+// Kernel parameters of stage 1 (one definition for every translation unit
+// built from this source, see the dispatch section).
 struct Stage1Params {
   const __bf16* q;
   const uint8_t* kv;
@@ -269,6 +273,8 @@ struct Stage1Params {
   float score_log2;  // scale * log2(e) (* k_scale for per-tensor fp8 caches)
   float out_scale;   // 1, or k_scale for per-tensor fp8 caches
 };
+
+namespace {
 
 // ---------------------------------------------------------------- work units
 
@@ -1621,6 +1627,39 @@ int launch_stage1_for(const HeadTiling& ht, const Stage1Params& sp, int grid, hi
 
 }  // namespace
 
+// The stage-1 launches of one group of variants.  This source is compiled
+// once per group (MLA_STAGE1_GROUP = 0..7: sparse gather or not x bf16,
+// per-tensor fp8, per-token fp8 or per-token int8 cache) and once with
+// MLA_MAIN for the rest, so that the many template instances build in
+// parallel.
+#define MLA_CAT2(a, b) a##b
+#define MLA_CAT(a, b) MLA_CAT2(a, b)
+#define MLA_DECLARE_GROUP(g)                                                              \
+  int MLA_CAT(launch_stage1_group, g)(int head_size, const HeadTiling& ht,               \
+                                      const Stage1Params& sp, int grid, hipStream_t st);
+MLA_DECLARE_GROUP(0)
+MLA_DECLARE_GROUP(1)
+MLA_DECLARE_GROUP(2)
+MLA_DECLARE_GROUP(3)
+MLA_DECLARE_GROUP(4)
+MLA_DECLARE_GROUP(5)
+MLA_DECLARE_GROUP(6)
+MLA_DECLARE_GROUP(7)
+
+#ifdef MLA_STAGE1_GROUP
+int MLA_CAT(launch_stage1_group, MLA_STAGE1_GROUP)(int head_size, const HeadTiling& ht,
+                                                   const Stage1Params& sp, int grid,
+                                                   hipStream_t st) {
+  constexpr bool SP = MLA_STAGE1_GROUP >= 4;
+  constexpr int fmt = MLA_STAGE1_GROUP % 4;  // 0 bf16, 1 fp8 k_scale, 2 fp8 per token, 3 int8
+  constexpr bool F8 = fmt != 0;
+  constexpr int PT = fmt >= 2 ? fmt - 1 : 0;
+  return head_size == 576 ? launch_stage1_for<576, 512, F8, PT, SP>(ht, sp, grid, st)
+                          : launch_stage1_for<320, 256, F8, PT, SP>(ht, sp, grid, st);
+}
+#endif
+
+#ifdef MLA_MAIN
 // What starting a segment costs, in tiles of the balanced cost stream: the
 // query rows of a workgroup's heads and one partial row per head, plus about
 // one tile of latency.  Measured on the dsv3 shape (128 heads per
@@ -1670,32 +1709,20 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   const int units = a.split_mode == 0 ? a.batch * a.num_splits : a.num_splits;
   const int grid1 = (units + 7) / 8 * 8 * ht.head_chunks;
   if (stages & kStage1) {
+    // the group of variants: gather (+4) and cache format
+    const int fmt = a.kv_pt ? 1 + a.kv_pt : (a.kv_fp8 ? 1 : 0);
+    const int group = (a.topk_idx ? 4 : 0) + fmt;
     int err;
-    if (a.topk_idx) {
-      if (a.kv_pt == 1)
-        err = a.head_size == 576 ? launch_stage1_for<576, 512, true, 1, true>(ht, sp, grid1, st)
-                                 : launch_stage1_for<320, 256, true, 1, true>(ht, sp, grid1, st);
-      else if (a.kv_pt == 2)
-        err = a.head_size == 576 ? launch_stage1_for<576, 512, true, 2, true>(ht, sp, grid1, st)
-                                 : launch_stage1_for<320, 256, true, 2, true>(ht, sp, grid1, st);
-      else if (a.kv_fp8)
-        err = a.head_size == 576 ? launch_stage1_for<576, 512, true, 0, true>(ht, sp, grid1, st)
-                                 : launch_stage1_for<320, 256, true, 0, true>(ht, sp, grid1, st);
-      else
-        err = a.head_size == 576 ? launch_stage1_for<576, 512, false, 0, true>(ht, sp, grid1, st)
-                                 : launch_stage1_for<320, 256, false, 0, true>(ht, sp, grid1, st);
-    } else if (a.kv_pt == 1)
-      err = a.head_size == 576 ? launch_stage1_for<576, 512, true, 1>(ht, sp, grid1, st)
-                               : launch_stage1_for<320, 256, true, 1>(ht, sp, grid1, st);
-    else if (a.kv_pt == 2)
-      err = a.head_size == 576 ? launch_stage1_for<576, 512, true, 2>(ht, sp, grid1, st)
-                               : launch_stage1_for<320, 256, true, 2>(ht, sp, grid1, st);
-    else if (a.kv_fp8)
-      err = a.head_size == 576 ? launch_stage1_for<576, 512, true>(ht, sp, grid1, st)
-                               : launch_stage1_for<320, 256, true>(ht, sp, grid1, st);
-    else
-      err = a.head_size == 576 ? launch_stage1_for<576, 512, false>(ht, sp, grid1, st)
-                               : launch_stage1_for<320, 256, false>(ht, sp, grid1, st);
+    switch (group) {
+      case 0: err = launch_stage1_group0(a.head_size, ht, sp, grid1, st); break;
+      case 1: err = launch_stage1_group1(a.head_size, ht, sp, grid1, st); break;
+      case 2: err = launch_stage1_group2(a.head_size, ht, sp, grid1, st); break;
+      case 3: err = launch_stage1_group3(a.head_size, ht, sp, grid1, st); break;
+      case 4: err = launch_stage1_group4(a.head_size, ht, sp, grid1, st); break;
+      case 5: err = launch_stage1_group5(a.head_size, ht, sp, grid1, st); break;
+      case 6: err = launch_stage1_group6(a.head_size, ht, sp, grid1, st); break;
+      default: err = launch_stage1_group7(a.head_size, ht, sp, grid1, st); break;
+    }
     if (err) return err;
   }
   const bool merge = a.split_mode == 1 || a.num_splits > 1;
@@ -1723,5 +1750,6 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   else hipLaunchKernelGGL(mla_stage2<256>, dim3(grid2), dim3(256), 0, st, s2);
   return (int)hipGetLastError();
 }
+#endif  // MLA_MAIN
 
 }  // namespace mla
