@@ -25,9 +25,9 @@ What it computes (decode attention of one latent query per head):
 * For an fp8 cache one per-layer scale multiplies both K and V
   (Triton MLA page, data flow: ``k_scale = v_scale = layer._k_scale``); for a
   bf16 cache it has no effect (same listing's comment on the fp8 check).
-* A per-token-head cache (Triton MLA page, key files: fp8 and int8 modes
-  whose rows are padded to hold an inline scale) stores each token's codes
-  followed by its float32 scale; the token's K and V are code * scale.
+* A per-token-head cache (Triton MLA page, key files: fp8, int8 and int4
+  modes whose rows are padded to hold an inline scale) stores each token's
+  codes followed by its float32 scale; the token's K and V are code * scale.
 
 The online softmax (lshu.cn article, section 7) and the split-KV merge
 (section 12) are exact rewrites of this plain softmax, so ``decode`` is the
@@ -78,7 +78,7 @@ def e4m3fn_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 PER_TOKEN_PAD = 16  # bytes after the codes of a per-token row: fp32 scale + 12 unused
-PER_TOKEN_DTYPES = ("fp8_per_token", "int8_per_token")
+PER_TOKEN_DTYPES = ("fp8_per_token", "int8_per_token", "int4_per_token")
 
 
 def int8_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -86,12 +86,34 @@ def int8_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return np.asarray(bits, dtype=np.uint8).view(np.int8).astype(np.float64)
 
 
+def int4_bits_to_f64(packed: np.ndarray) -> np.ndarray:
+    """Two signed 4-bit codes per byte, element 2i in the low nibble of byte
+    i and element 2i+1 in the high nibble (two's complement, -8..7)."""
+    b = np.asarray(packed, dtype=np.uint8)
+    lo = (b & 0x0F).astype(np.int16)
+    hi = (b >> 4).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.float64)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def code_bytes(kv_dtype: str, head_size: int) -> int:
+    """Bytes of codes in a per-token row (int4 packs two codes per byte)."""
+    return head_size // 2 if kv_dtype == "int4_per_token" else head_size
+
+
 def row_width(kv_dtype: str, head_size: int) -> int:
-    """Stored elements (bytes for fp8 / int8) per cache row: the head_size
-    values, and for the per-token layouts the padding that holds the inline
-    scale (Triton MLA page, key files: in the per-token-head modes, fp8 and
-    int8 among them, the cache shape pads head_dim to hold an inline scale)."""
-    return head_size + PER_TOKEN_PAD if kv_dtype in PER_TOKEN_DTYPES else head_size
+    """Stored elements (bytes for the 1-byte and packed formats) per cache
+    row: the head_size values, and for the per-token layouts the padding that
+    holds the inline scale (Triton MLA page, key files: in the per-token-head
+    modes, fp8, int8 and int4 among them, the cache shape pads head_dim to
+    hold an inline scale)."""
+    if kv_dtype in PER_TOKEN_DTYPES:
+        return code_bytes(kv_dtype, head_size) + PER_TOKEN_PAD
+    return head_size
 
 
 def decode_kv(kv_bits: np.ndarray, kv_dtype: str, k_scale: float) -> np.ndarray:
@@ -106,11 +128,11 @@ def decode_kv(kv_bits: np.ndarray, kv_dtype: str, k_scale: float) -> np.ndarray:
         return e4m3fn_bits_to_f64(kv_bits) * float(np.float32(k_scale))
     if kv_dtype in PER_TOKEN_DTYPES:
         rows = np.ascontiguousarray(kv_bits, dtype=np.uint8)
-        D = rows.shape[-1] - PER_TOKEN_PAD
-        scale = rows[..., D:D + 4].copy().view("<f4")[..., 0].astype(np.float64)
-        codes = (e4m3fn_bits_to_f64 if kv_dtype == "fp8_per_token" else int8_bits_to_f64)(
-            rows[..., :D])
-        return codes * scale[..., None]
+        nb = rows.shape[-1] - PER_TOKEN_PAD  # code bytes
+        scale = rows[..., nb:nb + 4].copy().view("<f4")[..., 0].astype(np.float64)
+        decode = {"fp8_per_token": e4m3fn_bits_to_f64, "int8_per_token": int8_bits_to_f64,
+                  "int4_per_token": int4_bits_to_f64}[kv_dtype]
+        return decode(rows[..., :nb]) * scale[..., None]
     raise ValueError(f"unknown kv dtype {kv_dtype!r}")
 
 
@@ -388,5 +410,5 @@ __all__ = [
     "physical_slot", "gather_rows", "attend", "decode", "segment_bounds", "merge_partials",
     "merge_normalised", "segment_partial", "decode_split", "pages_split_count",
     "visible_keys", "decode_mtp", "decode_sparse", "row_width", "PER_TOKEN_PAD",
-    "PER_TOKEN_DTYPES", "int8_bits_to_f64", "merge_shards",
+    "PER_TOKEN_DTYPES", "int8_bits_to_f64", "int4_bits_to_f64", "code_bytes", "merge_shards",
 ]

@@ -59,6 +59,15 @@ def dense_keys(inp, b):
         codes = torch.from_numpy(flat[:, :D].copy()).view(code_t).to(torch.float64)
         scale = torch.from_numpy(flat[:, D:D + 4].copy()).view(torch.float32).to(torch.float64)
         return codes * scale
+    if w.kv_dtype == "int4_per_token":
+        # nibbles with torch integer ops: sign-extend by shifting into an int8's top bits
+        nb = w.head_size // 2
+        b = torch.from_numpy(flat[:, :nb].copy()).view(torch.int8)
+        lo = torch.bitwise_left_shift(b, 4) >> 4
+        hi = b >> 4
+        codes = torch.stack([lo, hi], dim=-1).reshape(b.shape[0], 2 * nb).to(torch.float64)
+        scale = torch.from_numpy(flat[:, nb:nb + 4].copy()).view(torch.float32).to(torch.float64)
+        return codes * scale
     t = torch.from_numpy(flat.copy()).view(torch.float8_e4m3fn)
     return t.to(torch.float64) * float(np.float32(w.k_scale))
 
@@ -842,3 +851,76 @@ def test_shard_merge_closed_form():
     o, lse = O.merge_shards(o_p, l_p)
     assert np.allclose(o[0], [0.75, 0.25], atol=1e-15, rtol=0)
     assert abs(lse[0] - math.log(4.0)) < 1e-15
+
+
+# ---------------------------------------------------------------- per-token int4 cache
+# (the same pages list int4 among the per-token-head modes; rows here are
+# [two signed 4-bit codes per byte, element 2i low nibble (D/2 bytes) |
+#  fp32 scale | 12 pad bytes], value = code * scale)
+
+def test_int4_every_byte_decodes_to_its_two_nibbles():
+    rows = np.zeros((1, 256 + 16), dtype=np.uint8)
+    rows[0, :256] = np.arange(256, dtype=np.uint8)
+    rows[0, 256:260] = np.array([1.0], dtype="<f4").view(np.uint8)
+    got = O.decode_kv(rows, "int4_per_token", 1.0)[0]
+    signed = lambda v: v - 16 if v >= 8 else v
+    want = np.array([f(b) for b in range(256) for f in (lambda b: signed(b & 15),
+                                                        lambda b: signed(b >> 4))],
+                    dtype=np.float64)
+    assert np.array_equal(got, want)
+    assert O.row_width("int4_per_token", 576) == 288 + 16
+
+
+def test_int4_quantisation_round_trips_within_half_a_step():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((64, 320), dtype=np.float32) * rng.uniform(0.01, 100, (64, 1)).astype(
+        np.float32)
+    rows = W.per_token_int4_rows(x)
+    assert rows.shape == (64, 160 + 16)
+    dec = O.decode_kv(rows, "int4_per_token", 1.0)
+    amax = np.abs(x).max(axis=1).astype(np.float64)
+    step = amax / 7.0
+    assert np.all(np.abs(np.abs(dec).max(axis=1) - amax) <= amax * 2.0 ** -22)
+    assert np.all(np.abs(dec - x) <= step[:, None] * (0.5 + 2.0 ** -20))
+
+
+@pytest.mark.parametrize("D", [576, 320])
+def test_int4_cache_matches_torch_sdpa(D):
+    inp = W.small_case(seed=73, batch=3, num_heads=16, head_size=D, kv_lora_rank=D - 64,
+                       page_size=16, seq_lens=(37, 100, 1), kv_dtype=W.INT4_PER_TOKEN)
+    w = inp.workload
+    o, lse = run(inp)
+    sc = float(np.float32(w.scale))
+    for b in range(3):
+        K = dense_keys(inp, b)
+        q = q_of(inp, b)
+        ref = torch.nn.functional.scaled_dot_product_attention(q[None], K[None],
+                                                               K[None, :, :D - 64], scale=sc)[0]
+        ref_lse = torch.logsumexp((q @ K.T) * sc, dim=1)
+        assert np.abs(o[b] - ref.numpy()).max() < 1e-12
+        assert np.abs(lse[b] - ref_lse.numpy()).max() < 1e-12
+
+
+def test_planted_int4_mistakes_are_caught(monkeypatch):
+    """Swapping the nibble order, or reading the nibbles unsigned, fails the
+    SDPA pin."""
+    real = OM.int4_bits_to_f64
+
+    def swapped(packed):
+        v = real(packed)
+        out = v.copy()
+        out[..., 0::2], out[..., 1::2] = v[..., 1::2], v[..., 0::2]
+        return out
+
+    def unsigned(packed):
+        b = np.asarray(packed, dtype=np.uint8)
+        out = np.empty(b.shape[:-1] + (2 * b.shape[-1],))
+        out[..., 0::2] = b & 15
+        out[..., 1::2] = b >> 4
+        return out
+
+    for fake in (swapped, unsigned):
+        monkeypatch.setattr(OM, "int4_bits_to_f64", fake)
+        with pytest.raises(AssertionError):
+            test_int4_cache_matches_torch_sdpa(576)
+        monkeypatch.undo()

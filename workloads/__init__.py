@@ -31,6 +31,7 @@ FP8_E4M3 = "fp8_e4m3"
 # bytes], scale = max|row| / 448 of the token's fp32 row
 FP8_PER_TOKEN = "fp8_per_token"
 INT8_PER_TOKEN = "int8_per_token"
+INT4_PER_TOKEN = "int4_per_token"
 PER_TOKEN_PAD = 16
 
 # fp32(192 ** -0.5): the softmax scale of a DeepSeek-V3 style head
@@ -124,6 +125,12 @@ WORKLOADS: Dict[str, Workload] = {
             scale=DSV3_SCALE, seq_len_range=(1024, 8192), parity_splits=(16, 1),
             description="B=64 H=128 D=576/512 per-token int8 cache (inline fp32 scale, rows of "
                         "592 B), page 64, 8192 pages, seq_lens U[1024,8192]"),
+        Workload(
+            name="int4_pt", seed=10, batch=64, num_heads=128, head_size=576, kv_lora_rank=512,
+            page_size=64, num_blocks=8192, kv_dtype=INT4_PER_TOKEN, k_scale=1.0,
+            scale=DSV3_SCALE, seq_len_range=(1024, 8192), parity_splits=(16, 1),
+            description="B=64 H=128 D=576/512 per-token int4 cache (two codes per byte, inline "
+                        "fp32 scale, rows of 304 B), page 64, 8192 pages, seq_lens U[1024,8192]"),
     ]
 }
 
@@ -185,6 +192,22 @@ def per_token_int8_rows(pool: np.ndarray) -> np.ndarray:
     return out
 
 
+def per_token_int4_rows(pool: np.ndarray) -> np.ndarray:
+    """fp32 rows [..., D] -> per-token quantised rows [..., D/2 + 16] bytes:
+    4-bit codes round(row / s) in [-7, 7], two per byte (element 2i in the low
+    nibble), then s as fp32, then zeros, with s = fp32(max|row| / 7) (1 for an
+    all-zero row)."""
+    amax = np.abs(pool).max(axis=-1, keepdims=True).astype(np.float32)
+    s = np.where(amax > 0, amax / np.float32(7.0), np.float32(1.0)).astype(np.float32)
+    codes = np.clip(np.rint(pool / s), -7, 7).astype(np.int16) & 0x0F
+    D = pool.shape[-1]
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    out = np.zeros(pool.shape[:-1] + (D // 2 + PER_TOKEN_PAD,), dtype=np.uint8)
+    out[..., :D // 2] = packed
+    out[..., D // 2:D // 2 + 4] = s.view(np.uint8)
+    return out
+
+
 def make_block_table(rng: np.random.Generator, seq_lens: np.ndarray, page_size: int,
                      num_blocks: int) -> np.ndarray:
     """Each sequence takes the next ceil(n/P) pages of one seeded permutation
@@ -240,6 +263,8 @@ def generate(workload: Workload | str, *, seq_lens: Optional[Sequence[int]] = No
         kv_bits = per_token_fp8_rows(pool)
     elif w.kv_dtype == INT8_PER_TOKEN:
         kv_bits = per_token_int8_rows(pool)
+    elif w.kv_dtype == INT4_PER_TOKEN:
+        kv_bits = per_token_int4_rows(pool)
     else:
         kv_bits = f32_to_e4m3fn_bits(pool / np.float32(w.k_scale))
     inp = DecodeInputs(workload=w, q_bits=q_bits, kv_bits=kv_bits, block_table=table,
@@ -294,7 +319,9 @@ def poison_unreferenced(inp: DecodeInputs, *, poison_table: bool = True) -> Deco
     used = referenced_slots(inp)
     kv = inp.kv_bits.copy()
     nan = np.uint16(0x7FC0) if inp.kv_dtype == BF16 else np.uint8(0x7F)
-    kv[~used] = nan  # per-token rows: NaN codes and a NaN scale (0x7F7F7F7F)
+    # per-token rows get bytes 0x7F: NaN fp8 codes, int8 code 127 or int4 codes (-1, 7), and
+    # a scale of about 3.4e38, so that any read of them wrecks the result
+    kv[~used] = nan
     table = inp.block_table.copy()
     if poison_table:
         free_pages = np.nonzero(~used.any(axis=1))[0]
