@@ -62,9 +62,11 @@ def algorithmic(inp):
     w = inp.workload
     n = np.asarray(inp.seq_lens, dtype=np.int64)
     B, H, D, DV, P = w.batch, w.num_heads, w.head_size, w.kv_lora_rank, w.page_size
-    # bytes of one cache row the method needs: bf16 values, fp8 codes, or fp8
-    # codes and the token's fp32 scale (the rest of the per-token pad is unused)
-    row = {"bf16": 2 * D, "fp8_per_token": D + 4, "int8_per_token": D + 4}.get(w.kv_dtype, D)
+    # bytes of one cache row the method needs: bf16 values, fp8 codes, or the
+    # per-token codes (fp8, int8: D bytes; int4: D/2) and the token's fp32 scale
+    # (the rest of the per-token pad is unused)
+    row = {"bf16": 2 * D, "fp8_per_token": D + 4, "int8_per_token": D + 4,
+           "int4_per_token": D // 2 + 4}.get(w.kv_dtype, D)
     ql = w.q_len
     if w.topk:
         # sparse decode: the selected rows, the index lists and one table entry each
@@ -381,7 +383,7 @@ def main():
     q = torch.from_numpy(inp.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     if w.kv_dtype == "bf16":
         kv = torch.from_numpy(inp.kv_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    elif w.kv_dtype in ("fp8_per_token", "int8_per_token"):
+    elif w.kv_dtype in ("fp8_per_token", "int8_per_token", "int4_per_token"):
         kv = torch.from_numpy(inp.kv_bits).to(dev)  # uint8 rows: codes | fp32 scale | pad
     else:
         kv = torch.from_numpy(inp.kv_bits).view(torch.float8_e4m3fn).to(dev)

@@ -93,7 +93,14 @@ typedef enum mla_dtype {
   /* Cache only: as MLA_FP8_E4M3_PER_TOKEN with signed (two's-complement)
    * int8 codes; value = code * scale (the same page lists int8 among the
    * per-token-head modes). */
-  MLA_INT8_PER_TOKEN = 4
+  MLA_INT8_PER_TOKEN = 4,
+  /* Cache only: two signed (two's-complement) 4-bit codes per byte, element
+   * 2i in the low nibble and 2i+1 in the high nibble of byte i; a row is
+   * head_size / 2 code bytes followed by the MLA_PER_TOKEN_PAD-byte pad with
+   * the token's float32 scale; value = code * scale (the same page lists
+   * int4 among the per-token-head modes).  Rows start on 16-byte boundaries
+   * (head_size / 2 + 16 is a multiple of 16). */
+  MLA_INT4_PER_TOKEN = 5
 } mla_dtype;
 
 #define MLA_PER_TOKEN_PAD 16 /* bytes after the codes of a per-token cache row */
@@ -132,7 +139,8 @@ typedef enum mla_split_mode {
  *   q           [batch, num_heads, head_size]              q_dtype (bf16)
  *   kv_cache    [num_blocks, page_size, head_size]         kv_dtype; row =
  *               [kv_c (kv_lora_rank) | k_pe (64)]; per-token caches are
- *               [num_blocks, page_size, head_size + MLA_PER_TOKEN_PAD] bytes
+ *               [num_blocks, page_size, C + MLA_PER_TOKEN_PAD] bytes,
+ *               C = head_size (fp8, int8 codes) or head_size / 2 (int4)
  *   block_table [batch, max_blocks_per_seq]                int32; entries at
  *               index >= ceil(seq_lens[b] / page_size) are never read
  *   seq_lens    [batch]                                    int32, >= 0
@@ -149,7 +157,8 @@ typedef struct mla_shape {
   int32_t max_blocks_per_seq; /* block_table row stride in entries, >= 1    */
   int32_t q_dtype;            /* mla_dtype: MLA_BF16                        */
   int32_t kv_dtype;           /* mla_dtype: MLA_BF16, MLA_FP8_E4M3,
-                                 MLA_FP8_E4M3_PER_TOKEN or MLA_INT8_PER_TOKEN */
+                                 MLA_FP8_E4M3_PER_TOKEN, MLA_INT8_PER_TOKEN
+                                 or MLA_INT4_PER_TOKEN */
   int32_t o_dtype;            /* mla_dtype: MLA_BF16 or MLA_FP32            */
 } mla_shape;
 

@@ -30,12 +30,14 @@ __all__ = [
     "MlaError", "mla_decode", "mla_decode_sparse", "mla_plan", "mla_workspace_size", "mla_pages_split_count",
     "mla_status_string", "SPLIT_PER_SEQUENCE", "SPLIT_BALANCED", "library_path", "load_library",
     "MLA_BF16", "MLA_FP8_E4M3", "MLA_FP32", "MLA_FP8_E4M3_PER_TOKEN", "MLA_INT8_PER_TOKEN",
+    "MLA_INT4_PER_TOKEN",
     "MLA_PER_TOKEN_PAD", "mla_merge_shards", "MLA_LSE_LN", "MLA_LSE_LOG2",
 ]
 
 MLA_OK, MLA_ERR_NULL, MLA_ERR_HEAD_SIZE, MLA_ERR_PAGE_SIZE, MLA_ERR_DTYPE = 0, 1, 2, 3, 4
 MLA_ERR_SHAPE, MLA_ERR_SPLITS, MLA_ERR_WORKSPACE, MLA_ERR_LAUNCH, MLA_ERR_ARGUMENT = 5, 6, 7, 8, 9
 MLA_BF16, MLA_FP8_E4M3, MLA_FP32, MLA_FP8_E4M3_PER_TOKEN, MLA_INT8_PER_TOKEN = 0, 1, 2, 3, 4
+MLA_INT4_PER_TOKEN = 5  # two signed 4-bit codes per byte, element 2i in the low nibble
 MLA_PER_TOKEN_PAD = 16  # bytes after the codes of a per-token cache row (fp32 scale first)
 SPLIT_PER_SEQUENCE, SPLIT_BALANCED = 0, 1
 MLA_LSE_LN, MLA_LSE_LOG2 = 0, 1
@@ -155,14 +157,15 @@ def _torch():
 
 def _kv_code(kv_cache, kv_dtype):
     """Cache dtype code: from ``kv_dtype`` ("bf16", "fp8_e4m3", "fp8_per_token",
-    "int8_per_token" or an mla_dtype value) or else from the tensor's dtype.  A per-token cache
-    is a uint8 tensor [num_blocks, page, head_size + MLA_PER_TOKEN_PAD] and
-    must be named explicitly."""
+    "int8_per_token", "int4_per_token" or an mla_dtype value) or else from the tensor's dtype.
+    A per-token cache is a uint8 tensor [num_blocks, page, C + MLA_PER_TOKEN_PAD] (C = head_size
+    code bytes, head_size / 2 for int4) and must be named explicitly."""
     torch = _torch()
     if kv_dtype is not None:
         return {"bf16": MLA_BF16, "fp8_e4m3": MLA_FP8_E4M3,
                 "fp8_per_token": MLA_FP8_E4M3_PER_TOKEN,
-                "int8_per_token": MLA_INT8_PER_TOKEN}.get(kv_dtype, kv_dtype)
+                "int8_per_token": MLA_INT8_PER_TOKEN,
+                "int4_per_token": MLA_INT4_PER_TOKEN}.get(kv_dtype, kv_dtype)
     if kv_cache.dtype == torch.bfloat16:
         return MLA_BF16
     if kv_cache.dtype == torch.float8_e4m3fn:
@@ -184,8 +187,8 @@ def shape_of(q, kv_cache, block_table, *, kv_dtype=None, o_dtype=None) -> MlaSha
                          "block_table [B,W]")
     B, H, D = q.shape[0], q.shape[-2], q.shape[-1]
     code = _kv_code(kv_cache, kv_dtype)
-    per_token = code in (MLA_FP8_E4M3_PER_TOKEN, MLA_INT8_PER_TOKEN)
-    width = D + MLA_PER_TOKEN_PAD if per_token else D
+    per_token = code in (MLA_FP8_E4M3_PER_TOKEN, MLA_INT8_PER_TOKEN, MLA_INT4_PER_TOKEN)
+    width = ((D // 2 if code == MLA_INT4_PER_TOKEN else D) + MLA_PER_TOKEN_PAD) if per_token else D
     if kv_cache.shape[-1] != width:
         raise ValueError(f"kv_cache rows hold {kv_cache.shape[-1]} elements, expected {width}")
     if kv_cache.element_size() != (2 if code == MLA_BF16 else 1):

@@ -5,7 +5,7 @@ library is missing.  The library is a plain C-ABI shared object (no torch
 types), loaded by the ctypes binding in this package.
 
 The stage-1 kernel source is compiled once per group of template instances
-(MLA_STAGE1_GROUP 0..7) and once for the rest (MLA_MAIN); the translation
+(MLA_STAGE1_GROUP 0..9) and once for the rest (MLA_MAIN); the translation
 units build in parallel and are linked into one library.
 """
 from __future__ import annotations
@@ -26,7 +26,7 @@ KERNELS = os.path.join(CSRC, "mla_kernels.hip")
 # (source, extra defines) of every translation unit
 UNITS = ([(os.path.join(CSRC, "mla_api.cpp"), []), (os.path.join(CSRC, "mla_merge.hip"), []),
           (KERNELS, ["-DMLA_MAIN"])] +
-         [(KERNELS, [f"-DMLA_STAGE1_GROUP={g}"]) for g in range(8)])
+         [(KERNELS, [f"-DMLA_STAGE1_GROUP={g}"]) for g in range(10)])
 SOURCES = sorted({u[0] for u in UNITS})
 ARCH = "gfx950"
 

@@ -46,12 +46,26 @@ HeadTiling head_tiling(int32_t heads) {
   return t;
 }
 
+// Per-token cache kind of a dtype: 0 none, 1 e4m3fn, 2 int8, 3 int4 codes.
+static int per_token_kind(int32_t kv_dtype) {
+  return kv_dtype == MLA_FP8_E4M3_PER_TOKEN ? 1
+         : kv_dtype == MLA_INT8_PER_TOKEN   ? 2
+         : kv_dtype == MLA_INT4_PER_TOKEN   ? 3
+                                            : 0;
+}
+
+// Bytes of one cache row (one token).
+static uint64_t kv_row_bytes(const mla_shape& s) {
+  const int pt = per_token_kind(s.kv_dtype);
+  if (pt) return (uint64_t)(pt == 3 ? s.head_size / 2 : s.head_size) + MLA_PER_TOKEN_PAD;
+  return (uint64_t)s.head_size * (s.kv_dtype == MLA_BF16 ? 2 : 1);
+}
+
 // LDS bytes of one stage-1 workgroup (the same plan the kernel dispatch uses).
 static int64_t stage1_lds(const mla_shape& s) {
   const HeadTiling t = head_tiling(s.num_heads);
-  return stage1_lds_bytes(t.heads_per_wave, t.waves, s.head_size,
-                          s.kv_dtype != MLA_BF16,
-                          s.kv_dtype == MLA_FP8_E4M3_PER_TOKEN || s.kv_dtype == MLA_INT8_PER_TOKEN);
+  return stage1_lds_bytes(t.heads_per_wave, t.waves, s.head_size, s.kv_dtype != MLA_BF16,
+                          per_token_kind(s.kv_dtype));
 }
 
 }  // namespace mla
@@ -65,8 +79,7 @@ static mla_status check_shape(const mla_shape* s) {
     return MLA_ERR_HEAD_SIZE;
   if (s->page_size <= 0 || s->page_size % 16 != 0) return MLA_ERR_PAGE_SIZE;
   if (s->q_dtype != MLA_BF16) return MLA_ERR_DTYPE;
-  if (s->kv_dtype != MLA_BF16 && s->kv_dtype != MLA_FP8_E4M3 &&
-      s->kv_dtype != MLA_FP8_E4M3_PER_TOKEN && s->kv_dtype != MLA_INT8_PER_TOKEN)
+  if (s->kv_dtype != MLA_BF16 && s->kv_dtype != MLA_FP8_E4M3 && !per_token_kind(s->kv_dtype))
     return MLA_ERR_DTYPE;
   if (s->o_dtype != MLA_BF16 && s->o_dtype != MLA_FP32) return MLA_ERR_DTYPE;
   if (s->batch < 1 || s->num_heads < 16 || s->num_heads % 16 != 0 || s->num_blocks < 1 ||
@@ -187,8 +200,7 @@ static mla_status decode_stages(const mla_shape* shape, int32_t q_len, const voi
     return MLA_ERR_SPLITS;
   if (!(isfinite(scale) && scale > 0.f)) return MLA_ERR_ARGUMENT;
   const bool fp8 = shape->kv_dtype != MLA_BF16;
-  const bool per_token =
-      shape->kv_dtype == MLA_FP8_E4M3_PER_TOKEN || shape->kv_dtype == MLA_INT8_PER_TOKEN;
+  const bool per_token = per_token_kind(shape->kv_dtype) != 0;
   if (fp8 && !per_token && !(isfinite(k_scale) && k_scale > 0.f)) return MLA_ERR_ARGUMENT;
   if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
       !aligned(block_table, 4) || !aligned(seq_lens, 4))
@@ -218,17 +230,13 @@ static mla_status decode_stages(const mla_shape* shape, int32_t q_len, const voi
   a.page_size = shape->page_size;
   a.bt_stride = shape->max_blocks_per_seq;
   a.kv_fp8 = fp8 ? 1 : 0;
-  a.kv_pt = shape->kv_dtype == MLA_FP8_E4M3_PER_TOKEN ? 1
-            : shape->kv_dtype == MLA_INT8_PER_TOKEN   ? 2
-                                                      : 0;
+  a.kv_pt = per_token_kind(shape->kv_dtype);
   a.o_f32 = shape->o_dtype == MLA_FP32 ? 1 : 0;
   a.split_mode = split_mode;
   a.num_splits = num_kv_splits;
   a.scale = scale;
   a.k_scale = k_scale;
-  a.pool_bytes = (uint64_t)shape->num_blocks * shape->page_size *
-                 (per_token ? shape->head_size + MLA_PER_TOKEN_PAD
-                            : shape->head_size * (fp8 ? 1 : 2));
+  a.pool_bytes = (uint64_t)shape->num_blocks * shape->page_size * kv_row_bytes(*shape);
   if (topk_idx) {
     a.topk_idx = topk_idx;
     a.topk_stride = topk;
@@ -303,11 +311,7 @@ static mla_status check_sparse(const mla_shape* shape, int32_t topk, const int32
   if (st != MLA_OK) return st;
   if (!topk_indices || !topk_lens) return MLA_ERR_NULL;
   if (topk < 1) return MLA_ERR_ARGUMENT;
-  const bool per_token =
-      shape->kv_dtype == MLA_FP8_E4M3_PER_TOKEN || shape->kv_dtype == MLA_INT8_PER_TOKEN;
-  const uint64_t row = per_token ? shape->head_size + MLA_PER_TOKEN_PAD
-                                 : (uint64_t)shape->head_size * (shape->kv_dtype == MLA_BF16 ? 2 : 1);
-  const uint64_t pool = (uint64_t)shape->num_blocks * shape->page_size * row;
+  const uint64_t pool = (uint64_t)shape->num_blocks * shape->page_size * kv_row_bytes(*shape);
   if (pool + 65536 >= ((uint64_t)1 << 32)) return MLA_ERR_SHAPE;
   if (!aligned(topk_indices, 4)) return MLA_ERR_ARGUMENT;
   return MLA_OK;

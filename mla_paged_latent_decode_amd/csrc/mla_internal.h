@@ -49,7 +49,11 @@ constexpr int kLdsBytes = 160 * 1024;
 // the plain fp8 loop with a ring of 2 and keep each tile's 32 scales in LDS:
 // two staging slots of 2 x 256 B and a ring of 128 B slots.
 constexpr int kPerTokenPad = 16;
-constexpr int stage1_ring_depth(int hpw, int waves, int d, bool fp8, bool pt = false) {
+// pt (per-token rows): 0 none, 1 e4m3fn codes, 2 int8 codes, 3 int4 codes
+constexpr int stage1_code_bytes(int d, bool fp8, int pt) {
+  return pt == 3 ? d / 2 : (fp8 ? d : 2 * d);
+}
+constexpr int stage1_ring_depth(int hpw, int waves, int d, bool fp8, int pt = 0) {
   if (pt) return 2;
   if (fp8) return (hpw == 32 && waves == 4) ? 3 : 2;
   if (d != 576) return 4;
@@ -58,19 +62,23 @@ constexpr int stage1_ring_depth(int hpw, int waves, int d, bool fp8, bool pt = f
   if (hpw == 32) return waves == 4 ? 3 : (waves == 2 ? 3 : 2);
   return waves == 4 ? 4 : 2;
 }
-constexpr int stage1_staging_bytes(int d, bool fp8) { return fp8 ? 2 * kTile * d : 0; }
-constexpr int stage1_scale_bytes(int hpw, int waves, int d, bool fp8, bool pt) {
-  return pt ? 2 * 512 + stage1_ring_depth(hpw, waves, d, fp8, pt) * 128 : 0;
+constexpr int stage1_staging_bytes(int d, bool fp8, int pt) {
+  return fp8 ? 2 * kTile * stage1_code_bytes(d, fp8, pt) : 0;
 }
-constexpr int stage1_qlds_steps(int hpw, int waves, int d, bool fp8, bool pt = false) {
+constexpr int stage1_scale_bytes(int hpw, int waves, int d, bool fp8, int pt) {
+  // two staging slots of 2 x 256 B; per ring slot the 32 scales and their reciprocals
+  return pt ? 2 * 512 + stage1_ring_depth(hpw, waves, d, fp8, pt) * 256 : 0;
+}
+constexpr int stage1_qlds_steps(int hpw, int waves, int d, bool fp8, int pt = 0) {
   if (!(hpw == 32 && d == 576)) return 0;
   const int room = (kLdsBytes - stage1_ring_depth(hpw, waves, d, fp8, pt) * kTile * d * 2 -
-                    stage1_staging_bytes(d, fp8) - stage1_scale_bytes(hpw, waves, d, fp8, pt)) /
+                    stage1_staging_bytes(d, fp8, pt) - stage1_scale_bytes(hpw, waves, d, fp8, pt)) /
                    (waves * 1024);
   return room < 12 ? room : 12;
 }
-constexpr int stage1_lds_bytes(int hpw, int waves, int d, bool fp8, bool pt = false) {
-  return stage1_ring_depth(hpw, waves, d, fp8, pt) * kTile * d * 2 + stage1_staging_bytes(d, fp8) +
+constexpr int stage1_lds_bytes(int hpw, int waves, int d, bool fp8, int pt = 0) {
+  return stage1_ring_depth(hpw, waves, d, fp8, pt) * kTile * d * 2 +
+         stage1_staging_bytes(d, fp8, pt) +
          stage1_qlds_steps(hpw, waves, d, fp8, pt) * waves * 1024 +
          stage1_scale_bytes(hpw, waves, d, fp8, pt);
 }
@@ -93,7 +101,7 @@ struct DecodeArgs {
   int32_t page_size;
   int32_t bt_stride;
   int32_t kv_fp8;
-  int32_t kv_pt;  // per-token rows (D codes + an inline fp32 scale): 1 e4m3fn, 2 int8
+  int32_t kv_pt;  // per-token rows (codes + an inline fp32 scale): 1 e4m3fn, 2 int8, 3 int4
   int32_t o_f32;
   int32_t split_mode;
   int32_t num_splits;

@@ -179,6 +179,19 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 v) {
   return r;
 }
 
+// Eight signed int4 codes (element 2i in the low nibble of byte i, 2i+1 in
+// its high nibble) to eight bf16: every value in [-8, 7] is exact in bf16.
+__device__ __forceinline__ u32x4 i4x8_to_bf16x8(uint32_t v) {
+  u32x4 r;
+  const int x = (int)v;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x2 e = {(float)((x << (28 - 8 * k)) >> 28), (float)((x << (24 - 8 * k)) >> 28)};
+    r[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(e, bf16x2));
+  }
+  return r;
+}
+
 // Eight signed int8 codes (one per byte, lowest byte first) to eight bf16:
 // every value in [-128, 127] is exact in bf16.
 __device__ __forceinline__ u32x4 i8x8_to_bf16x8(u32x2 v) {
@@ -322,7 +335,8 @@ __device__ __forceinline__ int64_t total_cost(const int32_t* seq_lens, int B, in
 
 // ---------------------------------------------------------------- stage 1
 
-// PT: 0 = no per-token scales, 1 = per-token e4m3fn codes, 2 = per-token int8 codes
+// PT: 0 = no per-token scales, 1 = per-token e4m3fn codes, 2 = per-token int8
+// codes, 3 = per-token int4 codes (two per byte)
 template <int HPW, int W, int D, int DV, int NBUF, bool F8, int PT = 0>
 struct Cfg {
   static constexpr int NKQ = D / 32;                       // 32-wide d groups per row
@@ -338,16 +352,19 @@ struct Cfg {
   static constexpr int TILE_BYTES = NBLK * 1024;
   static constexpr int NVB = HPW == 32 ? DV / 32 : DV / 16;  // PV output blocks
   static constexpr int HEADS_PER_WG = HPW * W;
-  static constexpr int SRC_ROW = F8 ? (PT ? D + kPerTokenPad : D) : 2 * D;  // cache row bytes
-  // fp8: a 16-row half tile (16*D contiguous bytes of one page) is copied to
-  // a staging tile with G-byte LDS DMA per lane (consecutive lanes write
-  // consecutive G bytes), G = 16 when every wave then issues the same number
-  // of copies, else 4; bf16: one 16-byte copy per lane and block.
+  static constexpr int CB = stage1_code_bytes(D, F8, PT);      // code bytes of a cache row
+  static constexpr int SRC_ROW = PT ? CB + kPerTokenPad : CB;  // cache row bytes
+  // 1-byte and 4-bit codes: a 16-row half tile (16*CB code bytes of one
+  // page) is copied to a row-major staging tile with G-byte LDS DMA per lane
+  // (consecutive lanes write consecutive G bytes), G = 16 when every wave
+  // then issues the same number of copies, else 4; bf16: one 16-byte copy
+  // per lane and block.
   static constexpr int G =
-      !F8 ? 16 : ((16 * D) % 1024 == 0 && (2 * 16 * D / 1024) % W == 0) ? 16 : 4;
-  static constexpr int NIH = F8 ? 16 * D / (64 * G) : NKQ;  // DMA copies per half tile
-  static constexpr int NIW = 2 * NIH / W;                   // DMA copies per wave per tile
-  static constexpr int STG_TILE = F8 ? kTile * D : 0;       // fp8 staging tile bytes
+      !F8 ? 16 : ((16 * CB) % 1024 == 0 && (2 * 16 * CB / 1024) % W == 0) ? 16 : 4;
+  static constexpr int NIH = F8 ? 16 * CB / (64 * G) : NKQ;  // DMA copies per half tile
+  static constexpr int NIW = 2 * NIH / W;                    // DMA copies per wave per tile
+  static constexpr int STG_TILE = F8 ? kTile * CB : 0;       // staging tile bytes
+  static constexpr int CVB = PT == 3 ? 4 : 8;                // code bytes of 8 elements
   static constexpr int STG_BYTES = 2 * STG_TILE;
   static constexpr int SCL_BYTES = stage1_scale_bytes(HPW, W, D, F8, PT);
   // Pipelined bf16 loop: the k-th of a wave's NIW tile loads goes out at step
@@ -369,10 +386,11 @@ struct Cfg {
   // spread a tile's loads over two iterations.
   static constexpr bool PIPE = HPW == 32 && !F8 && NBUF >= 4;
   static_assert(NBUF == stage1_ring_depth(HPW, W, D, F8, PT), "ring depth");
-  static_assert(!PT || F8, "per-token rows hold 1-byte codes (e4m3fn or int8)");
+  static_assert(!PT || F8, "per-token rows hold narrow codes (e4m3fn, int8 or int4)");
+  static_assert(!PT || CB % G == 0, "a copy never straddles a row's scale pad");
   static_assert(NBLK * 1024 == kTile * D * 2, "tile bytes");
   static_assert(NBLK % W == 0, "each wave loads or widens the same number of blocks");
-  static_assert(!F8 || ((16 * D) % (64 * G) == 0 && (2 * NIH) % W == 0), "fp8 copy split");
+  static_assert(!F8 || ((16 * CB) % (64 * G) == 0 && (2 * NIH) % W == 0), "narrow copy split");
   static_assert(F8 ? NIW <= 63 : (NBUF - 1) * LPW <= 63,
                 "outstanding loads must fit the vmcnt counter");
   static_assert(NBUF * TILE_BYTES + STG_BYTES + QLDS_BYTES + SCL_BYTES <= kLdsBytes, "LDS budget");
@@ -394,7 +412,8 @@ template <int HPW, int W, int D, int DV, int NBUF, bool F8, bool SP, int PT>
 __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   using C = Cfg<HPW, W, D, DV, NBUF, F8, PT>;
   // [bf16 ring: NBUF tiles][fp8 staging: 2 tiles][Q k-steps of each wave]
-  // [per-token scales: 2 staging slots of 2 x 256 B, NBUF ring slots of 128 B]
+  // [per-token scales: 2 staging slots of 2 x 256 B, NBUF ring slots of 256 B
+  //  (32 scales, then their reciprocals)]
   __shared__ __attribute__((aligned(1024)))
   uint8_t ring[NBUF * C::TILE_BYTES + C::STG_BYTES + C::QLDS_BYTES + C::SCL_BYTES];
   uint8_t* const stg = ring + NBUF * C::TILE_BYTES;
@@ -430,7 +449,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   // fp8 widening: lane l converts chunk c4 = l % 4 of position t16 = l / 4
   // of a block, read from the row-major staging tile and written to the
   // chunk's slot of the bf16 tile layout
-  const uint32_t cv_src = (uint32_t)((lane >> 2) * D + 8 * (lane & 3));
+  const uint32_t cv_src = (uint32_t)((lane >> 2) * C::CB + C::CVB * (lane & 3));
   const uint32_t cv_dst = (uint32_t)(tile_slot(lane >> 2, lane & 3) * 16);
   int qk_off_e, qk_off_o, v_off0, v_off1;
   if constexpr (HPW == 32) {
@@ -584,10 +603,10 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           // slot; lane t < 16 holds the offset of row t of the half
           // (dma_t16 = lane there), read here with a lane shuffle
           const int c = C::G * lane + sgpr_here(r * 64 * C::G);  // code byte in the half
-          const int row = c / D;
+          const int row = c / C::CB;
           const uint32_t roff = (uint32_t)__shfl((int)(th ? tl.off[1] : tl.off[0]), row, 64);
-          LDS_AS void* dst = (LDS_AS void*)(tl.dst + th * 16 * D + r * 64 * C::G);
-          const int voff = (int)(roff + (uint32_t)(c - row * D));
+          LDS_AS void* dst = (LDS_AS void*)(tl.dst + th * 16 * C::CB + r * 64 * C::G);
+          const int voff = (int)(roff + (uint32_t)(c - row * C::CB));
           if constexpr (C::G == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, 0, 0, 0);
           else __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, voff, 0, 0, 0);
           if constexpr (PT) {
@@ -596,7 +615,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
               // (rows past the segment, and lanes >= 16, read 0)
 #pragma unroll
               for (int h2 = 0; h2 < 2; ++h2) {
-                const int soff = lane < 16 ? (int)((h2 ? tl.off[1] : tl.off[0]) + D)
+                const int soff = lane < 16 ? (int)((h2 ? tl.off[1] : tl.off[0]) + C::CB)
                                            : (int)p.pool_bytes;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rs, (LDS_AS uint8_t*)ring + kSclOff + tl.sslot * 512 + h2 * 256, 4, soff,
@@ -616,14 +635,14 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           (void*)(th ? tl.base[1] : tl.base[0]), (short)0, th ? tl.bytes[1] : tl.bytes[0],
           0x00020000);
       if constexpr (F8) {
-        LDS_AS void* dst = (LDS_AS void*)(tl.dst + th * 16 * D + r * 64 * C::G);
+        LDS_AS void* dst = (LDS_AS void*)(tl.dst + th * 16 * C::CB + r * 64 * C::G);
         int voff;
         if constexpr (PT) {
           // the codes of a half tile are contiguous in staging, but in the
           // cache each row is followed by its 16-byte scale pad
           // (formed here from an SGPR constant, not hoisted into a VGPR per copy)
           const uint32_t c = (uint32_t)(C::G * lane) + (uint32_t)sgpr_here(r * 64 * C::G);
-          voff = (int)(c + (c / D) * kPerTokenPad);  // c: code byte within the half tile
+          voff = (int)(c + (c / C::CB) * kPerTokenPad);  // c: code byte within the half tile
           if (k == 0 && wave == 0) {
             // the 16 inline scales of each half: lane l < 16 reads row l's
             // scale into slot l of a 256-byte area; rows past the segment
@@ -632,7 +651,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
             for (int h2 = 0; h2 < 2; ++h2) {
               const __amdgpu_buffer_rsrc_t rsh = __builtin_amdgcn_make_buffer_rsrc(
                   (void*)tl.base[h2], (short)0, tl.bytes[h2], 0x00020000);
-              const int soff = lane < 16 ? lane * C::SRC_ROW + D : tl.bytes[h2];
+              const int soff = lane < 16 ? lane * C::SRC_ROW + C::CB : tl.bytes[h2];
               __builtin_amdgcn_raw_ptr_buffer_load_lds(
                   rsh, (LDS_AS uint8_t*)ring + kSclOff + tl.sslot * 512 + h2 * 256, 4, soff, 0, 0,
                   0);
@@ -660,7 +679,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       const int j = wave + k * W;
       const int th = j >= C::NKQ ? 1 : 0;
       return cv_src + (uint32_t)sgpr_here((int)(uint32_t)(uintptr_t)stg + (x & 1) * C::STG_TILE +
-                                          th * 16 * D + 32 * (j - th * C::NKQ));
+                                          th * 16 * C::CB + 4 * C::CVB * (j - th * C::NKQ));
     };
     auto widen_dst = [&](int x, int k) __attribute__((always_inline)) {
       return cv_dst + (uint32_t)sgpr_here((int)(uint32_t)(uintptr_t)ring +
@@ -671,32 +690,50 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       static_for<(C::LPW + 3) / 4>([&](auto bc) __attribute__((always_inline)) {
         constexpr int k0 = 4 * decltype(bc)::value;
         constexpr int nb = C::LPW - k0 < 4 ? C::LPW - k0 : 4;
-        u32x2 v[nb];
+        // 8 code bytes per lane and block (4 for int4 codes)
+        using Raw = std::conditional_t<PT == 3, uint32_t, u32x2>;
+        Raw v[nb];
         static_for<nb>([&](auto ic) __attribute__((always_inline)) {
-          v[decltype(ic)::value] = ds_read_b64_asm(widen_src(x, k0 + decltype(ic)::value));
+          if constexpr (PT == 3)
+            v[decltype(ic)::value] = ds_read_b32_asm(widen_src(x, k0 + decltype(ic)::value));
+          else
+            v[decltype(ic)::value] = ds_read_b64_asm(widen_src(x, k0 + decltype(ic)::value));
         });
         static_for<nb>([&](auto ic) __attribute__((always_inline)) {
           constexpr int i = decltype(ic)::value;
           // issued after read i: the other nb-1-i reads and i writes
           lds_wait<nb - 1>(v[i]);
-          ds_write_b128_asm(widen_dst(x, k0 + i),
-                            PT == 2 ? i8x8_to_bf16x8(v[i]) : e4m3x8_to_bf16x8(v[i]));
+          if constexpr (PT == 3)
+            ds_write_b128_asm(widen_dst(x, k0 + i), i4x8_to_bf16x8(v[i]));
+          else
+            ds_write_b128_asm(widen_dst(x, k0 + i),
+                              PT == 2 ? i8x8_to_bf16x8(v[i]) : e4m3x8_to_bf16x8(v[i]));
         });
       });
       if constexpr (PT) {
         // the tile's 32 token scales: staging slot x % 2 (two 256-byte
-        // halves, row l of a half at float l) -> ring slot x % NBUF (float t)
+        // halves, row l of a half at float l) -> ring slot x % NBUF (float t),
+        // and their reciprocals 128 bytes further (0 where the scale is 0,
+        // subnormal or not finite)
         if (wave == 0 && lane < 32) {
           uint32_t sc = ds_read_b32_asm(scl_stage + (x & 1) * 512 + (lane >> 4) * 256 +
                                         (lane & 15) * 4);
           lds_wait<0>(sc);
-          ds_write_b32_asm(scl_ring + (x % NBUF) * 128 + lane * 4, sc);
+          const float s = __uint_as_float(sc);
+          const float as = __builtin_fabsf(s);
+          const float inv = (as >= 0x1p-126f && as <= 0x1.fffffep127f) ? 1.f / s : 0.f;
+          ds_write_b32_asm(scl_ring + (x % NBUF) * 256 + lane * 4, sc);
+          ds_write_b32_asm(scl_ring + (x % NBUF) * 256 + 128 + lane * 4, __float_as_uint(inv));
         }
       }
     };
-    // per-token scales of the four consecutive positions t .. t+3 of ring tile x
+    // per-token scales of the four consecutive positions t .. t+3 of ring
+    // tile x, and their reciprocals
     auto token_scales4 = [&](int x, int t) __attribute__((always_inline)) {
-      return ds_read_b128_asm(scl_ring + (x % NBUF) * 128 + t * 4);
+      return ds_read_b128_asm(scl_ring + (x % NBUF) * 256 + t * 4);
+    };
+    auto token_inv4 = [&](int x, int t) __attribute__((always_inline)) {
+      return ds_read_b128_asm(scl_ring + (x % NBUF) * 256 + 128 + t * 4);
     };
 
     // Q fragments of this wave's heads (B operand of S^T = K Q^T): the first
@@ -1062,6 +1099,46 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
             for (int r = 0; r < 4; ++r) x[4 * q + r] *= __uint_as_float(g[q][r]);
           });
         };
+        // Per-token caches: P V takes the weights w_t = bf16(p_t * scale_t)
+        // (x holds p_t on entry and w_t on return).  o is normalised by the
+        // sum of w_t / scale_t, formed as p_t + (w_t - p_t * scale_t) / scale_t,
+        // which is p_t itself where the scale is 0: o is then an exact convex
+        // combination of the cache rows with the weights the MFMA uses.
+        auto pt_weights = [&](f32x16& x) __attribute__((always_inline)) {
+          const int tl = 4 * (lane >> 5);
+          u32x4 g[4], h[4];
+          g[0] = token_scales4(i, tl);
+          h[0] = token_inv4(i, tl);
+          g[1] = token_scales4(i, 8 + tl);
+          h[1] = token_inv4(i, 8 + tl);
+          f32x4 racc = {};
+          static_for<4>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
+            // LDS reads complete in order: after h[q] only the pair of q + 1 is
+            // outstanding (none after the last pair)
+            lds_wait<q < 3 ? 2 : 0>(g[q]);
+            lds_wait<q < 3 ? 2 : 0>(h[q]);
+            f32x4 pv, sv, iv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              pv[r] = x[4 * q + r];
+              sv[r] = __uint_as_float(g[q][r]);
+              iv[r] = __uint_as_float(h[q][r]);
+            }
+            const f32x4 pw = pv * sv;
+            const f32x4 wq = __builtin_convertvector(__builtin_convertvector(pw, bf16x4), f32x4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              racc[r] += __builtin_fmaf(wq[r] - pw[r], iv[r], pv[r]);
+              x[4 * q + r] = wq[r];
+            }
+            if constexpr (q + 2 < 4) {
+              g[q + 2] = token_scales4(i, 8 * (q + 2) + tl);
+              h[q + 2] = token_inv4(i, 8 * (q + 2) + tl);
+            }
+          });
+          lr_part += (racc[0] + racc[1]) + (racc[2] + racc[3]);
+        };
         if constexpr (PT) scale_by_tokens(s);  // before the mask: zero rows have scale 0
         // mask past the segment and past the row's causal limit (multi-token decode)
         const int t0 = ts + i * kTile;
@@ -1098,18 +1175,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
                           (f32x8){pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]};
           l_part += ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
         }
-        if constexpr (PT) {
-          // per-token caches: the PV weights are bf16(p_t * scale_t) and o is
-          // normalised by the sum of the bf16(p_t), so a lone position gives
-          // its row exactly when its scale is exact in bf16
-          const f32x8 r01 =
-              __builtin_convertvector(__builtin_convertvector(
-                  (f32x8){pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]}, bf16x8), f32x8) +
-              __builtin_convertvector(__builtin_convertvector(
-                  (f32x8){pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]}, bf16x8), f32x8);
-          lr_part += ((r01[0] + r01[1]) + (r01[2] + r01[3])) + ((r01[4] + r01[5]) + (r01[6] + r01[7]));
-          scale_by_tokens(pr);
-        }
+        if constexpr (PT) pt_weights(pr);
         const bf16x8 p0 = __builtin_convertvector(
             (f32x8){pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]}, bf16x8);
         const bf16x8 p1 = __builtin_convertvector(
@@ -1211,13 +1277,29 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           pr[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.score_log2, -m_exp));
         }
         l_part += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-        {
-          // the sum of the bf16 weights normalises o (per-token caches: the
-          // weights of P V are bf16(p_t * scale_t), the sum that of bf16(p_t))
+        if constexpr (PT) {
+          // per-token caches: weights w_t = bf16(p_t * scale_t); o is
+          // normalised by the sum of p_t + (w_t - p_t * scale_t) / scale_t
+          // (= w_t / scale_t, and p_t where the scale is 0), as in 32-head waves
+          u32x4 h0 = token_inv4(i, 4 * (lane >> 4));
+          u32x4 h1 = token_inv4(i, 16 + 4 * (lane >> 4));
+          lds_wait<0>(h1);
+          lds_wait<0>(h0);
+          const f32x8 pw = pr * tsc;
+          const f32x8 wq = __builtin_convertvector(__builtin_convertvector(pw, bf16x8), f32x8);
+          f32x8 r;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            r[k] = __builtin_fmaf(wq[k] - pw[k], __uint_as_float(h0[k]), pr[k]);
+            r[4 + k] = __builtin_fmaf(wq[4 + k] - pw[4 + k], __uint_as_float(h1[k]), pr[4 + k]);
+          }
+          lr_part += ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
+          pr = wq;
+        } else {
+          // the sum of the bf16 weights the MFMA uses normalises o
           const f32x8 r = __builtin_convertvector(__builtin_convertvector(pr, bf16x8), f32x8);
           lr_part += ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
         }
-        if constexpr (PT) pr *= tsc;
         const bf16x8 pb = __builtin_convertvector(pr, bf16x8);
         {
           const uint32_t vbase0 = (uint32_t)(uintptr_t)tile + v_off0;
@@ -1628,8 +1710,8 @@ int launch_stage1_for(const HeadTiling& ht, const Stage1Params& sp, int grid, hi
 }  // namespace
 
 // The stage-1 launches of one group of variants.  This source is compiled
-// once per group (MLA_STAGE1_GROUP = 0..7: sparse gather or not x bf16,
-// per-tensor fp8, per-token fp8 or per-token int8 cache) and once with
+// once per group (MLA_STAGE1_GROUP = 0..9: sparse gather or not x bf16,
+// per-tensor fp8, per-token fp8, per-token int8 or per-token int4 cache) and once with
 // MLA_MAIN for the rest, so that the many template instances build in
 // parallel.
 #define MLA_CAT2(a, b) a##b
@@ -1645,13 +1727,16 @@ MLA_DECLARE_GROUP(4)
 MLA_DECLARE_GROUP(5)
 MLA_DECLARE_GROUP(6)
 MLA_DECLARE_GROUP(7)
+MLA_DECLARE_GROUP(8)
+MLA_DECLARE_GROUP(9)
 
 #ifdef MLA_STAGE1_GROUP
 int MLA_CAT(launch_stage1_group, MLA_STAGE1_GROUP)(int head_size, const HeadTiling& ht,
                                                    const Stage1Params& sp, int grid,
                                                    hipStream_t st) {
-  constexpr bool SP = MLA_STAGE1_GROUP >= 4;
-  constexpr int fmt = MLA_STAGE1_GROUP % 4;  // 0 bf16, 1 fp8 k_scale, 2 fp8 per token, 3 int8
+  constexpr bool SP = MLA_STAGE1_GROUP >= 5;
+  // 0 bf16, 1 fp8 with k_scale, per token: 2 fp8, 3 int8, 4 int4
+  constexpr int fmt = MLA_STAGE1_GROUP % 5;
   constexpr bool F8 = fmt != 0;
   constexpr int PT = fmt >= 2 ? fmt - 1 : 0;
   return head_size == 576 ? launch_stage1_for<576, 512, F8, PT, SP>(ht, sp, grid, st)
@@ -1709,9 +1794,9 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   const int units = a.split_mode == 0 ? a.batch * a.num_splits : a.num_splits;
   const int grid1 = (units + 7) / 8 * 8 * ht.head_chunks;
   if (stages & kStage1) {
-    // the group of variants: gather (+4) and cache format
+    // the group of variants: gather (+5) and cache format
     const int fmt = a.kv_pt ? 1 + a.kv_pt : (a.kv_fp8 ? 1 : 0);
-    const int group = (a.topk_idx ? 4 : 0) + fmt;
+    const int group = (a.topk_idx ? 5 : 0) + fmt;
     int err;
     switch (group) {
       case 0: err = launch_stage1_group0(a.head_size, ht, sp, grid1, st); break;
@@ -1721,7 +1806,9 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
       case 4: err = launch_stage1_group4(a.head_size, ht, sp, grid1, st); break;
       case 5: err = launch_stage1_group5(a.head_size, ht, sp, grid1, st); break;
       case 6: err = launch_stage1_group6(a.head_size, ht, sp, grid1, st); break;
-      default: err = launch_stage1_group7(a.head_size, ht, sp, grid1, st); break;
+      case 7: err = launch_stage1_group7(a.head_size, ht, sp, grid1, st); break;
+      case 8: err = launch_stage1_group8(a.head_size, ht, sp, grid1, st); break;
+      default: err = launch_stage1_group9(a.head_size, ht, sp, grid1, st); break;
     }
     if (err) return err;
   }

@@ -1,9 +1,10 @@
 """GPU parity of decode over per-token quantised caches: each row holds
-head_size codes (e4m3fn or signed int8) and its own float32 scale inline in a
-16-byte pad (Triton MLA page, key files: the per-token-head modes, fp8 and
-int8 among them, pad the cache's head_dim to hold an inline scale).  The HIP
-path runs through the C ABI (ctypes binding, kv dtype MLA_FP8_E4M3_PER_TOKEN
-or MLA_INT8_PER_TOKEN) and is compared with the float64 oracle, which decodes
+head_size codes (e4m3fn, signed int8, or signed int4 packed two per byte) and
+its own float32 scale inline in a 16-byte pad (Triton MLA page, key files: the
+per-token-head modes, fp8, int8 and int4 among them, pad the cache's head_dim
+to hold an inline scale).  The HIP path runs through the C ABI (ctypes
+binding, kv dtype MLA_FP8_E4M3_PER_TOKEN, MLA_INT8_PER_TOKEN or
+MLA_INT4_PER_TOKEN) and is compared with the float64 oracle, which decodes
 every row to code * scale of that token.
 
 Tolerances (max-abs) are those of the per-tensor fp8 cache: o 3e-2, lse 3e-3.
@@ -21,7 +22,11 @@ pytestmark = pytest.mark.gpu
 
 TOL_O, TOL_LSE = 3e-2, 3e-3
 PAD = W.PER_TOKEN_PAD
-DTYPES = [W.FP8_PER_TOKEN, W.INT8_PER_TOKEN]
+DTYPES = [W.FP8_PER_TOKEN, W.INT8_PER_TOKEN, W.INT4_PER_TOKEN]
+
+
+def code_bytes(dt, D):
+    return D // 2 if dt == W.INT4_PER_TOKEN else D
 
 
 @pytest.fixture(scope="module")
@@ -89,8 +94,8 @@ def case(seed, H, D, P, sl, dt=W.FP8_PER_TOKEN, **kw):
 def set_scales(inp, scales):
     """Replace the inline scale of every row by scales [NB, P] (float32)."""
     kv = inp.kv_bits.copy()
-    D = inp.workload.head_size
-    kv[..., D:D + 4] = np.ascontiguousarray(scales, dtype="<f4").view(np.uint8).reshape(
+    cb = code_bytes(inp.workload.kv_dtype, inp.workload.head_size)
+    kv[..., cb:cb + 4] = np.ascontiguousarray(scales, dtype="<f4").view(np.uint8).reshape(
         scales.shape + (4,))
     inp.kv_bits = kv
     return inp
@@ -134,8 +139,9 @@ def test_scales_differ_from_token_to_token(mla, H, D, mode, splits, dt):
     sl = (45, 200, 33)
     inp = case(41, H, D, 16, sl, dt, extra_pages=2)
     rng = np.random.default_rng(42)
-    D2 = D + PAD
-    base = inp.kv_bits[..., D:D + 4].copy().view("<f4")[..., 0]
+    cb = code_bytes(dt, D)
+    D2 = cb + PAD
+    base = inp.kv_bits[..., cb:cb + 4].copy().view("<f4")[..., 0]
     mult = np.exp2(rng.integers(-2, 2, size=base.shape)).astype(np.float32)
     set_scales(inp, base * mult)
     assert inp.kv_bits.shape[-1] == D2
@@ -149,9 +155,13 @@ def test_scales_differ_from_token_to_token(mla, H, D, mode, splits, dt):
 @pytest.mark.parametrize("mode,splits", [(0, 1), (1, 2)])
 def test_one_position_returns_the_scaled_row(mla, H, D, mode, splits, dt):
     """A single position has softmax weight 1, so o is its kv_c codes times
-    its scale.  Each sequence's row runs through all finite codes (254 e4m3fn
-    or 256 int8) and has its own scale with 2 significant bits (exact in
-    bf16), so every product is exact in fp32 and must come back bit for bit."""
+    its scale.  Each sequence's row runs through the finite code bytes (254
+    e4m3fn, 256 int8 or 256 pairs of int4 codes, as far as the row holds
+    them) and has its own scale with 2 significant bits (exact in bf16), so
+    every product is exact in fp32.  The kernel's weight of the position is
+    exp2 of a fused multiply-add residual, 1 to within an ulp, so o must be
+    the row to within 2^-22 relative (a wrong code or scale is off by far
+    more)."""
     Dv, P, B = D - 64, 16, 3
     rng = np.random.default_rng(51)
     if dt == W.FP8_PER_TOKEN:
@@ -159,12 +169,14 @@ def test_one_position_returns_the_scaled_row(mla, H, D, mode, splits, dt):
     else:
         finite = np.arange(256, dtype=np.uint8)
     nb = B + 2
-    kv = np.zeros((nb, P, D + PAD), dtype=np.uint8)
-    kv[..., :D] = rng.choice(finite, size=(nb, P, D))
+    cb = code_bytes(dt, D)
+    kv = np.zeros((nb, P, cb + PAD), dtype=np.uint8)
+    kv[..., :cb] = rng.choice(finite, size=(nb, P, cb))
     scales = np.exp2(rng.integers(-8, 3, size=(nb, P))).astype(np.float32) * np.float32(0.75)
+    n = min(finite.size, cb)
     for b in range(B):
-        kv[b + 1, 0, :finite.size] = np.roll(finite, 29 * b)
-    kv[..., D:D + 4] = scales.astype("<f4").view(np.uint8).reshape(nb, P, 4)
+        kv[b + 1, 0, :n] = np.roll(finite, 29 * b)[:n]
+    kv[..., cb:cb + 4] = scales.astype("<f4").view(np.uint8).reshape(nb, P, 4)
     table = np.array([[b + 1, 0] for b in range(B)], dtype=np.int32)
     q = W.f32_to_bf16_bits(rng.standard_normal((B, H, D), dtype=np.float32) * 0.1)
     w = W.Workload(name="pt-codes", seed=51, batch=B, num_heads=H, head_size=D,
@@ -174,7 +186,7 @@ def test_one_position_returns_the_scaled_row(mla, H, D, mode, splits, dt):
                          seq_lens=np.ones(B, dtype=np.int32))
     ro, rl = ref(inp)
     o32, l32 = run_gpu(mla, inp, splits, mode, o_dtype=torch.float32)
-    assert np.array_equal(o32, ro), np.abs(o32 - ro).max()
+    assert np.all(np.abs(o32 - ro) <= 2.0 ** -22 * np.abs(ro)), np.abs(o32 - ro).max()
     assert np.abs(l32 - rl).max() <= 1e-4 * max(1.0, np.abs(rl).max())
 
 
@@ -229,9 +241,9 @@ def test_multi_token_decode(mla, q_len, dt):
     assert_close(o, lse, ro, rl, empty, f"pt mtp q_len={q_len}")
 
 
-@pytest.mark.parametrize("name", ["fp8_pt", "int8_pt"])
+@pytest.mark.parametrize("name", ["fp8_pt", "int8_pt", "int4_pt"])
 def test_full_size_per_token(mla, name):
-    """The fp8_pt / int8_pt workloads (B=64, H=128, D=576, P=64, lengths
+    """The fp8_pt / int8_pt / int4_pt workloads (B=64, H=128, D=576, P=64, lengths
     1024..8192) at the planner's launch configuration and at per-sequence
     splits, checked on sampled sequences."""
     inp = W.generate(name)

@@ -147,20 +147,21 @@ def test_sparse_ignores_unlisted_slots(mla, mode, splits):
 
 
 QUANT_CASES = [
-    # (H, D, P, seq_lens, topk): 1-byte caches through the same gather
+    # (H, D, P, seq_lens, topk): 1-byte and 4-bit caches through the same gather
     (128, 576, 64, (300, 2000, 40, 1031), 256),
     (16, 576, 16, (1, 33, 64, 100), 48),
     (64, 576, 64, (300, 2000), 200),
     (128, 320, 32, (17, 95, 333), 72),
 ]
+QUANT_DTYPES = [W.FP8_E4M3, W.FP8_PER_TOKEN, W.INT8_PER_TOKEN, W.INT4_PER_TOKEN]
 
 
-@pytest.mark.parametrize("dt", [W.FP8_E4M3, W.FP8_PER_TOKEN, W.INT8_PER_TOKEN])
+@pytest.mark.parametrize("dt", QUANT_DTYPES)
 @pytest.mark.parametrize("case", range(len(QUANT_CASES)))
 @pytest.mark.parametrize("mode,splits", [(0, 1), (0, 3), (1, 5), (1, 37)])
 def test_sparse_quantised_caches(mla, case, mode, splits, dt):
-    """Quantised caches (per-tensor fp8; per-token fp8 / int8 with inline
-    scales) gathered by the index lists; tolerances of the fp8 cache."""
+    """Quantised caches (per-tensor fp8; per-token fp8 / int8 / int4 with
+    inline scales) gathered by the index lists; tolerances of the fp8 cache."""
     H, D, P, sl, k = QUANT_CASES[case]
     inp = W.small_case(seed=420 + case, batch=len(sl), num_heads=H, head_size=D,
                        kv_lora_rank=D - 64, page_size=P, seq_lens=sl, topk=k, kv_dtype=dt,
@@ -178,7 +179,7 @@ def test_sparse_quantised_caches(mla, case, mode, splits, dt):
     assert np.all(np.isfinite(o[live])) and do <= 3e-2 and dl <= 3e-3
 
 
-@pytest.mark.parametrize("dt", [W.FP8_E4M3, W.FP8_PER_TOKEN, W.INT8_PER_TOKEN])
+@pytest.mark.parametrize("dt", QUANT_DTYPES)
 @pytest.mark.parametrize("mode,splits", [(0, 1), (1, 7)])
 def test_sparse_quantised_over_every_position_is_dense_bitwise(mla, mode, splits, dt):
     sl = (37, 100, 1, 700)

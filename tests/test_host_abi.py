@@ -139,18 +139,18 @@ def test_fp8_query_is_refused():
 
 # ---------------------------------------------------------------- per-token fp8 cache
 
-@pytest.mark.parametrize("code", [3, 4])
+@pytest.mark.parametrize("code", [3, 4, 5])
 def test_per_token_cache_is_planned_like_the_others(code):
-    assert code in (mla.MLA_FP8_E4M3_PER_TOKEN, mla.MLA_INT8_PER_TOKEN)
+    assert code in (mla.MLA_FP8_E4M3_PER_TOKEN, mla.MLA_INT8_PER_TOKEN, mla.MLA_INT4_PER_TOKEN)
     s, pt = shape(), shape(kv_dtype=code)
     assert mla.mla_plan(pt, 8192, 64 * 4608, 256) == mla.mla_plan(s, 8192, 64 * 4608, 256)
     assert mla.mla_workspace_size(pt, mla.SPLIT_BALANCED, 64) == \
         mla.mla_workspace_size(s, mla.SPLIT_BALANCED, 64)
     with pytest.raises(NotImplementedError):  # MLA_ERR_DTYPE
-        mla.mla_plan(shape(kv_dtype=5), 1024, 0, 256)
+        mla.mla_plan(shape(kv_dtype=6), 1024, 0, 256)
 
 
-@pytest.mark.parametrize("code", [3, 4])
+@pytest.mark.parametrize("code", [3, 4, 5])
 def test_per_token_cache_argument_checks(code):
     pt = shape(kv_dtype=code)
     # k_scale is not read for a per-token cache, so 0 passes this check and
@@ -158,9 +158,10 @@ def test_per_token_cache_argument_checks(code):
     assert _decode_raw(pt, k_scale=0.0, splits=16) == mla.MLA_ERR_WORKSPACE
     assert _decode_raw(pt, q=258) == mla.MLA_ERR_ARGUMENT
     # the sparse gather addresses the pool with 32-bit offsets: pools past
-    # 4 GB (here 200000 pages of 64 rows of 592 bytes) are refused
+    # 4 GB (here 200000 pages of 64 rows of 592 bytes, or 400000 pages of
+    # 304-byte int4 rows) are refused
     lib = mla.load_library()
-    big = shape(kv_dtype=code, num_blocks=200000)
+    big = shape(kv_dtype=code, num_blocks=400000 if code == mla.MLA_INT4_PER_TOKEN else 200000)
     st = lib.mla_decode_sparse(ctypes.byref(big), 2048, 256, 256, 256, 256, 256, 0.07,
                                big.page_size, 1.0, 1, 0, 256, 256, None, 0, None)
     assert st == mla.MLA_ERR_SHAPE
@@ -182,6 +183,11 @@ def test_shape_of_checks_cache_row_width():
         mla.shape_of(q, torch.zeros(8, 16, 576, dtype=torch.uint8), bt, kv_dtype="fp8_per_token")
     with pytest.raises(ValueError):
         mla.shape_of(q, torch.zeros(8, 16, 576, dtype=torch.bfloat16), bt, kv_dtype="fp8_e4m3")
+    i4 = torch.zeros(8, 16, 288 + mla.MLA_PER_TOKEN_PAD, dtype=torch.uint8)
+    s = mla.shape_of(q, i4, bt, kv_dtype="int4_per_token")
+    assert s.kv_dtype == mla.MLA_INT4_PER_TOKEN and s.head_size == 576
+    with pytest.raises(ValueError):
+        mla.shape_of(q, pt, bt, kv_dtype="int4_per_token")  # rows of whole-byte codes
 
 
 # ---------------------------------------------------------------- cross-shard merge
