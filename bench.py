@@ -194,8 +194,10 @@ def ingest_pmc(fetch_csv, write_csv, workload, mfma_csv=None):
 
 def run_peaks(args):
     """Measured peaks next to the spec ones: HBM from a 1 GiB device-to-device
-    copy (2 GiB moved per copy), MFMA from a bf16 8192^3 GEMM (hipBLASLt),
-    each the median of 20 timed runs after 5 warm-ups."""
+    copy (2 GiB moved per copy) and from read-only fp32 sums (torch's
+    reduction over 1 GiB and over the 356 MB the dsv3 batch's cache rows
+    take), MFMA from a bf16 8192^3 GEMM (hipBLASLt), each the median of 20
+    timed runs after 5 warm-ups."""
     import numpy as np
     import torch
     dev = torch.device("cuda:0")
@@ -218,7 +220,11 @@ def run_peaks(args):
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     t_copy = timed(lambda: dst.copy_(src))
-    del src, dst
+    del dst
+    t_sum = timed(lambda: src.sum())
+    small = src[:309371 * 1152 // 4]
+    t_sum_small = timed(lambda: small.sum())
+    del src, small
     n = 8192
     a = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
     b = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
@@ -228,10 +234,13 @@ def run_peaks(args):
     print(json.dumps({
         "metric": "measured peaks (one MI355X)",
         "copy_GBps": round(copy_gbs, 1), "copy_frac_of_spec": round(copy_gbs / HBM_PEAK_GBS, 4),
+        "read_sum_GBps": round(COPY_BYTES / t_sum / 1e9, 1),
+        "read_sum_356MB_GBps": round(309371 * 1152 / t_sum_small / 1e9, 1),
         "gemm_bf16_TFLOPs": round(mm_tflops, 1),
         "gemm_frac_of_spec": round(mm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "spec": {"hbm_GBps": HBM_PEAK_GBS, "mfma_bf16_TFLOPs": MFMA_BF16_PEAK_TFLOPS},
         "how": "median of 20 HIP-event-timed runs: torch copy_ of 1 GiB (read + write), "
+               "torch sum of 1 GiB and of 356 MB fp32 (read only), "
                "torch.mm bf16 8192x8192x8192"}), flush=True)
     return 0
 
