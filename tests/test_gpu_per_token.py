@@ -191,6 +191,29 @@ def test_one_position_returns_the_scaled_row(mla, H, D, mode, splits, dt):
 
 
 @pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("H,D", [(16, 576), (128, 576), (32, 320)])
+@pytest.mark.parametrize("mode,splits", [(0, 1), (1, 5)])
+def test_zero_and_subnormal_scales(mla, H, D, mode, splits, dt):
+    """Rows whose scale is 0 (value 0 whatever their codes, but a full
+    softmax weight exp(0 - max)) or subnormal (1e-40) sit among ordinary rows:
+    the normaliser must count them with their weight p, which the kernel's
+    reciprocal-of-scale correction leaves out for such scales."""
+    sl = (70, 200, 33)
+    inp = case(71, H, D, 16, sl, dt, extra_pages=2)
+    rng = np.random.default_rng(72)
+    cb = code_bytes(dt, D)
+    base = inp.kv_bits[..., cb:cb + 4].copy().view("<f4")[..., 0]
+    pick = rng.random(base.shape)
+    scales = np.where(pick < 0.2, np.float32(0.0),
+                      np.where(pick < 0.3, np.float32(1e-40), base)).astype(np.float32)
+    set_scales(inp, scales)
+    ro, rl = ref(inp)
+    o, lse = run_gpu(mla, inp, splits, mode, o_dtype=torch.float32)
+    assert_close(o, lse, ro, rl, np.zeros(len(sl), bool),
+                 f"{dt} zero/subnormal scales H={H} D={D} S={splits}")
+
+
+@pytest.mark.parametrize("dt", DTYPES)
 def test_k_scale_does_not_apply(mla, dt):
     inp = case(61, 128, 576, 64, (100, 513), dt)
     a = run_gpu(mla, inp, 3, 1, k_scale=1.0)
