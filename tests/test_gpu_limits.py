@@ -2,8 +2,8 @@
 the most query tokens per sequence (MLA_MAX_Q_LEN), large pages, 512 heads
 (four head chunks per work unit), a thousand short sequences, the most
 split units (MLA_MAX_KV_SPLITS, nearly all of them owning no tile), one very
-long sequence, and a cache pool past 4 GB (64-bit page addressing, checked
-bitwise against the same pages in a small pool).  Tolerances as in the other
+long sequence, and cache pools past 4 GB (64-bit page addressing, bf16 and
+per-token rows, checked bitwise against the same pages in a small pool).  Tolerances as in the other
 parity tests: o 1e-2 (plus the bf16 rounding of the output), lse 1e-3.
 """
 import numpy as np
@@ -167,3 +167,38 @@ def test_pool_past_4_gb_is_addressed_exactly(mla):
     lse = lse.cpu().numpy().astype(np.float64)
     del big
     assert np.array_equal(o, small[0]) and np.array_equal(lse, small[1])
+
+
+@pytest.mark.parametrize("dt", [W.FP8_PER_TOKEN, W.INT4_PER_TOKEN])
+def test_per_token_pool_past_4_gb_is_addressed_exactly(mla, dt):
+    """Per-token rows (592 bytes for fp8 codes, 304 for int4) at the top of
+    a 5 GB pool give bitwise the result of the same pages in a small pool."""
+    sl = (100, 1031, 37)
+    inp = W.small_case(seed=561, batch=len(sl), num_heads=128, head_size=576, kv_lora_rank=512,
+                       page_size=16, seq_lens=sl, extra_pages=0, kv_dtype=dt)
+    w = inp.workload
+    q = torch.from_numpy(inp.q_bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    kv = torch.from_numpy(np.ascontiguousarray(inp.kv_bits)).to(DEV)  # uint8 rows
+    bt = torch.from_numpy(np.ascontiguousarray(inp.block_table)).to(DEV)
+    sl_d = torch.from_numpy(np.ascontiguousarray(inp.seq_lens)).to(DEV)
+    print(f"[limits] per-token {dt} pool past 4 GB", flush=True)
+    o_s, l_s = mla.mla_decode(q, kv, bt, sl_d, w.scale, w.page_size, 1.0, 5,
+                              split_mode=mla.SPLIT_BALANCED, kv_dtype=dt)
+    nb_small, row = kv.shape[0], kv.shape[2]
+    page_bytes = 16 * row
+    nb_big = (5 << 30) // page_bytes + nb_small
+    big = torch.empty((nb_big, 16, row), dtype=torch.uint8, device=DEV)
+    big[-nb_small:] = kv
+    bt_big = (bt + (nb_big - nb_small)).to(torch.int32)
+    assert int(bt_big.max()) * page_bytes > (1 << 32)
+    o_b, l_b = mla.mla_decode(q, big, bt_big, sl_d, w.scale, w.page_size, 1.0, 5,
+                              split_mode=mla.SPLIT_BALANCED, kv_dtype=dt)
+    torch.cuda.synchronize()
+    del big
+    assert torch.equal(o_s, o_b) and torch.equal(l_s, l_b)
+    ro, rl = ref(inp)  # quantised-cache tolerances: o 3e-2 beyond the bf16 rounding, lse 3e-3
+    o = o_b.float().cpu().numpy().astype(np.float64)
+    lse = l_b.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert (np.abs(o - ro) - half_ulp_bf16(ro)).max() <= 3e-2
+    assert np.abs(lse - rl).max() <= 3e-3
