@@ -25,7 +25,8 @@ Extra modes:
                        SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE) into
                        profiles/<kernel>_<workload>_traffic.json
   --peaks              measured peaks next to the spec ones: a 1 GiB device
-                       copy (HBM) and a bf16 8192^3 GEMM (hipBLASLt, MFMA)
+                       copy and read-only sums (HBM) and a bf16 8192^3 GEMM
+                       (hipBLASLt, MFMA)
   --dcp G              time the cross-shard merge of G page shards
 """
 import argparse
