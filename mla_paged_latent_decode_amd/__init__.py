@@ -179,6 +179,27 @@ def _dtype_code(t):
             torch.float8_e4m3fn: MLA_FP8_E4M3}.get(t, -1)
 
 
+def _check_sizes(shape, rows, block_table, lens, o, lse, topk_indices=None):
+    """The buffers the kernels index by sequence and row must hold B of them:
+    block_table [B, W], the lengths [B] (seq_lens, or topk_lens with
+    topk_indices [B, topk]), o rows + (D_v,) and lse rows float32, contiguous,
+    with rows = (B, H), or (B, q_len, H) for a [B, q_len, H, D] query.  The C
+    ABI takes raw pointers and cannot check this."""
+    torch = _torch()
+    B = shape.batch
+    if block_table.shape[0] != B:
+        raise ValueError(f"block_table has {block_table.shape[0]} rows, expected {B}")
+    if lens.dim() != 1 or lens.shape[0] != B:
+        raise ValueError(f"sequence lengths must be [{B}]")
+    if topk_indices is not None and (topk_indices.dim() != 2 or topk_indices.shape[0] != B):
+        raise ValueError(f"topk_indices must be [{B}, topk]")
+    if (tuple(o.shape) != rows + (shape.kv_lora_rank,) or tuple(lse.shape) != rows
+            or lse.dtype != torch.float32 or not o.is_contiguous() or not lse.is_contiguous()
+            or not (o.is_cuda and lse.is_cuda)):
+        raise ValueError("o must be [B,(q_len,)H,kv_lora_rank] and lse [B,(q_len,)H] float32, "
+                         "contiguous device tensors")
+
+
 def shape_of(q, kv_cache, block_table, *, kv_dtype=None, o_dtype=None) -> MlaShape:
     """The mla_shape of a call; q is [B, H, D] or [B, q_len, H, D] (H per token)."""
     torch = _torch()
@@ -246,10 +267,7 @@ def mla_decode(q, kv_cache, block_table, seq_lens, scale: float, page_size: int,
                         device=q.device)
     if lse is None:
         lse = torch.empty(rows, dtype=torch.float32, device=q.device)
-    if (tuple(o.shape) != rows + (shape.kv_lora_rank,) or tuple(lse.shape) != rows
-            or lse.dtype != torch.float32 or not o.is_contiguous() or not lse.is_contiguous()):
-        raise ValueError("o must be [B,(q_len,)H,kv_lora_rank] and lse [B,(q_len,)H] float32, "
-                         "contiguous")
+    _check_sizes(shape, rows, block_table, seq_lens, o, lse)
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -305,10 +323,13 @@ def mla_decode_sparse(q, kv_cache, block_table, topk_indices, topk_lens, scale: 
                         device=q.device)
     if lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _check_sizes(shape, (B, H), block_table, topk_lens, o, lse, topk_indices)
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
     fn = {"both": lib.mla_decode_sparse, "stage1": lib.mla_decode_sparse_stage1,
           "stage2": lib.mla_decode_sparse_stage2}[stages]
     st = fn(ctypes.byref(shape), topk, q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
@@ -379,11 +400,16 @@ class PreparedDecode:
         self.keep = (q, kv_cache, block_table, seq_lens, o, lse, workspace)
         self.shape = shape_of(q, kv_cache, block_table, kv_dtype=kv_dtype, o_dtype=o.dtype)
         q_len = q.shape[1] if q.dim() == 4 else 1
+        rows = ((self.shape.batch, q_len, self.shape.num_heads) if q.dim() == 4
+                else (self.shape.batch, self.shape.num_heads))
+        _check_sizes(self.shape, rows, block_table, seq_lens, o, lse, topk_indices)
         need = mla_workspace_size(self.shape, split_mode, num_kv_splits, q_len)
         if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
             raise MlaError(MLA_ERR_WORKSPACE, "workspace too small")
         if stream is None:
             stream = torch.cuda.current_stream(q.device).cuda_stream
+        elif hasattr(stream, "cuda_stream"):
+            stream = stream.cuda_stream
         lead = (ctypes.byref(self.shape), int(q_len), q.data_ptr(), kv_cache.data_ptr(),
                 block_table.data_ptr())
         if topk_indices is not None:

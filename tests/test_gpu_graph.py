@@ -81,3 +81,67 @@ def test_captured_decode_replays_match_eager(mla, mode, splits):
             slack = np.exp2(np.floor(np.log2(ax)) - 8)  # bf16 output rounding
             assert (np.abs(o_np - ro) - slack).max() <= 1e-2
             assert np.abs(l_g.cpu().numpy() - rl).max() <= 1e-3
+
+
+@pytest.mark.parametrize("kind", ["int4_per_token", "mtp", "sparse"])
+def test_other_entry_points_replay_like_eager(mla, kind):
+    """Per-token int4 cache, multi-token decode (q_len 3) and sparse decode,
+    each captured once and replayed on new queries, bitwise equal to eager
+    calls on the same inputs."""
+    sl = (37, 700, 1031, 5)
+    dt = W.INT4_PER_TOKEN if kind == "int4_per_token" else W.BF16
+    inp = W.small_case(seed=610, batch=len(sl), num_heads=128, head_size=576, kv_lora_rank=512,
+                       page_size=64, seq_lens=sl, kv_dtype=dt,
+                       q_len=3 if kind == "mtp" else 1, topk=256 if kind == "sparse" else None)
+    w = inp.workload
+    q = torch.from_numpy(inp.q_bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    if dt == W.BF16:
+        kv = torch.from_numpy(inp.kv_bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    else:
+        kv = torch.from_numpy(np.ascontiguousarray(inp.kv_bits)).to(DEV)
+    bt = torch.from_numpy(inp.block_table).to(DEV)
+    B, H = len(sl), 128
+    rows = (B, 3, H) if kind == "mtp" else (B, H)
+    o = torch.empty(rows + (512,), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(rows, dtype=torch.float32, device=DEV)
+    shape = mla.shape_of(q, kv, bt, kv_dtype=w.kv_dtype)
+    splits, mode = 9, mla.SPLIT_BALANCED
+    ws = torch.empty(max(mla.mla_workspace_size(shape, mode, splits,
+                                                3 if kind == "mtp" else 1), 256),
+                     dtype=torch.uint8, device=DEV)
+    if kind == "sparse":
+        idx = torch.from_numpy(inp.topk_indices).to(DEV)
+        lens = torch.from_numpy(inp.topk_lens).to(DEV)
+    else:
+        sl_d = torch.from_numpy(inp.seq_lens).to(DEV)
+    print(f"[graph] {kind}", flush=True)
+
+    def step(stream):
+        if kind == "sparse":
+            mla.mla_decode_sparse(q, kv, bt, idx, lens, w.scale, w.page_size, w.k_scale, splits,
+                                  o, lse, split_mode=mode, workspace=ws, stream=stream)
+        else:
+            mla.mla_decode(q, kv, bt, sl_d, w.scale, w.page_size, w.k_scale, splits, o, lse,
+                           split_mode=mode, workspace=ws, kv_dtype=w.kv_dtype, stream=stream)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(611)
+    for rep in range(3):
+        q_new = W.f32_to_bf16_bits(rng.standard_normal(inp.q_bits.shape, dtype=np.float32))
+        q.copy_(torch.from_numpy(q_new.view(np.int16)).view(torch.bfloat16).to(DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o_g, l_g = o.clone(), lse.clone()
+        step(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o) and torch.equal(l_g, lse), f"{kind} replay {rep}"
