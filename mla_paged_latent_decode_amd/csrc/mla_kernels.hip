@@ -17,9 +17,10 @@
 //   XOR swizzle, so that both the QK^T read (ds_read_b128) and the
 //   transposed V read (ds_read_b64_tr_b16) hit distinct banks.
 //
-//   Variants of the same kernel: 1-byte caches (e4m3fn with a per-tensor
-//   scale, or e4m3fn / int8 codes with a per-token inline scale, "Triton と
-//   MLA" page, 主要ファイル) are staged in LDS and widened to bf16 there;
+//   Variants of the same kernel: narrow caches (e4m3fn with a per-tensor
+//   scale, or e4m3fn / int8 / packed int4 codes with a per-token inline
+//   scale, "Triton と MLA" page, 主要ファイル) are staged in LDS and widened
+//   to bf16 there;
 //   multi-token decode gives each query-token row its own causal limit
 //   (article above, section 十); sparse decode takes its rows from a list of
 //   logical positions (section 十三) through an index-driven gather.
