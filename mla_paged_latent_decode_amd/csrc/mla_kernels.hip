@@ -182,12 +182,14 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 v) {
 
 // Eight signed int4 codes (element 2i in the low nibble of byte i, 2i+1 in
 // its high nibble) to eight bf16: every value in [-8, 7] is exact in bf16.
+// (Each code is moved to the top of the word as unsigned, then shifted back
+// down as signed: an arithmetic shift sign-extends it.)
 __device__ __forceinline__ u32x4 i4x8_to_bf16x8(uint32_t v) {
   u32x4 r;
-  const int x = (int)v;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const f32x2 e = {(float)((x << (28 - 8 * k)) >> 28), (float)((x << (24 - 8 * k)) >> 28)};
+    const f32x2 e = {(float)((int)(v << (28 - 8 * k)) >> 28),
+                     (float)((int)(v << (24 - 8 * k)) >> 28)};
     r[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(e, bf16x2));
   }
   return r;
@@ -199,9 +201,9 @@ __device__ __forceinline__ u32x4 i8x8_to_bf16x8(u32x2 v) {
   u32x4 r;
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
-    const int x = (int)v[w];
-    const f32x2 lo = {(float)((x << 24) >> 24), (float)((x << 16) >> 24)};
-    const f32x2 hi = {(float)((x << 8) >> 24), (float)(x >> 24)};
+    const uint32_t x = v[w];
+    const f32x2 lo = {(float)((int)(x << 24) >> 24), (float)((int)(x << 16) >> 24)};
+    const f32x2 hi = {(float)((int)(x << 8) >> 24), (float)((int)x >> 24)};
     r[2 * w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
     r[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
   }
