@@ -25,8 +25,11 @@ Extra modes:
                        SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE) into
                        profiles/<kernel>_<workload>_traffic.json
   --peaks              measured peaks next to the spec ones: a 1 GiB device
-                       copy and read-only sums (HBM) and a bf16 8192^3 GEMM
-                       (hipBLASLt, MFMA)
+                       copy and read-only sums (HBM), a bf16 8192^3 GEMM
+                       (hipBLASLt, MFMA), and the in-tree probes of
+                       libmla_peaks.so: HBM -> LDS streaming in the decode's
+                       load pattern, a v_mfma_f32_32x32x16_bf16 loop and
+                       ds_read_b128 LDS reads
   --dcp G              time the cross-shard merge of G page shards
 """
 import argparse
@@ -88,18 +91,39 @@ def algorithmic(inp):
             "tokens": int(n.sum())}
 
 
-def cpu_baseline(inp, alg, budget_s=25.0):
-    """The float64 oracle on the host cores, over whole sequences of the same
-    batch until the batch is done or the time budget is spent."""
-    import numpy as np
-    import oracle
-    w = inp.workload
+def host_facts():
+    """Cores this process may run on (sched_getaffinity), the CPU model name
+    (lscpu), and the thread count of the BLAS numpy uses."""
+    cores = len(os.sched_getaffinity(0))
+    model = None
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for ln in out.splitlines():
+            if ln.strip().lower().startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except Exception:
+        pass
+    threads = None
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()
                        if i.get("user_api") == "blas"] or [1])
     except Exception:
-        threads = None
+        pass
+    return cores, model, threads
+
+
+def cpu_baseline(inp, alg, budget_s=25.0):
+    """The float64 oracle on the host cores, over whole sequences of the same
+    batch until the batch is done or the time budget is spent.  The oracle
+    processes one sequence at a time; its two products per sequence (scores,
+    then weights times V) run in the host BLAS with `blas_threads` threads."""
+    import numpy as np
+    import oracle
+    w = inp.workload
+    cores, model, threads = host_facts()
     done, tok = 0, 0
     t0 = time.perf_counter()
     fn = oracle.decode if w.q_len == 1 else oracle.decode_mtp
@@ -120,9 +144,10 @@ def cpu_baseline(inp, alg, budget_s=25.0):
     dt = time.perf_counter() - t0
     per_token = alg["total_bytes"] / alg["tokens"]
     return {"value": round(tok * per_token / dt / 1e9, 4), "unit": "GB/s",
-            "cores": threads, "kind": "oracle",
+            "cores": cores, "kind": "oracle",
             "sample": f"{done} of {w.batch} sequences ({tok} tokens) of the same batch, "
                       f"{dt:.1f} s, numpy float64 with BLAS on the host",
+            "cpu_model": model, "blas_threads": threads,
             "tokens_heads_per_s": round(tok * w.num_heads / dt, 1)}
 
 
@@ -232,6 +257,8 @@ def run_peaks(args):
     t_mm = timed(lambda: torch.mm(a, b))
     copy_gbs = 2 * COPY_BYTES / t_copy / 1e9
     mm_tflops = 2 * n ** 3 / t_mm / 1e12
+    del a, b
+    probes = run_probes(timed)
     print(json.dumps({
         "metric": "measured peaks (one MI355X)",
         "copy_GBps": round(copy_gbs, 1), "copy_frac_of_spec": round(copy_gbs / HBM_PEAK_GBS, 4),
@@ -240,10 +267,88 @@ def run_peaks(args):
         "gemm_bf16_TFLOPs": round(mm_tflops, 1),
         "gemm_frac_of_spec": round(mm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "spec": {"hbm_GBps": HBM_PEAK_GBS, "mfma_bf16_TFLOPs": MFMA_BF16_PEAK_TFLOPS},
+        "probes": probes,
         "how": "median of 20 HIP-event-timed runs: torch copy_ of 1 GiB (read + write), "
                "torch sum of 1 GiB and of 356 MB fp32 (read only), "
-               "torch.mm bf16 8192x8192x8192"}), flush=True)
+               "torch.mm bf16 8192x8192x8192; probes: libmla_peaks.so kernels, GB/s or "
+               "TFLOP/s from the events, cycles from each workgroup's s_memtime and the "
+               "shader clock from s_memtime over s_memrealtime (100 MHz)"}), flush=True)
     return 0
+
+
+def run_probes(timed):
+    """The in-tree probes of libmla_peaks.so (see mla_peaks.hip):
+    - stream: HBM -> LDS copies of 36 KB tiles (halves of 64-row pages of
+      1152-byte rows, pages in a seeded random order) through a ring of LDS
+      tiles, one workgroup per CU, about the dsv3 cache's bytes per launch;
+      the decode's configuration is 4 waves, ring 3, 16-row loads;
+    - mfma: v_mfma_f32_32x32x16_bf16 on every SIMD;
+    - lds: ds_read_b128 by 4 and 8 waves per CU."""
+    import ctypes
+    import numpy as np
+    import torch
+    from mla_paged_latent_decode_amd import _build
+    lib = ctypes.CDLL(_build.PEAKS_LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.mla_peak_stream.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp]
+    lib.mla_peak_mfma.argtypes = [i32, i32, vp, vp, vp]
+    lib.mla_peak_lds.argtypes = [i32, i32, i32, vp, vp, vp]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    grid = cus
+    cyc = torch.zeros((4 * grid, 2), dtype=torch.int64, device=dev)
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    out = {}
+
+    def clock(g):
+        c = cyc[:g].cpu().numpy().astype(np.float64)
+        return c[:, 0], float(np.median(c[:, 0] / np.maximum(c[:, 1], 1) * 100.0))
+
+    pool_pages = 8192
+    pool = torch.empty(pool_pages * 64 * 1152, dtype=torch.uint8, device=dev).fill_(1)
+    per_wg = 38
+    g = np.random.default_rng(1234)
+    pages = torch.from_numpy(g.permutation(pool_pages)[: grid * per_wg // 2].astype(np.int32)).to(dev)
+    nbytes = grid * per_wg * 36 * 1024
+    for waves, ring, rows, read in ((4, 3, 1, 0), (4, 2, 1, 0), (4, 4, 1, 0), (4, 3, 0, 0),
+                                    (4, 3, 1, 1), (8, 3, 1, 0), (8, 4, 1, 0), (8, 3, 1, 1)):
+        def go():
+            rc = lib.mla_peak_stream(pool.data_ptr(), pages.data_ptr(), grid, per_wg, waves, ring,
+                                     rows, read, cyc.data_ptr(), sink.data_ptr(), stream)
+            if rc:
+                raise RuntimeError(f"mla_peak_stream failed: {rc}")
+        t = timed(go)
+        cycles, mhz = clock(grid)
+        key = f"stream_w{waves}_ring{ring}_{'rows' if rows else 'contig'}{'_read' if read else ''}"
+        out[key] = {"GBps": round(nbytes / t / 1e9, 1), "frac_of_spec": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                    "cycles_per_tile": round(float(np.median(cycles)) / per_wg, 1),
+                    "mhz": round(mhz)}
+    del pool
+    iters = 2000
+
+    def go_mfma():
+        if lib.mla_peak_mfma(grid, iters, cyc.data_ptr(), sink.data_ptr(), stream):
+            raise RuntimeError("mla_peak_mfma failed")
+    t = timed(go_mfma)
+    cycles, mhz = clock(grid)
+    flops = grid * 4 * iters * 8 * 32 * 32 * 16 * 2
+    out["mfma_bf16_32x32x16"] = {"TFLOPs": round(flops / t / 1e12, 1),
+                                 "frac_of_spec": round(flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                                 "cycles_per_mfma": round(float(np.median(cycles)) / (iters * 8), 2),
+                                 "mhz": round(mhz)}
+    for waves in (4, 8):
+        lit = 200
+
+        def go_lds():
+            if lib.mla_peak_lds(grid, waves, lit, cyc.data_ptr(), sink.data_ptr(), stream):
+                raise RuntimeError("mla_peak_lds failed")
+        t = timed(go_lds)
+        cycles, mhz = clock(grid)
+        per_wg_bytes = waves * lit * 64 * 1024
+        out[f"lds_read_b128_w{waves}"] = {"bytes_per_clk_per_cu": round(per_wg_bytes / float(np.median(cycles)), 1),
+                                          "mhz": round(mhz)}
+    return out
 
 
 def run_dcp(args, G):

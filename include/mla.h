@@ -39,8 +39,14 @@
  *     library never allocates, frees, copies to the host or synchronises.
  *   - Arguments are checked on the host before anything is enqueued; on any
  *     error the function returns a non-zero mla_status and enqueues nothing.
- *   - The contents of block_table entries are trusted: a page index outside
- *     [0, num_blocks) is undefined behaviour (the kernels do not check it).
+ *   - Table contents are not validated before a launch (that would need a
+ *     device-to-host copy), but the kernels stay inside every buffer whatever
+ *     they hold: a length in seq_lens is clamped to [0, max_blocks_per_seq *
+ *     page_size] (a top-k length to [0, topk]); a block_table entry outside
+ *     [0, num_blocks) and a top-k position outside [0, max_blocks_per_seq *
+ *     page_size) read as all-zero cache rows.  The results of such a call
+ *     are unspecified.  mla_check_inputs() checks host copies of the tables
+ *     and names the first offending entry.
  *   - Entry points are re-entrant; concurrent calls must use distinct
  *     workspaces and outputs.
  */
@@ -65,7 +71,8 @@ typedef enum mla_status {
                             page, Limites et échecs: block sizes are multiples of 16)   */
   MLA_ERR_DTYPE = 4,     /* q not bf16 (an fp8 query is refused: "Triton と MLA" page,
                             境界と失敗), kv not bf16 / fp8 e4m3fn (per-tensor or
-                            per-token scale) / per-token int8, o not bf16/fp32           */
+                            per-token scale) / per-token int8 / per-token int4, o not
+                            bf16/fp32                                                    */
   MLA_ERR_SHAPE = 5,     /* batch < 1, num_heads not a positive multiple of 16,
                             num_blocks < 1 (empty cache), max_blocks_per_seq < 1, or a
                             size whose byte count overflows                              */
@@ -74,8 +81,11 @@ typedef enum mla_status {
   MLA_ERR_WORKSPACE = 7, /* workspace NULL or smaller than mla_workspace_size() for the
                             same shape, split mode and split count                       */
   MLA_ERR_LAUNCH = 8,    /* HIP reported an error when the kernels were enqueued        */
-  MLA_ERR_ARGUMENT = 9   /* a non-finite or non-positive scale / k_scale, num_cus < 1,
-                            q_len outside [1, MLA_MAX_Q_LEN], or a misaligned pointer    */
+  MLA_ERR_ARGUMENT = 9,  /* a non-finite or non-positive scale / k_scale, num_cus < 1,
+                            q_len outside [1, MLA_MAX_Q_LEN], topk < 1, or a misaligned
+                            pointer or query stride                                      */
+  MLA_ERR_TABLE = 10     /* mla_check_inputs: a length, block-table entry or top-k entry
+                            out of range                                                 */
 } mla_status;
 
 typedef enum mla_dtype {
@@ -274,6 +284,38 @@ mla_status mla_decode_mtp_stage2(const mla_shape* shape, int32_t q_len, const vo
                                  void* o, float* lse, void* workspace, size_t workspace_bytes,
                                  void* hip_stream);
 
+/* The query as two separate parts, q_nope (the first kv_lora_rank columns of a
+ * query row) and q_pe (the last 64), each with its own strides, read directly
+ * by the decode kernel: no concatenated copy is made ("Triton と MLA" page,
+ * データフロー: forward_mqa takes q either whole or as the tuple (q_nope,
+ * q_pe) and joins the tuple on the last axis, in that order, before the
+ * kernel).  Row r of sequence b (r = query token * num_heads + head) is
+ *     [ q_nope + b * nope_seq_stride + r * nope_row_stride : kv_lora_rank elems
+ *     | q_pe   + b * pe_seq_stride   + r * pe_row_stride   : 64 elems ]
+ * Strides are in bf16 elements, non-negative multiples of 8 (each 16-byte
+ * chunk is loaded aligned); both pointers are 16-byte aligned device
+ * pointers owned by the caller. */
+typedef struct mla_query {
+  const void* q_nope;
+  const void* q_pe;
+  int64_t nope_seq_stride, nope_row_stride;
+  int64_t pe_seq_stride, pe_row_stride;
+} mla_query;
+
+/* mla_decode_mtp (q_len = 1: mla_decode) with the query given as an
+ * mla_query instead of one contiguous [B, q_len, H, head_size] tensor.  Every
+ * other argument, check, layout and ownership rule is that of
+ * mla_decode_mtp; a misaligned pointer or stride is MLA_ERR_ARGUMENT, a NULL
+ * query or part MLA_ERR_NULL.  With q_nope = q, q_pe = q + kv_lora_rank and
+ * strides (q_len * H * head_size, head_size) for both parts the call is
+ * exactly mla_decode_mtp on q. */
+mla_status mla_decode_split_q(const mla_shape* shape, int32_t q_len, const mla_query* q,
+                              const void* kv_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, float scale, int32_t page_size,
+                              float k_scale, int32_t num_kv_splits, int32_t split_mode, void* o,
+                              float* lse, void* workspace, size_t workspace_bytes,
+                              void* hip_stream);
+
 /* Sparse (top-k) decode ("vLLM 中 Attention Kernel 如何并行处理多个请求",
  * section 十三): each sequence attends only to a selected list of its
  * positions, e.g. the top 2048, instead of all of them.  Request isolation is
@@ -285,7 +327,8 @@ mla_status mla_decode_mtp_stage2(const mla_shape* shape, int32_t q_len, const vo
  * place of seq_lens[b] for the split plan (plan with max_seq_len = topk and
  * total_seq_len = sum of topk_lens; workspace from mla_workspace_size).
  *   topk_indices  [batch, topk] int32, device; entries and topk_lens[b] <= topk
- *                 are trusted like block_table entries
+ *                 are not validated (see the conventions above:
+ *                 out-of-range values stay inside every buffer)
  *   topk_lens     [batch] int32, device; 0 gives o = 0, lse = -inf
  * The index-driven gather takes every cache dtype, head size and head count
  * mla_decode takes, for pools of at most 4 GB (else MLA_ERR_SHAPE); topk < 1
@@ -310,6 +353,25 @@ mla_status mla_decode_sparse_stage2(const mla_shape* shape, int32_t topk, const 
                                     int32_t num_kv_splits, int32_t split_mode, void* o,
                                     float* lse, void* workspace, size_t workspace_bytes,
                                     void* hip_stream);
+
+/* Host-side check of the tables a decode call will read ("vLLM 中 Attention
+ * Kernel 如何并行处理多个请求", section 十一: each request reaches the cache only
+ * through its own block-table row, so a bad entry would read another
+ * request's rows).  All pointers are HOST pointers (copies of the device
+ * tables); nothing is enqueued.  Dense decode (topk_indices = topk_lens =
+ * NULL): every seq_lens[b] must lie in [0, max_blocks_per_seq * page_size]
+ * and the entries block_table[b][j], j < ceil(seq_lens[b] / page_size), in
+ * [0, num_blocks).  Sparse decode (both lists given, seq_lens ignored):
+ * topk_lens[b] in [0, topk], and every listed position e < topk_lens[b] in
+ * [0, max_blocks_per_seq * page_size) with its page entry in [0, num_blocks).
+ * Returns MLA_OK, MLA_ERR_TABLE with *bad_index (if not NULL) = the flat
+ * index of the first offending element (into seq_lens / topk_lens for a
+ * length, into block_table for a page, into topk_indices for a position),
+ * or the shape / NULL / argument errors of the decode calls.  Multi-token
+ * decode uses the same tables as dense decode. */
+mla_status mla_check_inputs(const mla_shape* shape, const int32_t* block_table,
+                            const int32_t* seq_lens, int32_t topk, const int32_t* topk_indices,
+                            const int32_t* topk_lens, int64_t* bad_index);
 
 /* Merge the results of a context-parallel decode ("Triton と MLA" page,
  * 設計動機: decode always returns lse because the context shards are merged

@@ -11,7 +11,9 @@ be loaded, every call raises.
 
 ``q`` [B, H, D] bf16 = [q_nope (D_v) | q_pe (64)], or [B, q_len, H, D] for a
 multi-token decode (query token i of a sequence with n keys sees positions
-< n - q_len + 1 + i); ``kv_cache``
+< n - q_len + 1 + i), or the tuple ``(q_nope, q_pe)`` of [.., D_v] and [.., 64]
+tensors with unit stride on the last axis, read in place (no concatenation);
+``kv_cache``
 [num_blocks, page_size, D] bf16 or fp8 e4m3fn with rows [kv_c | k_pe];
 ``block_table`` [B, max_blocks_per_seq] int32; ``seq_lens`` [B] int32.
 Returns ``o`` [B, H, D_v] (bf16 by default) and ``lse`` [B, H] float32
@@ -27,7 +29,7 @@ from typing import Optional, Tuple
 from . import _build
 
 __all__ = [
-    "MlaError", "mla_decode", "mla_decode_sparse", "mla_plan", "mla_workspace_size", "mla_pages_split_count",
+    "MlaError", "mla_decode", "mla_decode_sparse", "mla_plan", "mla_check_inputs", "mla_workspace_size", "mla_pages_split_count",
     "mla_status_string", "SPLIT_PER_SEQUENCE", "SPLIT_BALANCED", "library_path", "load_library",
     "MLA_BF16", "MLA_FP8_E4M3", "MLA_FP32", "MLA_FP8_E4M3_PER_TOKEN", "MLA_INT8_PER_TOKEN",
     "MLA_INT4_PER_TOKEN",
@@ -36,6 +38,7 @@ __all__ = [
 
 MLA_OK, MLA_ERR_NULL, MLA_ERR_HEAD_SIZE, MLA_ERR_PAGE_SIZE, MLA_ERR_DTYPE = 0, 1, 2, 3, 4
 MLA_ERR_SHAPE, MLA_ERR_SPLITS, MLA_ERR_WORKSPACE, MLA_ERR_LAUNCH, MLA_ERR_ARGUMENT = 5, 6, 7, 8, 9
+MLA_ERR_TABLE = 10
 MLA_BF16, MLA_FP8_E4M3, MLA_FP32, MLA_FP8_E4M3_PER_TOKEN, MLA_INT8_PER_TOKEN = 0, 1, 2, 3, 4
 MLA_INT4_PER_TOKEN = 5  # two signed 4-bit codes per byte, element 2i in the low nibble
 MLA_PER_TOKEN_PAD = 16  # bytes after the codes of a per-token cache row (fp32 scale first)
@@ -50,6 +53,12 @@ class MlaShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "num_heads", "head_size", "kv_lora_rank", "page_size", "num_blocks",
         "max_blocks_per_seq", "q_dtype", "kv_dtype", "o_dtype")]
+
+
+class MlaQuery(ctypes.Structure):
+    _fields_ = [("q_nope", ctypes.c_void_p), ("q_pe", ctypes.c_void_p),
+                ("nope_seq_stride", ctypes.c_int64), ("nope_row_stride", ctypes.c_int64),
+                ("pe_seq_stride", ctypes.c_int64), ("pe_row_stride", ctypes.c_int64)]
 
 
 class MlaError(RuntimeError):
@@ -98,6 +107,12 @@ def load_library():
             fn.argtypes = [shp, i32, vp, vp, vp, vp, vp, ctypes.c_float, i32, ctypes.c_float,
                            i32, i32, vp, vp, vp, sz, vp]
             fn.restype = i32
+        lib.mla_decode_split_q.argtypes = [shp, i32, ctypes.POINTER(MlaQuery), vp, vp, vp,
+                                           ctypes.c_float, i32, ctypes.c_float, i32, i32, vp,
+                                           vp, vp, sz, vp]
+        lib.mla_decode_split_q.restype = i32
+        lib.mla_check_inputs.argtypes = [shp, vp, vp, i32, vp, vp, ctypes.POINTER(i64)]
+        lib.mla_check_inputs.restype = i32
         lib.mla_merge_shards.argtypes = [i32, i64, i32, vp, i32, vp, i32, vp, i32, vp, vp]
         lib.mla_merge_shards.restype = i32
         lib.mla_status_string.argtypes = [i32]
@@ -112,7 +127,7 @@ def mla_status_string(status: int) -> str:
 
 def _raise(status: int, what: str):
     msg = f"{what}: {mla_status_string(status)}"
-    if status in (MLA_ERR_HEAD_SIZE, MLA_ERR_PAGE_SIZE):
+    if status in (MLA_ERR_HEAD_SIZE, MLA_ERR_PAGE_SIZE, MLA_ERR_TABLE):
         raise ValueError(msg)
     if status == MLA_ERR_DTYPE:
         raise NotImplementedError(msg)
@@ -220,41 +235,104 @@ def shape_of(q, kv_cache, block_table, *, kv_dtype=None, o_dtype=None) -> MlaSha
                       q_dtype=_dtype_code(q.dtype))
 
 
+def mla_check_inputs(shape: MlaShape, block_table, seq_lens=None, topk_indices=None,
+                     topk_lens=None) -> None:
+    """Check the tables a decode call will read (host-side, ``mla_check_inputs``
+    of the C ABI): lengths within the table width, every page a sequence reads
+    inside the pool, and for sparse decode every listed position addressable
+    and its page inside the pool.  Device tensors are copied to the host
+    first, which synchronises with the device.  Raises ValueError naming the
+    first bad entry."""
+    import numpy as np
+    lib = load_library()
+
+    def host(t):
+        if t is None:
+            return None
+        a = t.detach().cpu().numpy() if hasattr(t, "detach") else np.asarray(t)
+        return np.ascontiguousarray(a, dtype=np.int32)
+    bt, sl, ti, tl = host(block_table), host(seq_lens), host(topk_indices), host(topk_lens)
+    topk = int(ti.shape[1]) if ti is not None else 0
+    ptr = lambda a: a.ctypes.data if a is not None else None  # noqa: E731
+    bad = ctypes.c_int64(-1)
+    st = lib.mla_check_inputs(ctypes.byref(shape), ptr(bt), ptr(sl), topk, ptr(ti), ptr(tl),
+                              ctypes.byref(bad))
+    if st != MLA_OK:
+        _raise(st, f"mla_check_inputs (first bad element: flat index {bad.value})")
+
+
+def _query_of(q, B, H, D, D_v, q_len):
+    """(MlaQuery, device, dtype) of a tuple query (q_nope [.., D_v], q_pe [.., 64]) laid out
+    as [B, H, *] or [B, q_len, H, *]; strides in elements, rows merged over (q_len, H)."""
+    q_nope, q_pe = q
+    q_len_dims = 4 if q_len > 1 else 3
+    for name, t, w in (("q_nope", q_nope, D_v), ("q_pe", q_pe, D - D_v)):
+        if not t.is_cuda or t.dim() != q_len_dims or t.shape[-1] != w or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be a device tensor [B,(q_len,)H,{w}] with unit "
+                             "stride on its last axis")
+        if tuple(t.shape[:-1]) != tuple(q_nope.shape[:-1]):
+            raise ValueError("q_nope and q_pe must have the same leading shape")
+        if q_len > 1 and t.stride(1) != H * t.stride(2):
+            raise ValueError(f"{name}: the (q_len, H) axes must be mergeable into one row axis")
+    row = -2
+    return MlaQuery(q_nope.data_ptr(), q_pe.data_ptr(), q_nope.stride(0), q_nope.stride(row),
+                    q_pe.stride(0), q_pe.stride(row))
+
+
 def mla_decode(q, kv_cache, block_table, seq_lens, scale: float, page_size: int,
                k_scale: float = 1.0, num_kv_splits: Optional[int] = None, o=None, lse=None, *,
                split_mode: Optional[int] = None, workspace=None, kv_dtype=None,
                o_dtype=None, max_seq_len: Optional[int] = None,
                total_seq_len: Optional[int] = None, num_cus: Optional[int] = None,
-               deterministic: bool = False, stream=None, stages: str = "both"):
+               deterministic: bool = False, stream=None, stages: str = "both",
+               check: bool = False):
     """Enqueue one MLA decode step on the current (or given) stream.
 
     When ``num_kv_splits`` is None the split plan comes from ``mla_plan``
-    (which needs ``max_seq_len``; it is read from ``seq_lens`` when not
-    given).  When ``num_kv_splits`` is given without ``split_mode``, the
-    per-sequence split layout is used.  Missing ``o``/``lse``/``workspace``
-    are allocated with torch.  ``stages`` = "stage1" / "stage2" enqueues only
-    that half (mla_decode_stage1 / mla_decode_stage2).  Returns (o, lse)."""
+    with the host-side ``max_seq_len`` / ``total_seq_len`` if given (as a
+    serving loop keeps them in its metadata); otherwise the table width
+    (``block_table.shape[1] * page_size``) bounds every length, so planning
+    never reads ``seq_lens`` back from the device.  When ``num_kv_splits`` is
+    given without ``split_mode``, the per-sequence split layout is used.
+    Missing ``o``/``lse``/``workspace`` are allocated with torch.  ``stages`` =
+    "stage1" / "stage2" enqueues only that half (mla_decode_stage1 /
+    mla_decode_stage2; not for a tuple q).  ``check=True`` first validates the
+    tables on the host (``mla_check_inputs``; a device-to-host copy).  Returns
+    (o, lse)."""
     torch = _torch()
     lib = load_library()
+    split_q = isinstance(q, (tuple, list))
+    if split_q:
+        if len(q) != 2:
+            raise ValueError("a tuple query is (q_nope, q_pe)")
+        q_tuple = (q[0], q[1])
+        q = q_tuple[0]  # leading dims, device and dtype come from q_nope
     if not (q.is_cuda and kv_cache.is_cuda and block_table.is_cuda and seq_lens.is_cuda):
         raise ValueError("mla_decode needs device tensors (HIP)")
     for name, t in (("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
                     ("seq_lens", seq_lens)):
-        if not t.is_contiguous():
+        if not t.is_contiguous() and not (split_q and name == "q"):
             raise ValueError(f"{name} must be contiguous")
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise ValueError("block_table and seq_lens must be int32")
     if o is not None:
         o_dtype = o.dtype
-    shape = shape_of(q, kv_cache, block_table, kv_dtype=kv_dtype, o_dtype=o_dtype)
+    if split_q:
+        D = q_tuple[0].shape[-1] + q_tuple[1].shape[-1]
+        qshape = torch.empty(tuple(q.shape[:-1]) + (D,), dtype=q.dtype, device="meta")
+        shape = shape_of(qshape, kv_cache, block_table, kv_dtype=kv_dtype, o_dtype=o_dtype)
+    else:
+        shape = shape_of(q, kv_cache, block_table, kv_dtype=kv_dtype, o_dtype=o_dtype)
     B, H = shape.batch, shape.num_heads
     q_len = q.shape[1] if q.dim() == 4 else 1
     rows = (B, q_len, H) if q.dim() == 4 else (B, H)
+    if check:
+        mla_check_inputs(shape, block_table, seq_lens)
     if num_kv_splits is None:
         if max_seq_len is None:
-            max_seq_len = int(seq_lens.max().item()) if B else 0
-            if total_seq_len is None:
-                total_seq_len = int(seq_lens.sum().item())
+            # no device read-back: the table width bounds every length
+            max_seq_len = int(block_table.shape[1]) * int(page_size)
+            total_seq_len = total_seq_len or 0
         if num_cus is None:
             num_cus = torch.cuda.get_device_properties(q.device).multi_processor_count
         split_mode, num_kv_splits, _ = mla_plan(shape, max_seq_len, total_seq_len or 0,
@@ -276,6 +354,18 @@ def mla_decode(q, kv_cache, block_table, seq_lens, scale: float, page_size: int,
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
+    if split_q:
+        if stages != "both":
+            raise ValueError("a tuple query runs both stages (mla_decode_split_q)")
+        qd = _query_of(q_tuple, B, H, shape.head_size, shape.kv_lora_rank, q_len)
+        st = lib.mla_decode_split_q(ctypes.byref(shape), int(q_len), ctypes.byref(qd),
+                                    kv_cache.data_ptr(), block_table.data_ptr(),
+                                    seq_lens.data_ptr(), float(scale), int(page_size),
+                                    float(k_scale), int(num_kv_splits), int(split_mode),
+                                    o.data_ptr(), lse.data_ptr(), ws_ptr, int(ws_bytes), stream)
+        if st != MLA_OK:
+            _raise(st, "mla_decode_split_q")
+        return o, lse
     fn = {"both": lib.mla_decode_mtp, "stage1": lib.mla_decode_mtp_stage1,
           "stage2": lib.mla_decode_mtp_stage2}[stages]
     st = fn(ctypes.byref(shape), int(q_len), q.data_ptr(), kv_cache.data_ptr(),
@@ -292,11 +382,13 @@ def mla_decode_sparse(q, kv_cache, block_table, topk_indices, topk_lens, scale: 
                       num_kv_splits: Optional[int] = None, o=None, lse=None, *,
                       split_mode: Optional[int] = None, workspace=None, o_dtype=None,
                       num_cus: Optional[int] = None, stream=None, stages: str = "both",
-                      kv_dtype=None):
+                      kv_dtype=None, total_topk: Optional[int] = None, check: bool = False):
     """Sparse (top-k) MLA decode: sequence b attends to the cache rows of the
     logical positions ``topk_indices[b, :topk_lens[b]]`` (int32 [B, topk] and
     [B]).  Other arguments as in ``mla_decode``; the split plan counts list
-    entries.  Returns (o [B, H, D_v], lse [B, H])."""
+    entries (``total_topk`` = their sum if known on the host, else B * topk is
+    assumed; nothing is read back from the device).  ``check=True`` validates
+    the lists and tables on the host first.  Returns (o [B, H, D_v], lse [B, H])."""
     torch = _torch()
     lib = load_library()
     for name, t in (("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
@@ -310,11 +402,12 @@ def mla_decode_sparse(q, kv_cache, block_table, topk_indices, topk_lens, scale: 
     shape = shape_of(q, kv_cache, block_table, kv_dtype=kv_dtype, o_dtype=o_dtype)
     B, H = shape.batch, shape.num_heads
     topk = int(topk_indices.shape[1])
+    if check:
+        mla_check_inputs(shape, block_table, None, topk_indices, topk_lens)
     if num_kv_splits is None:
         if num_cus is None:
             num_cus = torch.cuda.get_device_properties(q.device).multi_processor_count
-        split_mode, num_kv_splits, _ = mla_plan(shape, topk, int(topk_lens.sum().item()),
-                                                num_cus)
+        split_mode, num_kv_splits, _ = mla_plan(shape, topk, int(total_topk or 0), num_cus)
     elif split_mode is None:
         split_mode = SPLIT_PER_SEQUENCE
     ws_need = mla_workspace_size(shape, split_mode, num_kv_splits)

@@ -6,7 +6,9 @@ types), loaded by the ctypes binding in this package.
 
 The stage-1 kernel source is compiled once per group of template instances
 (MLA_STAGE1_GROUP 0..9) and once for the rest (MLA_MAIN); the translation
-units build in parallel and are linked into one library.
+units build in parallel and are linked into one library.  A second, separate
+library, libmla_peaks.so, holds the measured-ceiling probes the benchmark runs
+(`bench.py --peaks`); the decode path never loads it.
 """
 from __future__ import annotations
 
@@ -22,12 +24,14 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libmla.so")
+PEAKS_LIB_PATH = os.path.join(PKG_DIR, "libmla_peaks.so")
+PEAKS_SRC = os.path.join(CSRC, "mla_peaks.hip")
 KERNELS = os.path.join(CSRC, "mla_kernels.hip")
 # (source, extra defines) of every translation unit
 UNITS = ([(os.path.join(CSRC, "mla_api.cpp"), []), (os.path.join(CSRC, "mla_merge.hip"), []),
           (KERNELS, ["-DMLA_MAIN"])] +
          [(KERNELS, [f"-DMLA_STAGE1_GROUP={g}"]) for g in range(10)])
-SOURCES = sorted({u[0] for u in UNITS})
+SOURCES = sorted({u[0] for u in UNITS} | {PEAKS_SRC})
 ARCH = "gfx950"
 
 
@@ -83,6 +87,15 @@ def build(verbose: bool = True) -> str:
         if verbose and (msgs or lmsgs):
             print("\n".join(msgs + lmsgs), file=sys.stderr)
         os.replace(tmp_lib, LIB_PATH)
+        # the probe library: one translation unit, linked on its own
+        tmp_peaks = PEAKS_LIB_PATH + ".tmp"
+        cmd = [hipcc(), *_flags(), "-shared", PEAKS_SRC, "-o", tmp_peaks]
+        if verbose:
+            print("[libmla] " + " ".join(cmd), flush=True)
+        rc, pmsgs = _run(cmd)
+        if rc != 0:
+            raise RuntimeError("libmla_peaks build failed:\n" + "\n".join(pmsgs))
+        os.replace(tmp_peaks, PEAKS_LIB_PATH)
     return LIB_PATH
 
 

@@ -175,7 +175,30 @@ mla_status mla_plan(const mla_shape* shape, int32_t max_seq_len, int64_t total_s
                       num_kv_splits, workspace_bytes);
 }
 
-static mla_status decode_stages(const mla_shape* shape, int32_t q_len, const void* q,
+// The query of a call as two parts with strides (see mla_query in mla.h);
+// a contiguous q [B, rows, D] is q_nope = q, q_pe = q + D_v, row stride D.
+static mla_query contiguous_query(const mla_shape* s, int32_t q_len, const void* q) {
+  mla_query x;
+  memset(&x, 0, sizeof(x));
+  if (!s || !q) return x;  // decode_stages reports the missing shape or query
+  const int64_t rows = (int64_t)s->num_heads * q_len;
+  x.q_nope = q;
+  x.q_pe = reinterpret_cast<const uint16_t*>(q) + s->kv_lora_rank;
+  x.nope_seq_stride = x.pe_seq_stride = rows * s->head_size;
+  x.nope_row_stride = x.pe_row_stride = s->head_size;
+  return x;
+}
+
+static bool query_ok(const mla_query* q) {
+  // every 8-element (16-byte) chunk a lane loads must be aligned
+  const int64_t st[4] = {q->nope_seq_stride, q->nope_row_stride, q->pe_seq_stride,
+                         q->pe_row_stride};
+  for (int64_t v : st)
+    if (v < 0 || v % 8 != 0 || v > ((int64_t)1 << 40)) return false;
+  return aligned(q->q_nope, 16) && aligned(q->q_pe, 16);
+}
+
+static mla_status decode_stages(const mla_shape* shape, int32_t q_len, const mla_query* qd,
                                 const void* kv_cache,
                                 const int32_t* block_table, const int32_t* seq_lens,
                                 float scale, int32_t page_size, float k_scale,
@@ -190,7 +213,8 @@ static mla_status decode_stages(const mla_shape* shape, int32_t q_len, const voi
   shape = &rs;
   st = check_shape(shape);
   if (st != MLA_OK) return st;
-  if (!q || !kv_cache || !block_table || !seq_lens || !o || !lse) return MLA_ERR_NULL;
+  if (!qd || !qd->q_nope || !qd->q_pe || !kv_cache || !block_table || !seq_lens || !o || !lse)
+    return MLA_ERR_NULL;
   if (page_size != shape->page_size) return MLA_ERR_PAGE_SIZE;
   if (split_mode != MLA_SPLIT_PER_SEQUENCE && split_mode != MLA_SPLIT_BALANCED)
     return MLA_ERR_SPLITS;
@@ -202,7 +226,7 @@ static mla_status decode_stages(const mla_shape* shape, int32_t q_len, const voi
   const bool fp8 = shape->kv_dtype != MLA_BF16;
   const bool per_token = per_token_kind(shape->kv_dtype) != 0;
   if (fp8 && !per_token && !(isfinite(k_scale) && k_scale > 0.f)) return MLA_ERR_ARGUMENT;
-  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+  if (!query_ok(qd) || !aligned(kv_cache, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
       !aligned(block_table, 4) || !aligned(seq_lens, 4))
     return MLA_ERR_ARGUMENT;
   const WorkspaceLayout wl = workspace_layout(shape->batch, shape->num_heads,
@@ -213,7 +237,12 @@ static mla_status decode_stages(const mla_shape* shape, int32_t q_len, const voi
   }
 
   DecodeArgs a;
-  a.q = q;
+  a.q_nope = qd->q_nope;
+  a.q_pe = qd->q_pe;
+  a.qn_seq = qd->nope_seq_stride;
+  a.qn_row = qd->nope_row_stride;
+  a.qp_seq = qd->pe_seq_stride;
+  a.qp_row = qd->pe_row_stride;
   a.kv = kv_cache;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
@@ -237,6 +266,7 @@ static mla_status decode_stages(const mla_shape* shape, int32_t q_len, const voi
   a.scale = scale;
   a.k_scale = k_scale;
   a.pool_bytes = (uint64_t)shape->num_blocks * shape->page_size * kv_row_bytes(*shape);
+  a.num_blocks = shape->num_blocks;
   if (topk_idx) {
     a.topk_idx = topk_idx;
     a.topk_stride = topk;
@@ -249,7 +279,8 @@ mla_status mla_decode(const mla_shape* shape, const void* q, const void* kv_cach
                       int32_t page_size, float k_scale, int32_t num_kv_splits,
                       int32_t split_mode, void* o, float* lse, void* workspace,
                       size_t workspace_bytes, void* hip_stream) {
-  return decode_stages(shape, 1, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
+  const mla_query qd = contiguous_query(shape, 1, q);
+  return decode_stages(shape, 1, &qd, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
                        num_kv_splits, split_mode, o, lse, workspace, workspace_bytes, hip_stream,
                        kBothStages);
 }
@@ -259,9 +290,21 @@ mla_status mla_decode_mtp(const mla_shape* shape, int32_t q_len, const void* q,
                       float scale, int32_t page_size, float k_scale, int32_t num_kv_splits,
                       int32_t split_mode, void* o, float* lse, void* workspace,
                       size_t workspace_bytes, void* hip_stream) {
-  return decode_stages(shape, q_len, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
+  const mla_query qd = contiguous_query(shape, q_len, q);
+  return decode_stages(shape, q_len, &qd, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
                        num_kv_splits, split_mode, o, lse, workspace, workspace_bytes, hip_stream,
                        kBothStages);
+}
+
+mla_status mla_decode_split_q(const mla_shape* shape, int32_t q_len, const mla_query* q,
+                              const void* kv_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, float scale, int32_t page_size,
+                              float k_scale, int32_t num_kv_splits, int32_t split_mode, void* o,
+                              float* lse, void* workspace, size_t workspace_bytes,
+                              void* hip_stream) {
+  return decode_stages(shape, q_len, q, kv_cache, block_table, seq_lens, scale, page_size,
+                       k_scale, num_kv_splits, split_mode, o, lse, workspace, workspace_bytes,
+                       hip_stream, kBothStages);
 }
 
 mla_status mla_decode_stage1(const mla_shape* shape, const void* q, const void* kv_cache,
@@ -269,7 +312,8 @@ mla_status mla_decode_stage1(const mla_shape* shape, const void* q, const void* 
                              int32_t page_size, float k_scale, int32_t num_kv_splits,
                              int32_t split_mode, void* o, float* lse, void* workspace,
                              size_t workspace_bytes, void* hip_stream) {
-  return decode_stages(shape, 1, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
+  const mla_query qd = contiguous_query(shape, 1, q);
+  return decode_stages(shape, 1, &qd, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
                        num_kv_splits, split_mode, o, lse, workspace, workspace_bytes, hip_stream,
                        kStage1);
 }
@@ -279,7 +323,8 @@ mla_status mla_decode_mtp_stage1(const mla_shape* shape, int32_t q_len, const vo
                       float scale, int32_t page_size, float k_scale, int32_t num_kv_splits,
                       int32_t split_mode, void* o, float* lse, void* workspace,
                       size_t workspace_bytes, void* hip_stream) {
-  return decode_stages(shape, q_len, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
+  const mla_query qd = contiguous_query(shape, q_len, q);
+  return decode_stages(shape, q_len, &qd, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
                        num_kv_splits, split_mode, o, lse, workspace, workspace_bytes, hip_stream,
                        kStage1);
 }
@@ -289,7 +334,8 @@ mla_status mla_decode_stage2(const mla_shape* shape, const void* q, const void* 
                              int32_t page_size, float k_scale, int32_t num_kv_splits,
                              int32_t split_mode, void* o, float* lse, void* workspace,
                              size_t workspace_bytes, void* hip_stream) {
-  return decode_stages(shape, 1, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
+  const mla_query qd = contiguous_query(shape, 1, q);
+  return decode_stages(shape, 1, &qd, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
                        num_kv_splits, split_mode, o, lse, workspace, workspace_bytes, hip_stream,
                        kStage2);
 }
@@ -299,7 +345,8 @@ mla_status mla_decode_mtp_stage2(const mla_shape* shape, int32_t q_len, const vo
                       float scale, int32_t page_size, float k_scale, int32_t num_kv_splits,
                       int32_t split_mode, void* o, float* lse, void* workspace,
                       size_t workspace_bytes, void* hip_stream) {
-  return decode_stages(shape, q_len, q, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
+  const mla_query qd = contiguous_query(shape, q_len, q);
+  return decode_stages(shape, q_len, &qd, kv_cache, block_table, seq_lens, scale, page_size, k_scale,
                        num_kv_splits, split_mode, o, lse, workspace, workspace_bytes, hip_stream,
                        kStage2);
 }
@@ -325,7 +372,8 @@ static mla_status check_sparse(const mla_shape* shape, int32_t topk, const int32
                   void* workspace, size_t workspace_bytes, void* hip_stream) {                  \
     const mla_status st = check_sparse(shape, topk, topk_indices, topk_lens);                   \
     if (st != MLA_OK) return st;                                                                \
-    return decode_stages(shape, 1, q, kv_cache, block_table, topk_lens, scale, page_size,       \
+    const mla_query qd = contiguous_query(shape, 1, q);                                         \
+    return decode_stages(shape, 1, &qd, kv_cache, block_table, topk_lens, scale, page_size,     \
                          k_scale, num_kv_splits, split_mode, o, lse, workspace,                 \
                          workspace_bytes, hip_stream, STAGES, topk_indices, topk);              \
   }
@@ -333,6 +381,47 @@ MLA_SPARSE_ENTRY(mla_decode_sparse, kBothStages)
 MLA_SPARSE_ENTRY(mla_decode_sparse_stage1, kStage1)
 MLA_SPARSE_ENTRY(mla_decode_sparse_stage2, kStage2)
 #undef MLA_SPARSE_ENTRY
+
+mla_status mla_check_inputs(const mla_shape* shape, const int32_t* block_table,
+                            const int32_t* seq_lens, int32_t topk, const int32_t* topk_indices,
+                            const int32_t* topk_lens, int64_t* bad_index) {
+  if (bad_index) *bad_index = -1;
+  const mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!block_table) return MLA_ERR_NULL;
+  const bool sparse = topk_indices != nullptr || topk_lens != nullptr;
+  if (sparse && (!topk_indices || !topk_lens)) return MLA_ERR_NULL;
+  if (!sparse && !seq_lens) return MLA_ERR_NULL;
+  if (sparse && topk < 1) return MLA_ERR_ARGUMENT;
+  const int64_t W = shape->max_blocks_per_seq, P = shape->page_size;
+  const int64_t cap = W * P;  // positions one table row can address
+  auto bad = [&](int64_t i) {
+    if (bad_index) *bad_index = i;
+    return MLA_ERR_TABLE;
+  };
+  auto page_ok = [&](int64_t b, int64_t j) {
+    const int32_t pg = block_table[b * W + j];
+    return pg >= 0 && pg < shape->num_blocks;
+  };
+  for (int64_t b = 0; b < shape->batch; ++b) {
+    if (!sparse) {
+      // every page a sequence of n positions reads: table entries 0 .. ceil(n/P) - 1
+      const int64_t n = seq_lens[b];
+      if (n < 0 || n > cap) return bad(b);
+      for (int64_t j = 0; j < (n + P - 1) / P; ++j)
+        if (!page_ok(b, j)) return bad(b * W + j);
+    } else {
+      // every listed position, and the page it goes through
+      const int64_t k = topk_lens[b];
+      if (k < 0 || k > topk) return bad(b);
+      for (int64_t e = 0; e < k; ++e) {
+        const int64_t pos = topk_indices[b * topk + e];
+        if (pos < 0 || pos >= cap || !page_ok(b, pos / P)) return bad(b * topk + e);
+      }
+    }
+  }
+  return MLA_OK;
+}
 
 mla_status mla_merge_shards(int32_t num_shards, int64_t rows, int32_t d_v, const void* o_parts,
                             int32_t parts_dtype, const float* lse_parts, int32_t lse_base,
@@ -367,12 +456,13 @@ const char* mla_status_string(int32_t status) {
     case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
     case MLA_ERR_HEAD_SIZE: return "MLA_ERR_HEAD_SIZE: head_size must be 576 or 320 with kv_lora_rank = head_size - 64";
     case MLA_ERR_PAGE_SIZE: return "MLA_ERR_PAGE_SIZE: page_size must be a positive multiple of 16 and match the shape";
-    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: q must be bf16, kv bf16, fp8 e4m3fn (per-tensor or per-token scale) or per-token int8, o bf16 or fp32";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: q must be bf16, kv bf16, fp8 e4m3fn (per-tensor or per-token scale) or per-token int8 / int4, o bf16 or fp32";
     case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: batch, heads (multiple of 16), num_blocks or table width out of range";
     case MLA_ERR_SPLITS: return "MLA_ERR_SPLITS: num_kv_splits or split_mode out of range";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
     case MLA_ERR_LAUNCH: return "MLA_ERR_LAUNCH: HIP kernel launch failed";
-    case MLA_ERR_ARGUMENT: return "MLA_ERR_ARGUMENT: non-finite/non-positive scale or k_scale, num_cus < 1, q_len outside [1, MLA_MAX_Q_LEN], or a misaligned pointer";
+    case MLA_ERR_ARGUMENT: return "MLA_ERR_ARGUMENT: non-finite/non-positive scale or k_scale, num_cus < 1, q_len outside [1, MLA_MAX_Q_LEN], topk < 1, or a misaligned pointer or query stride";
+    case MLA_ERR_TABLE: return "MLA_ERR_TABLE: a sequence length, block-table entry or top-k entry is out of range";
     default: return "unknown mla_status";
   }
 }

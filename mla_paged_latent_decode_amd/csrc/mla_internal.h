@@ -84,7 +84,12 @@ constexpr int stage1_lds_bytes(int hpw, int waves, int d, bool fp8, int pt = 0) 
 }
 
 struct DecodeArgs {
-  const void* q;
+  // query rows [q_nope | q_pe] of sequence b, row r (query token x heads +
+  // head): q_nope + b * qn_seq + r * qn_row and q_pe + b * qp_seq + r * qp_row
+  // (bf16 elements)
+  const void* q_nope;
+  const void* q_pe;
+  int64_t qn_seq, qn_row, qp_seq, qp_row;
   const void* kv;
   const int32_t* block_table;
   const int32_t* seq_lens;
@@ -112,6 +117,7 @@ struct DecodeArgs {
   const int32_t* topk_idx = nullptr;
   int32_t topk_stride = 0;
   uint64_t pool_bytes = 0;  // num_blocks * page_size * head_size * kv bytes
+  int32_t num_blocks = 0;   // pages in the pool (page numbers outside read as zero rows)
 };
 
 enum Stages { kStage1 = 1, kStage2 = 2, kBothStages = 3 };

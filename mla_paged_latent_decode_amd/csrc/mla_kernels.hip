@@ -262,7 +262,13 @@ __device__ __forceinline__ void store_out4(void* o, int o_f32, size_t idx, f32x4
 // Kernel parameters of stage 1 (one definition for every translation unit
 // built from this source, see the dispatch section).
 struct Stage1Params {
-  const __bf16* q;
+  // The query rows: row r (= query token x heads + head) of sequence b is
+  // [q_nope (D_v) | q_pe (64)], the two parts read from two base pointers
+  // with their own sequence and row strides (in elements), so that a caller
+  // holding them as separate tensors needs no concatenation.
+  const __bf16* q_nope;
+  const __bf16* q_pe;
+  int64_t qn_seq, qn_row, qp_seq, qp_row;
   const uint8_t* kv;
   const int32_t* block_table;
   const int32_t* seq_lens;
@@ -274,6 +280,12 @@ struct Stage1Params {
   int32_t batch, heads, page_size, bt_stride;
   int32_t o_f32, split_mode, num_splits, head_chunks;
   int32_t seg_cost;  // balanced mode: virtual tiles charged per sequence start
+  // Memory safety: every length read from seq_lens is clamped to [0, len_cap]
+  // (len_cap = bt_stride * page_size, or topk for sparse decode), so no read
+  // goes past a block-table or index row; a page number outside
+  // [0, num_blocks) reads as zero rows.
+  int32_t len_cap;
+  uint32_t num_blocks;
   // Multi-token decode: the rows are q_len query tokens x heads_per_token
   // heads (row = token * heads_per_token + head).  Token i of a sequence with
   // n keys sees positions t < n - q_len + 1 + i.  Plain decode: q_len = 1.
@@ -308,6 +320,13 @@ __device__ __forceinline__ int unit_of_tile(int64_t x, int64_t TT, int U) {
 
 __device__ __forceinline__ int tiles_of(int n) { return (n + kTile - 1) / kTile; }
 
+// Length of sequence b, clamped to [0, cap]: the kernels never read past the
+// table (or index list) row a length implies, whatever seq_lens holds.
+__device__ __forceinline__ int seq_len_at(const int32_t* seq_lens, int b, int cap) {
+  const int n = seq_lens[b];
+  return n < 0 ? 0 : (n > cap ? cap : n);
+}
+
 // Inclusive wave prefix sum.
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
@@ -325,11 +344,12 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 // therefore streams fewer tiles, and units finish together.
 __device__ __forceinline__ int cost_of(int n, int sc) { return n > 0 ? sc + tiles_of(n) : 0; }
 
-__device__ __forceinline__ int64_t total_cost(const int32_t* seq_lens, int B, int sc, int lane) {
+__device__ __forceinline__ int64_t total_cost(const int32_t* seq_lens, int B, int sc, int cap,
+                                              int lane) {
   int64_t tot = 0;
   for (int c0 = 0; c0 < B; c0 += 64) {
     int b = c0 + lane;
-    int nt = b < B ? cost_of(seq_lens[b], sc) : 0;
+    int nt = b < B ? cost_of(seq_len_at(seq_lens, b, cap), sc) : 0;
     int s = wave_incl_scan(nt, lane);
     tot += __shfl(s, 63, 64);
   }
@@ -510,10 +530,14 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     // range check turns into zero rows.
     const int32_t* sp_list = SP ? p.topk_idx + (int64_t)b * p.topk_stride : nullptr;
     int spA0 = -1, spA1 = -1, spG0 = 0, spG1 = 0, spB0 = -1, spB1 = -1;
+    // (positions outside [0, bt_stride * P) count as past the segment: zero rows)
+    const uint32_t pos_cap = (uint32_t)min((int64_t)p.bt_stride * P, (int64_t)0x7fffffff);
     auto sp_entries = [&](int x, int& i0, int& i1) __attribute__((always_inline)) {
       const int e0 = ts + x * kTile + dma_t16;
       i0 = e0 < te ? sp_list[e0] : -1;
       i1 = e0 + 16 < te ? sp_list[e0 + 16] : -1;
+      if ((uint32_t)i0 >= pos_cap) i0 = -1;
+      if ((uint32_t)i1 >= pos_cap) i1 = -1;
     };
     auto sp_block = [&](int pos) __attribute__((always_inline)) {
       return p.page_shift >= 0 ? pos >> p.page_shift : pos / P;
@@ -523,9 +547,10 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       g1 = i1 >= 0 ? bt_row[sp_block(i1)] : 0;
     };
     auto sp_offset = [&](int pos, int page) __attribute__((always_inline)) {
-      return pos >= 0 ? ((uint32_t)page * (uint32_t)P + (uint32_t)(pos - sp_block(pos) * P)) *
-                            (uint32_t)C::SRC_ROW
-                      : p.pool_bytes;
+      return pos >= 0 && (uint32_t)page < p.num_blocks
+                 ? ((uint32_t)page * (uint32_t)P + (uint32_t)(pos - sp_block(pos) * P)) *
+                       (uint32_t)C::SRC_ROW
+                 : p.pool_bytes;
     };
     if constexpr (SP) {
       sp_entries(0, spA0, spA1);
@@ -561,7 +586,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       }
 #pragma unroll
       for (int th = 0; th < 2; ++th) {
-        const int nv = uniform(max(0, min(16, te - cur_tok)));
+        int nv = uniform(max(0, min(16, te - cur_tok)));
         uint64_t base = reinterpret_cast<uint64_t>(p.kv);
         if (nv > 0) {
           // The window load is read inside its own branch, so that the wait
@@ -574,7 +599,11 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           } else {
             page = __builtin_amdgcn_readlane(win, cur_lb - win_lb);
           }
-          base += (uint64_t)((page * P + cur_off) * (int64_t)C::SRC_ROW);
+          // a page outside the pool reads as zero rows (an empty resource)
+          if ((uint64_t)page < (uint64_t)p.num_blocks)
+            base += (uint64_t)((page * P + cur_off) * (int64_t)C::SRC_ROW);
+          else
+            nv = 0;
         }
         // every field wave-uniform, so the resource lives in SGPRs
         base = ((uint64_t)(uint32_t)uniform((int)(base >> 32)) << 32) |
@@ -750,23 +779,31 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     LDS_AS uint8_t* qlds =
         (LDS_AS uint8_t*)ring + NBUF * C::TILE_BYTES + C::STG_BYTES + wave * C::QLDS * 1024;
     {
-      const __bf16* qb = p.q + ((int64_t)b * H + h0) * D;
+      // this lane's row of q: columns d < D_v from q_nope, the rest from q_pe
+      const int qrow = h0 + (HPW == 32 ? (lane & 31) : (lane & 15));
+      const int dl = HPW == 32 ? 8 * (lane >> 5) : 8 * (lane >> 4);
+      const __bf16* qn = p.q_nope + (int64_t)b * p.qn_seq + (int64_t)qrow * p.qn_row + dl;
+      const __bf16* qp = p.q_pe + (int64_t)b * p.qp_seq + (int64_t)qrow * p.qp_row + dl;
+      constexpr int KW = HPW == 32 ? 16 : 32;  // columns per k-step
+      auto qchunk = [&](int ks) __attribute__((always_inline)) {
+        return ks * KW < DV ? *reinterpret_cast<const bf16x8*>(qn + ks * KW)
+                            : *reinterpret_cast<const bf16x8*>(qp + (ks * KW - DV));
+      };
+      static_assert(DV % 32 == 0, "a k-step never straddles q_nope and q_pe");
       if constexpr (HPW == 32) {
-        const __bf16* qr = qb + (int64_t)(lane & 31) * D + 8 * (lane >> 5);
 #pragma unroll
-        for (int ks = 0; ks < C::NQR; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qr + 16 * ks);
+        for (int ks = 0; ks < C::NQR; ++ks) qf[ks] = qchunk(ks);
 #pragma unroll
         for (int ks = C::NQR; ks < C::NKS; ++ks) {
           if constexpr (kEarlyRing)
-            qtmp[ks - C::NQR] = *reinterpret_cast<const bf16x8*>(qr + 16 * ks);
+            qtmp[ks - C::NQR] = qchunk(ks);
           else
             *reinterpret_cast<LDS_AS bf16x8*>(qlds + (ks - C::NQR) * 1024 + lane * 16) =
-                *reinterpret_cast<const bf16x8*>(qr + 16 * ks);
+                qchunk(ks);
         }
       } else {
-        const __bf16* qr = qb + (int64_t)(lane & 15) * D + 8 * (lane >> 4);
 #pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qr + 32 * ks);
+        for (int ks = 0; ks < C::NKS; ++ks) qf[ks] = qchunk(ks);
       }
     }
 
@@ -1439,7 +1476,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     const int S = p.num_splits;
     b = unit / S;
     const int s = unit % S;
-    const int n = p.seq_lens[b];
+    const int n = seq_len_at(p.seq_lens, b, p.len_cap);
     if (n <= 0) {
       if (s == 0) {  // empty sequence: o = 0, lse = -inf
         const int h = h0 + (HPW == 32 ? (lane & 31) : (lane & 15));
@@ -1462,7 +1499,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   } else {
     // the unit covers positions [a0, a1) of the batch's cost stream
     const int U = p.num_splits;
-    TC = uniform64(total_cost(p.seq_lens, p.batch, p.seg_cost, lane));
+    TC = uniform64(total_cost(p.seq_lens, p.batch, p.seg_cost, p.len_cap, lane));
     if (TC == 0) return;
     a0 = (int64_t)unit * TC / U;
     a1 = (int64_t)(unit + 1) * TC / U;
@@ -1470,7 +1507,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     // first sequence whose cost range reaches past a0, and where it starts
     for (int c0 = 0; c0 < p.batch; c0 += 64) {
       const int bl = c0 + lane;
-      const int ntl = bl < p.batch ? cost_of(p.seq_lens[bl], p.seg_cost) : 0;
+      const int ntl = bl < p.batch ? cost_of(seq_len_at(p.seq_lens, bl, p.len_cap), p.seg_cost) : 0;
       const int incl = wave_incl_scan(ntl, lane);
       const uint64_t past = __builtin_amdgcn_ballot_w64(bl < p.batch && st + incl > a0);
       if (past) {
@@ -1486,7 +1523,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   }
   for (;;) {
     if (p.split_mode != 0) {
-      const int n = p.seq_lens[b];
+      const int n = seq_len_at(p.seq_lens, b, p.len_cap);
       const int nt = tiles_of(n);
       const int64_t rs = st + (nt > 0 ? p.seg_cost : 0);  // position of tile 0
       const int64_t lo = (a0 > rs ? a0 : rs) - rs;
@@ -1524,6 +1561,7 @@ struct Stage2Params {
   float* lse;
   int32_t batch, heads, o_f32, split_mode, num_splits, head_groups, kgroups;
   int32_t seg_cost;  // balanced mode: the same cost stream as stage 1
+  int32_t len_cap;   // the same length clamp as stage 1
 };
 
 // One workgroup per (sequence, 8/KG heads, 256 output columns), 256 threads:
@@ -1564,7 +1602,7 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
   const int H = p.heads;
   const int h = hg * HPB + hl;  // < H: H is a multiple of 16
   const int v = vc * kS2Cols + 8 * j;
-  const int n = p.seq_lens[b];
+  const int n = seq_len_at(p.seq_lens, b, p.len_cap);
 
   int first, count;
   bool all_live = true;
@@ -1589,7 +1627,7 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
     int64_t before = 0, TT = 0;
     for (int c0 = 0; c0 < p.batch; c0 += 64) {
       const int bl = c0 + lane;
-      const int nt = bl < p.batch ? cost_of(p.seq_lens[bl], p.seg_cost) : 0;
+      const int nt = bl < p.batch ? cost_of(seq_len_at(p.seq_lens, bl, p.len_cap), p.seg_cost) : 0;
       const int incl = wave_incl_scan(nt, lane);
       const int tot = __shfl(incl, 63, 64);
       if (b >= c0 + 64) before += tot;
@@ -1762,7 +1800,12 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   const HeadTiling ht = head_tiling(a.heads);
 
   Stage1Params sp;
-  sp.q = reinterpret_cast<const __bf16*>(a.q);
+  sp.q_nope = reinterpret_cast<const __bf16*>(a.q_nope);
+  sp.q_pe = reinterpret_cast<const __bf16*>(a.q_pe);
+  sp.qn_seq = a.qn_seq;
+  sp.qn_row = a.qn_row;
+  sp.qp_seq = a.qp_seq;
+  sp.qp_row = a.qp_row;
   sp.kv = reinterpret_cast<const uint8_t*>(a.kv);
   sp.block_table = a.block_table;
   sp.seq_lens = a.seq_lens;
@@ -1785,6 +1828,13 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   sp.topk_idx = a.topk_idx;
   sp.topk_stride = a.topk_stride;
   sp.pool_bytes = (uint32_t)a.pool_bytes;
+  sp.num_blocks = (uint32_t)a.num_blocks;
+  {
+    // sparse decode: a list holds at most topk entries; dense decode: a table
+    // row of bt_stride pages holds at most bt_stride * page_size positions
+    const int64_t cap = a.topk_idx ? (int64_t)a.topk_stride : (int64_t)a.bt_stride * a.page_size;
+    sp.len_cap = (int32_t)(cap < 0x7fffffff ? cap : 0x7fffffff);
+  }
   sp.page_shift = -1;
   for (int sh = 0; sh < 31; ++sh)
     if ((1 << sh) == a.page_size) sp.page_shift = sh;
@@ -1830,6 +1880,7 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   s2.split_mode = a.split_mode;
   s2.num_splits = a.num_splits;
   s2.seg_cost = sp.seg_cost;
+  s2.len_cap = sp.len_cap;
   // partial groups per head: about a quarter of the mean partial count per
   // sequence (units / batch + 1), a power of two up to 8
   const int per_seq = a.split_mode == 0 ? a.num_splits : a.num_splits / a.batch + 1;

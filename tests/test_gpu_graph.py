@@ -81,6 +81,12 @@ def test_captured_decode_replays_match_eager(mla, mode, splits):
             slack = np.exp2(np.floor(np.log2(ax)) - 8)  # bf16 output rounding
             assert (np.abs(o_np - ro) - slack).max() <= 1e-2
             assert np.abs(l_g.cpu().numpy() - rl).max() <= 1e-3
+            # the same launch configuration with fp32 output, at the plain tolerances
+            o32, l32 = mla.mla_decode(q, kv, bt, sl_d, w.scale, w.page_size, w.k_scale, splits,
+                                      split_mode=mode, workspace=ws, o_dtype=torch.float32)
+            torch.cuda.synchronize()
+            assert np.abs(o32.cpu().numpy().astype(np.float64) - ro).max() <= 1e-2
+            assert np.abs(l32.cpu().numpy().astype(np.float64) - rl).max() <= 1e-3
 
 
 @pytest.mark.parametrize("kind", ["int4_per_token", "mtp", "sparse"])

@@ -149,21 +149,21 @@ def test_mtp_page_permutation_is_bitwise_invariant(mla, mode, splits):
 
 def test_mtp_full_size(mla):
     """The dsv3_mtp2 workload (B=64, q_len=2, H=128) at the planner's launch
-    configuration and at the pages' split count, on sampled sequences."""
+    configuration, at the pages' split count and in the single-split mode, every
+    sequence compared with the oracle (fp32 output at the plain tolerances, bf16
+    output beyond its final rounding)."""
     inp = W.generate("dsv3_mtp2")
     w = inp.workload
     dev_inputs = to_dev(inp)
     sl = np.asarray(inp.seq_lens)
-    rng = np.random.default_rng(1234)
-    picks = sorted({int(np.argmax(sl)), int(np.argmin(sl)), 0, len(sl) - 1}
-                   | set(rng.choice(len(sl), size=6, replace=False).tolist()))
-    ro, rl = ref(inp, picks)
+    ro, rl = ref(inp)
     shape = mla.shape_of(*dev_inputs[:2], dev_inputs[2])
     max_len, tot = int(sl.max()), int(sl.sum())
     mode, units, _ = mla.mla_plan(shape, max_len, tot, 256, q_len=w.q_len)
-    print(f"dsv3_mtp2: tokens={tot} plan mode={mode} units={units} sampled={picks}", flush=True)
+    print(f"dsv3_mtp2: tokens={tot} plan mode={mode} units={units}", flush=True)
     for mode, splits in [(mode, units)] + [(0, s) for s in w.parity_splits]:
+        label = f"dsv3_mtp2 mode={mode} S={splits}"
+        o, lse = run_gpu(mla, inp, splits, mode, o_dtype=torch.float32, dev_inputs=dev_inputs)
+        assert_close(inp, o, lse, ro, rl, label + " o=f32")
         o, lse = run_gpu(mla, inp, splits, mode, dev_inputs=dev_inputs)
-        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-        assert_close(inp, o[picks], lse[picks], ro, rl, f"dsv3_mtp2 mode={mode} S={splits}",
-                     batches=picks)
+        assert_close(inp, o, lse, ro, rl, label + " o=bf16", rounding_slack=True)

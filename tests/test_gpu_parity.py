@@ -189,9 +189,11 @@ def test_fp32_output(mla):
 def test_empty_sequences(mla, mode, splits):
     inp = W.small_case(seed=9, batch=5, num_heads=16, head_size=576, kv_lora_rank=512,
                        page_size=16, seq_lens=(0, 50, 0, 1, 0))
-    o, lse = run_gpu(mla, inp, splits, mode)
     ro, rl = ref(inp)
-    assert_close(inp, o, lse, ro, rl, f"empty mode={mode} S={splits}", rounding_slack=True)
+    o, lse = run_gpu(mla, inp, splits, mode, o_dtype=torch.float32)
+    assert_close(inp, o, lse, ro, rl, f"empty mode={mode} S={splits} o=f32")
+    o, lse = run_gpu(mla, inp, splits, mode)
+    assert_close(inp, o, lse, ro, rl, f"empty mode={mode} S={splits} o=bf16", rounding_slack=True)
 
 
 # ---------------------------------------------------------------- bit-exact indexing
@@ -244,29 +246,27 @@ def test_split_results_are_reproducible(mla):
 
 # ---------------------------------------------------------------- full-size configs
 
-def sample_batches(inp, k=6):
-    sl = np.asarray(inp.seq_lens)
-    pick = {int(np.argmax(sl)), int(np.argmin(sl)), 0, len(sl) - 1}
-    rng = np.random.default_rng(1234)
-    pick |= set(rng.choice(len(sl), size=min(k, len(sl)), replace=False).tolist())
-    return sorted(pick)
-
-
 @pytest.mark.parametrize("name", ["dsv3", "skewed", "h320", "fp8"])
 def test_full_size_configs(mla, name):
+    """Every sequence of each full-size workload against the oracle, in the
+    planner's launch configuration, at the pages' split count per sequence and
+    in the single-split (deterministic) mode; fp32 output at the stated
+    tolerance, bf16 output at the same tolerance (these batches hold only
+    sequences of 256 positions or more, where |o| stays far below 1 and the
+    final bf16 rounding is below 2^-9)."""
     inp = W.generate(name)
     w = inp.workload
     dev_inputs = to_dev(inp)
-    picks = sample_batches(inp)
-    ro, rl = ref(inp, picks)
+    ro, rl = ref(inp)
     max_len, tot = int(inp.seq_lens.max()), int(inp.seq_lens.sum())
     shape = mla.shape_of(*dev_inputs[:2], dev_inputs[2])
     print(f"{name}: B={w.batch} H={w.num_heads} D={w.head_size} {w.kv_dtype} "
-          f"tokens={tot} sampled={picks}", flush=True)
+          f"tokens={tot}", flush=True)
     mode, units, _ = mla.mla_plan(shape, max_len, tot, 256)
     runs = [(mode, units)] + [(0, s) for s in w.parity_splits]
+    if (0, 1) not in runs:
+        runs.append((0, 1))
     for mode, splits in runs:
-        o, lse = run_gpu(mla, inp, splits, mode, dev_inputs=dev_inputs)
-        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-        assert_close(W.subset(inp, picks), o[picks], lse[picks], ro, rl,
-                     f"{name} mode={mode} S={splits}")
+        for o_dtype in (torch.float32, torch.bfloat16):
+            o, lse = run_gpu(mla, inp, splits, mode, o_dtype=o_dtype, dev_inputs=dev_inputs)
+            assert_close(inp, o, lse, ro, rl, f"{name} mode={mode} S={splits} o={o_dtype}")

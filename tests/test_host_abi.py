@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for code in range(10):
+    for code in range(11):
         s = mla.mla_status_string(code)
         assert s and "unknown" not in s
     assert "unknown" in mla.mla_status_string(99)
@@ -209,3 +209,116 @@ def test_merge_argument_checks_fail_before_launch():
     assert _merge_raw(base=2) == mla.MLA_ERR_ARGUMENT
     assert _merge_raw(op=264) == mla.MLA_ERR_ARGUMENT  # misaligned
     assert _merge_raw(lse=258) == mla.MLA_ERR_ARGUMENT
+
+
+# ---------------------------------------------------------------- host-side table checker
+
+def _tables(B=3, W=4, P=16, num_blocks=20):
+    import numpy as np
+    s = shape(batch=B, num_heads=16, page_size=P, num_blocks=num_blocks, max_blocks_per_seq=W)
+    bt = np.arange(B * W, dtype=np.int32).reshape(B, W) % num_blocks
+    sl = np.array([1, P * W, 17], dtype=np.int32)[:B]
+    return s, bt, sl
+
+
+def test_checker_accepts_valid_tables():
+    s, bt, sl = _tables()
+    mla.mla_check_inputs(s, bt, sl)
+    # entries past ceil(n / P) are never read, whatever they hold
+    bt2 = bt.copy()
+    bt2[0, 1:] = -7
+    bt2[2, 2:] = 10 ** 6
+    mla.mla_check_inputs(s, bt2, sl)
+
+
+@pytest.mark.parametrize("what,where", [
+    ("len_negative", 0), ("len_past_table", 1), ("page_negative", 2 * 4 + 1),
+    ("page_past_pool", 1 * 4 + 3)])
+def test_checker_names_the_first_bad_entry(what, where):
+    """Request isolation ("vLLM 中 Attention Kernel 如何并行处理多个请求",
+    section 十一): a request may reach only pool pages through its own table
+    row; a length beyond its row, or a page outside the pool, is refused and
+    the flat index of the offending element is reported."""
+    s, bt, sl = _tables()
+    bt, sl = bt.copy(), sl.copy()
+    if what == "len_negative":
+        sl[0] = -1
+    elif what == "len_past_table":
+        sl[1] = 16 * 4 + 1
+    elif what == "page_negative":
+        bt[2, 1] = -1
+    else:
+        bt[1, 3] = 20
+    with pytest.raises(ValueError, match=rf"flat index {where}\b.*MLA_ERR_TABLE"):
+        mla.mla_check_inputs(s, bt, sl)
+
+
+def test_checker_sparse_lists():
+    import numpy as np
+    s, bt, sl = _tables()
+    ti = np.zeros((3, 5), dtype=np.int32)
+    tl = np.array([5, 0, 2], dtype=np.int32)
+    ti[0] = [0, 63, 17, 17, 32]
+    ti[2, :2] = [5, 40]
+    ti[1] = -99  # length 0: never read
+    ti[2, 2:] = 10 ** 7  # past topk_lens[2]: never read
+    mla.mla_check_inputs(s, bt, None, ti, tl)
+    for mutate, where in ((lambda a, l: l.__setitem__(1, 6), 1),
+                          (lambda a, l: l.__setitem__(0, -1), 0),
+                          (lambda a, l: a.__setitem__((0, 3), 64), 3),
+                          (lambda a, l: a.__setitem__((2, 1), -1), 2 * 5 + 1)):
+        a, l = ti.copy(), tl.copy()
+        mutate(a, l)
+        with pytest.raises(ValueError, match=rf"flat index {where}\b"):
+            mla.mla_check_inputs(s, bt, None, a, l)
+    # a listed position whose page entry is outside the pool: position 63 (entry 1 of
+    # sequence 0) is the first to go through table slot 3
+    bt2 = bt.copy()
+    bt2[0, 3] = 20
+    with pytest.raises(ValueError, match=r"flat index 1\b"):
+        mla.mla_check_inputs(s, bt2, None, ti, tl)
+
+
+def test_checker_argument_errors():
+    import numpy as np
+    lib = mla.load_library()
+    s, bt, sl = _tables()
+    bad = ctypes.c_int64(5)
+    p = lambda a: a.ctypes.data  # noqa: E731
+    assert lib.mla_check_inputs(ctypes.byref(s), None, p(sl), 0, None, None,
+                                ctypes.byref(bad)) == mla.MLA_ERR_NULL
+    assert lib.mla_check_inputs(ctypes.byref(s), p(bt), None, 0, None, None,
+                                ctypes.byref(bad)) == mla.MLA_ERR_NULL
+    ti = np.zeros((3, 2), dtype=np.int32)
+    assert lib.mla_check_inputs(ctypes.byref(s), p(bt), None, 2, p(ti), None,
+                                ctypes.byref(bad)) == mla.MLA_ERR_NULL
+    assert lib.mla_check_inputs(ctypes.byref(s), p(bt), None, 0, p(ti), p(sl),
+                                ctypes.byref(bad)) == mla.MLA_ERR_ARGUMENT
+    assert lib.mla_check_inputs(ctypes.byref(shape(head_size=400)), p(bt), p(sl), 0, None,
+                                None, ctypes.byref(bad)) == mla.MLA_ERR_HEAD_SIZE
+    assert lib.mla_check_inputs(ctypes.byref(s), p(bt), p(sl), 0, None, None, None) == mla.MLA_OK
+
+
+# ---------------------------------------------------------------- split query (q_nope, q_pe)
+
+def test_split_query_argument_checks():
+    """mla_decode_split_q is refused before any launch for a NULL part, a
+    misaligned part or a stride that is not a non-negative multiple of 8."""
+    lib = mla.load_library()
+    s = shape(batch=2, num_heads=16, page_size=16, num_blocks=16, max_blocks_per_seq=8)
+    base = 1 << 20  # fake, aligned device addresses: every call here fails its checks first
+
+    def call(q):
+        return lib.mla_decode_split_q(ctypes.byref(s), 1, ctypes.byref(q) if q else None,
+                                      base, base, base, 0.07, 16, 1.0, 1, 0, base, base,
+                                      None, 0, None)
+    good = dict(q_nope=base, q_pe=base + 1024, nope_seq_stride=16 * 512, nope_row_stride=512,
+                pe_seq_stride=16 * 64, pe_row_stride=64)
+    assert call(None) == mla.MLA_ERR_NULL
+    assert call(mla.MlaQuery(**dict(good, q_pe=None))) == mla.MLA_ERR_NULL
+    assert call(mla.MlaQuery(**dict(good, q_pe=base + 8))) == mla.MLA_ERR_ARGUMENT
+    assert call(mla.MlaQuery(**dict(good, nope_row_stride=515))) == mla.MLA_ERR_ARGUMENT
+    assert call(mla.MlaQuery(**dict(good, pe_seq_stride=-64))) == mla.MLA_ERR_ARGUMENT
+    # a valid query with an invalid shape still fails on the shape
+    s.head_size = 400
+    assert call(mla.MlaQuery(**good)) == mla.MLA_ERR_HEAD_SIZE
