@@ -84,8 +84,10 @@ typedef enum mla_status {
   MLA_ERR_ARGUMENT = 9,  /* a non-finite or non-positive scale / k_scale, num_cus < 1,
                             q_len outside [1, MLA_MAX_Q_LEN], topk < 1, or a misaligned
                             pointer or query stride                                      */
-  MLA_ERR_TABLE = 10     /* mla_check_inputs: a length, block-table entry or top-k entry
+  MLA_ERR_TABLE = 10,    /* mla_check_inputs: a length, block-table entry or top-k entry
                             out of range                                                 */
+  MLA_ERR_SCRATCH = 11   /* mla_decode_noalloc: the split layout needs more workspace than
+                            the built-in scratch holds (mla_noalloc_scratch_bytes())     */
 } mla_status;
 
 typedef enum mla_dtype {
@@ -353,6 +355,31 @@ mla_status mla_decode_sparse_stage2(const mla_shape* shape, int32_t topk, const 
                                     int32_t num_kv_splits, int32_t split_mode, void* o,
                                     float* lse, void* workspace, size_t workspace_bytes,
                                     void* hip_stream);
+
+/* Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): mla_decode_mtp (q_len = 1: mla_decode) without the workspace
+ * arguments.  The stage-1 partials go to a scratch array built into the
+ * library, one copy per device, of mla_noalloc_scratch_bytes() bytes
+ * (64 MiB, held from the library's load until the process ends); the call
+ * itself allocates nothing, synchronises nothing and enqueues the same
+ * kernels as mla_decode_mtp with the same split plan, so its results are
+ * bitwise those of mla_decode_mtp.  A split layout whose
+ * mla_workspace_size_mtp() exceeds the scratch is refused with
+ * MLA_ERR_SCRATCH before anything is enqueued (plan fewer units or use
+ * mla_decode_mtp with a workspace).  The scratch needs no clearing: every
+ * byte a call reads is written earlier in the same call.  All calls on one
+ * device share its scratch: calls that may overlap in time on one device
+ * (concurrent streams, or calls from several host threads) race and must be
+ * serialised by the caller; calls in order on one stream are safe.  Every
+ * other argument, check and ownership rule is that of mla_decode_mtp. */
+mla_status mla_decode_noalloc(const mla_shape* shape, int32_t q_len, const void* q,
+                              const void* kv_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, float scale, int32_t page_size,
+                              float k_scale, int32_t num_kv_splits, int32_t split_mode, void* o,
+                              float* lse, void* hip_stream);
+/* Bytes of the built-in scratch of mla_decode_noalloc (pure host). */
+size_t mla_noalloc_scratch_bytes(void);
 
 /* Host-side check of the tables a decode call will read ("vLLM 中 Attention
  * Kernel 如何并行处理多个请求", section 十一: each request reaches the cache only

@@ -29,7 +29,8 @@ from typing import Optional, Tuple
 from . import _build
 
 __all__ = [
-    "MlaError", "mla_decode", "mla_decode_sparse", "mla_plan", "mla_check_inputs", "mla_workspace_size", "mla_pages_split_count",
+    "MlaError", "mla_decode", "mla_decode_sparse", "mla_plan", "mla_check_inputs",
+    "mla_decode_noalloc", "mla_noalloc_scratch_bytes", "mla_workspace_size", "mla_pages_split_count",
     "mla_status_string", "SPLIT_PER_SEQUENCE", "SPLIT_BALANCED", "library_path", "load_library",
     "MLA_BF16", "MLA_FP8_E4M3", "MLA_FP32", "MLA_FP8_E4M3_PER_TOKEN", "MLA_INT8_PER_TOKEN",
     "MLA_INT4_PER_TOKEN",
@@ -38,7 +39,7 @@ __all__ = [
 
 MLA_OK, MLA_ERR_NULL, MLA_ERR_HEAD_SIZE, MLA_ERR_PAGE_SIZE, MLA_ERR_DTYPE = 0, 1, 2, 3, 4
 MLA_ERR_SHAPE, MLA_ERR_SPLITS, MLA_ERR_WORKSPACE, MLA_ERR_LAUNCH, MLA_ERR_ARGUMENT = 5, 6, 7, 8, 9
-MLA_ERR_TABLE = 10
+MLA_ERR_TABLE, MLA_ERR_SCRATCH = 10, 11
 MLA_BF16, MLA_FP8_E4M3, MLA_FP32, MLA_FP8_E4M3_PER_TOKEN, MLA_INT8_PER_TOKEN = 0, 1, 2, 3, 4
 MLA_INT4_PER_TOKEN = 5  # two signed 4-bit codes per byte, element 2i in the low nibble
 MLA_PER_TOKEN_PAD = 16  # bytes after the codes of a per-token cache row (fp32 scale first)
@@ -112,6 +113,11 @@ def load_library():
                                            vp, vp, sz, vp]
         lib.mla_decode_split_q.restype = i32
         lib.mla_check_inputs.argtypes = [shp, vp, vp, i32, vp, vp, ctypes.POINTER(i64)]
+        lib.mla_decode_noalloc.argtypes = [shp, i32, vp, vp, vp, vp, ctypes.c_float, i32,
+                                           ctypes.c_float, i32, i32, vp, vp, vp]
+        lib.mla_decode_noalloc.restype = i32
+        lib.mla_noalloc_scratch_bytes.argtypes = []
+        lib.mla_noalloc_scratch_bytes.restype = sz
         lib.mla_check_inputs.restype = i32
         lib.mla_merge_shards.argtypes = [i32, i64, i32, vp, i32, vp, i32, vp, i32, vp, vp]
         lib.mla_merge_shards.restype = i32
@@ -432,6 +438,46 @@ def mla_decode_sparse(q, kv_cache, block_table, topk_indices, topk_lens, scale: 
             workspace.numel() * workspace.element_size() if workspace is not None else 0, stream)
     if st != MLA_OK:
         _raise(st, "mla_decode_sparse")
+    return o, lse
+
+
+def mla_noalloc_scratch_bytes() -> int:
+    """Bytes of the built-in scratch that mla_decode_noalloc uses per device."""
+    return int(load_library().mla_noalloc_scratch_bytes())
+
+
+def mla_decode_noalloc(q, kv_cache, block_table, seq_lens, scale: float, page_size: int,
+                       k_scale: float, num_kv_splits: int, split_mode: int, o, lse, *,
+                       kv_dtype=None, stream=None):
+    """Enqueue one decode step through the allocation-free entry point of the C
+    ABI (mla_decode_noalloc): no workspace, no allocation by the library or by
+    this wrapper, so the caller passes o and lse and the split plan (from
+    mla_plan, a host-only call).  Results are bitwise those of mla_decode with
+    the same plan.  Calls that overlap in time on one device share its
+    built-in scratch and race; calls in order on one stream are safe."""
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
+                    ("seq_lens", seq_lens)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    shape = shape_of(q, kv_cache, block_table, kv_dtype=kv_dtype, o_dtype=o.dtype)
+    q_len = q.shape[1] if q.dim() == 4 else 1
+    rows = ((shape.batch, q_len, shape.num_heads) if q.dim() == 4
+            else (shape.batch, shape.num_heads))
+    _check_sizes(shape, rows, block_table, seq_lens, o, lse)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    st = lib.mla_decode_noalloc(ctypes.byref(shape), int(q_len), q.data_ptr(),
+                                kv_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
+                                float(scale), int(page_size), float(k_scale), int(num_kv_splits),
+                                int(split_mode), o.data_ptr(), lse.data_ptr(), stream)
+    if st != MLA_OK:
+        _raise(st, "mla_decode_noalloc")
     return o, lse
 
 

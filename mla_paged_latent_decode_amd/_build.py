@@ -29,6 +29,7 @@ PEAKS_SRC = os.path.join(CSRC, "mla_peaks.hip")
 KERNELS = os.path.join(CSRC, "mla_kernels.hip")
 # (source, extra defines) of every translation unit
 UNITS = ([(os.path.join(CSRC, "mla_api.cpp"), []), (os.path.join(CSRC, "mla_merge.hip"), []),
+          (os.path.join(CSRC, "mla_noalloc.hip"), []),
           (KERNELS, ["-DMLA_MAIN"])] +
          [(KERNELS, [f"-DMLA_STAGE1_GROUP={g}"]) for g in range(10)])
 SOURCES = sorted({u[0] for u in UNITS} | {PEAKS_SRC})

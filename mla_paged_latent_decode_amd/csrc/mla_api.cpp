@@ -205,7 +205,7 @@ static mla_status decode_stages(const mla_shape* shape, int32_t q_len, const mla
                                 int32_t num_kv_splits, int32_t split_mode, void* o, float* lse,
                                 void* workspace, size_t workspace_bytes, void* hip_stream,
                                 int stages, const int32_t* topk_idx = nullptr,
-                                int32_t topk = 0) {
+                                int32_t topk = 0, bool builtin_scratch = false) {
   mla_status st = check_shape(shape);
   if (st != MLA_OK) return st;
   mla_shape rs;
@@ -231,6 +231,12 @@ static mla_status decode_stages(const mla_shape* shape, int32_t q_len, const mla
     return MLA_ERR_ARGUMENT;
   const WorkspaceLayout wl = workspace_layout(shape->batch, shape->num_heads,
                                               shape->kv_lora_rank, split_mode, num_kv_splits);
+  if (builtin_scratch && wl.total > 0) {
+    // the built-in scratch of this device instead of a caller's workspace
+    if (wl.total > kNoAllocScratchBytes) return MLA_ERR_SCRATCH;
+    if (noalloc_scratch(&workspace) != 0) return MLA_ERR_LAUNCH;
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   if (wl.total > 0) {
     if (!workspace || workspace_bytes < wl.total) return MLA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return MLA_ERR_ARGUMENT;
@@ -306,6 +312,19 @@ mla_status mla_decode_split_q(const mla_shape* shape, int32_t q_len, const mla_q
                        k_scale, num_kv_splits, split_mode, o, lse, workspace, workspace_bytes,
                        hip_stream, kBothStages);
 }
+
+mla_status mla_decode_noalloc(const mla_shape* shape, int32_t q_len, const void* q,
+                              const void* kv_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, float scale, int32_t page_size,
+                              float k_scale, int32_t num_kv_splits, int32_t split_mode, void* o,
+                              float* lse, void* hip_stream) {
+  const mla_query qd = contiguous_query(shape, q_len, q);
+  return decode_stages(shape, q_len, &qd, kv_cache, block_table, seq_lens, scale, page_size,
+                       k_scale, num_kv_splits, split_mode, o, lse, nullptr, 0, hip_stream,
+                       kBothStages, nullptr, 0, true);
+}
+
+size_t mla_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 mla_status mla_decode_stage1(const mla_shape* shape, const void* q, const void* kv_cache,
                              const int32_t* block_table, const int32_t* seq_lens, float scale,
@@ -463,6 +482,7 @@ const char* mla_status_string(int32_t status) {
     case MLA_ERR_LAUNCH: return "MLA_ERR_LAUNCH: HIP kernel launch failed";
     case MLA_ERR_ARGUMENT: return "MLA_ERR_ARGUMENT: non-finite/non-positive scale or k_scale, num_cus < 1, q_len outside [1, MLA_MAX_Q_LEN], topk < 1, or a misaligned pointer or query stride";
     case MLA_ERR_TABLE: return "MLA_ERR_TABLE: a sequence length, block-table entry or top-k entry is out of range";
+    case MLA_ERR_SCRATCH: return "MLA_ERR_SCRATCH: the split layout needs more than the built-in scratch of mla_decode_noalloc (mla_noalloc_scratch_bytes())";
     default: return "unknown mla_status";
   }
 }

@@ -139,4 +139,11 @@ struct MergeArgs {
 
 int launch_merge_shards(const MergeArgs& a, void* stream);
 
+// Scratch of the allocation-free entry point (mla_noalloc.hip): a device
+// array of kNoAllocScratchBytes per device; noalloc_scratch() returns the
+// current device's copy (looked up once per device).  Returns 0 or a HIP
+// error code.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+int noalloc_scratch(void** ptr);
+
 }  // namespace mla

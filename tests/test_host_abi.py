@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for code in range(11):
+    for code in range(12):
         s = mla.mla_status_string(code)
         assert s and "unknown" not in s
     assert "unknown" in mla.mla_status_string(99)
