@@ -292,7 +292,7 @@ def run_probes(timed):
     vp, i32 = ctypes.c_void_p, ctypes.c_int
     lib.mla_peak_stream.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.mla_peak_mfma.argtypes = [i32, i32, vp, vp, vp]
-    lib.mla_peak_lds.argtypes = [i32, i32, i32, vp, vp, vp]
+    lib.mla_peak_lds.argtypes = [i32, i32, i32, i32, vp, vp, vp]
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev).cuda_stream
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -337,17 +337,20 @@ def run_probes(timed):
                                  "frac_of_spec": round(flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                                  "cycles_per_mfma": round(float(np.median(cycles)) / (iters * 8), 2),
                                  "mhz": round(mhz)}
-    for waves in (4, 8):
-        lit = 200
+    for tr in (0, 1):
+        for waves in (4, 8):
+            lit = 200
 
-        def go_lds():
-            if lib.mla_peak_lds(grid, waves, lit, cyc.data_ptr(), sink.data_ptr(), stream):
-                raise RuntimeError("mla_peak_lds failed")
-        t = timed(go_lds)
-        cycles, mhz = clock(grid)
-        per_wg_bytes = waves * lit * 64 * 1024
-        out[f"lds_read_b128_w{waves}"] = {"bytes_per_clk_per_cu": round(per_wg_bytes / float(np.median(cycles)), 1),
-                                          "mhz": round(mhz)}
+            def go_lds():
+                if lib.mla_peak_lds(grid, waves, lit, tr, cyc.data_ptr(), sink.data_ptr(), stream):
+                    raise RuntimeError("mla_peak_lds failed")
+            t = timed(go_lds)
+            cycles, mhz = clock(grid)
+            per_wg_bytes = waves * lit * (32 if tr else 64) * 1024
+            name = "lds_read_b64_tr_b16" if tr else "lds_read_b128"
+            out[f"{name}_w{waves}"] = {"bytes_per_clk_per_cu":
+                                       round(per_wg_bytes / float(np.median(cycles)), 1),
+                                       "mhz": round(mhz)}
     return out
 
 

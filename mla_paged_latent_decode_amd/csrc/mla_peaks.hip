@@ -159,6 +159,39 @@ __global__ __launch_bounds__(64 * W) void lds_probe(int iters, uint64_t* cycles,
   if (acc == 0x9e3779b9u) sink[threadIdx.x] = acc;
 }
 
+// W waves each read `iters` x 32 KB of LDS with ds_read_b64_tr_b16, the
+// transposed 16-bit read that feeds the P.V contraction its V^T operand.
+template <int W>
+__global__ __launch_bounds__(64 * W) void lds_tr_probe(int iters, uint64_t* cycles, uint32_t* sink) {
+  __shared__ __attribute__((aligned(1024))) uint8_t buf[65536];
+  for (int i = threadIdx.x; i < 65536 / 16; i += 64 * W)
+    reinterpret_cast<u32x4*>(buf)[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const uint32_t base = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)buf + 8 * lane;
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  uint32_t acc = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int b = 0; b < 64; b += 8) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      u32x2 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v[k]) : "v"(base), "i"((b + k) * 512));
+      // the wait is tied to every loaded value, so no use can move above it
+#pragma unroll
+      for (int k = 0; k < 8; ++k) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[k]));
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc ^= v[k][0] + v[k][1];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) stamp(cycles, c0, r0);
+  if (acc == 0x9e3779b9u) sink[threadIdx.x] = acc;
+}
+
 template <int W, int NBUF, bool ROWS, bool READ>
 int launch_stream(const void* pool, const int32_t* pages, int grid, int per_wg, uint64_t* cyc,
                   uint32_t* sink, hipStream_t st) {
@@ -205,9 +238,21 @@ int mla_peak_mfma(int grid, int iters, void* cycles, void* sink, void* stream) {
 }
 
 /* LDS read probe: grid workgroups of `waves` (4 or 8) waves, each wave reading
- * iters x 64 KB with ds_read_b128.  cycles and sink as above. */
-int mla_peak_lds(int grid, int waves, int iters, void* cycles, void* sink, void* stream) {
+ * iters x 64 KB with ds_read_b128 (tr = 0), or iters x 32 KB with
+ * ds_read_b64_tr_b16 (tr = 1).  cycles and sink as above. */
+int mla_peak_lds(int grid, int waves, int iters, int tr, void* cycles, void* sink, void* stream) {
   hipStream_t st = (hipStream_t)stream;
+  if (tr) {
+    if (waves == 4)
+      hipLaunchKernelGGL(lds_tr_probe<4>, dim3(grid), dim3(256), 0, st, iters, (uint64_t*)cycles,
+                         (uint32_t*)sink);
+    else if (waves == 8)
+      hipLaunchKernelGGL(lds_tr_probe<8>, dim3(grid), dim3(512), 0, st, iters, (uint64_t*)cycles,
+                         (uint32_t*)sink);
+    else
+      return -1;
+    return (int)hipGetLastError();
+  }
   if (waves == 4)
     hipLaunchKernelGGL(lds_probe<4>, dim3(grid), dim3(256), 0, st, iters, (uint64_t*)cycles,
                        (uint32_t*)sink);
