@@ -131,10 +131,10 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   const int H = p.heads;
 
   // ---------------- per-lane constants of the LDS layout
-  // DMA: lane l writes slot l of a block: chunk c4 = l / 16 of position
-  // t16 = (l % 16) ^ f(c4); its source offset within the 16-row page run.
-  const int dma_c4 = lane >> 4;
-  const int dma_t16 = (lane & 15) ^ (8 * (dma_c4 & 1) + 4 * (dma_c4 >> 1));
+  // DMA: lane l writes slot l of a block: position t16 = l / 4, chunk
+  // c4 = (l % 4) ^ tile_swz(t16); its source offset within the 16-row page run.
+  const int dma_t16 = lane >> 2;
+  const int dma_c4 = (lane & 3) ^ tile_swz(dma_t16);
   const int dma_voff = dma_t16 * C::SRC_ROW + 16 * dma_c4;
   // fp8 widening: lane l converts chunk c4 = l % 4 of position t16 = l / 4
   // of a block, read from the row-major staging tile and written to the
@@ -299,23 +299,25 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
         if constexpr (F8) {
           // 1-byte codes: the r-th 64*G bytes of half th go to the row-major
           // staging tile as in dense decode, but each row comes from its own
-          // slot; lane t < 16 holds the offset of row t of the half
-          // (dma_t16 = lane there), read here with a lane shuffle
+          // slot; lane 4t holds the offset of row t of the half
+          // (dma_t16 = t there), read here with a lane shuffle
           const int c = C::G * lane + sgpr_here(r * 64 * C::G);  // code byte in the half
           const int row = c / C::CB;
-          const uint32_t roff = (uint32_t)__shfl((int)(th ? tl.off[1] : tl.off[0]), row, 64);
+          const uint32_t roff = (uint32_t)__shfl((int)(th ? tl.off[1] : tl.off[0]), 4 * row, 64);
           LDS_AS void* dst = (LDS_AS void*)(tl.dst + th * 16 * C::CB + r * 64 * C::G);
           const int voff = (int)(roff + (uint32_t)(c - row * C::CB));
           if constexpr (C::G == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, 0, 0, 0);
           else __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, voff, 0, 0, 0);
           if constexpr (PT) {
             if (k == 0 && wave == 0) {
-              // the 16 inline scales of each half: lane l < 16 reads row l's
-              // (rows past the segment, and lanes >= 16, read 0)
+              // the 16 inline scales of each half: lane l < 16 reads row l's,
+              // whose offset lane 4l holds (rows past the segment, and lanes
+              // >= 16, read 0)
 #pragma unroll
               for (int h2 = 0; h2 < 2; ++h2) {
-                const int soff = lane < 16 ? (int)((h2 ? tl.off[1] : tl.off[0]) + C::CB)
-                                           : (int)p.pool_bytes;
+                const uint32_t ro =
+                    (uint32_t)__shfl((int)(h2 ? tl.off[1] : tl.off[0]), (4 * lane) & 63, 64);
+                const int soff = lane < 16 ? (int)(ro + C::CB) : (int)p.pool_bytes;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rs, (LDS_AS uint8_t*)ring + kSclOff + tl.sslot * 512 + h2 * 256, 4, soff,
                     0, 0, 0);
@@ -437,10 +439,18 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
 
     // Q fragments of this wave's heads (B operand of S^T = K Q^T): the first
     // NQR k-steps in VGPRs, the rest in this wave's LDS region (lane-linear).
-    // In the pipelined bf16 loop the LDS part is held in registers until the
-    // first tiles' loads are issued, so that the query, the block-table
-    // window and the first tiles are all in flight together.
-    constexpr bool kEarlyRing = C::PIPE;
+    // With 32-head waves the LDS part is held in registers until the first
+    // tiles' loads are issued, so that the query, the block-table window and
+    // the first tiles are all in flight together (one memory latency at the
+    // start of a segment, not two).
+    constexpr bool kEarlyRing = HPW == 32;
+    if constexpr (!C::PIPE) {
+      // Drain this wave's stores and loads of a previous segment once, so
+      // that no wait for them lands between the loads below, then make sure
+      // every wave is done with the ring of that segment.
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+    }
     bf16x8 qf[C::NQR];
     bf16x8 qtmp[kEarlyRing ? (C::QLDS > 0 ? C::QLDS : 1) : 1];
     LDS_AS uint8_t* qlds =
@@ -701,17 +711,24 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
         }
       }
     } else {
-    // Drain this wave's earlier stores and loads once, so that no wait for
-    // them lands between the ring loads below, then make sure every wave is
-    // done with the ring of a previous segment.
+    // The first tiles go out behind the query loads; then the query's LDS
+    // part is stored (asm: the compiler waits for the query registers it
+    // reads, which are older than the ring loads, and for nothing else).
     // fp8 (ring of 2): iteration i loads tile i+2 into staging slot i % 2
     // over its QK^T MFMAs and widens tile i+1 into ring slot (i+1) % 2 at
     // its end; the barrier at the top of iteration i+1 publishes both.
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
+    auto store_qlds = [&]() __attribute__((always_inline)) {
+      if constexpr (kEarlyRing) {
+#pragma unroll
+        for (int k = 0; k < C::QLDS; ++k)
+          ds_write_b128_asm((uint32_t)(uintptr_t)(qlds + k * 1024 + lane * 16),
+                            __builtin_bit_cast(u32x4, qtmp[k]));
+      }
+    };
     if constexpr (F8) {
       issue(0);
       issue(1);
+      store_qlds();
       wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();  // staging tiles 0 and 1 complete
       widen_tile(0);
@@ -719,6 +736,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
 #pragma unroll
       for (int i = 0; i < NBUF - 1; ++i)
         if (i < n_tiles) issue(i);
+      store_qlds();
     }
 
     for (int i = 0; i < n_tiles; ++i) {
