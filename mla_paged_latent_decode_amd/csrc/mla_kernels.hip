@@ -56,13 +56,16 @@ struct Cfg {
   static constexpr int SRC_ROW = PT ? CB + kPerTokenPad : CB;  // cache row bytes
   // 1-byte and 4-bit codes: a 16-row half tile (16*CB code bytes of one
   // page) is copied to a row-major staging tile with G-byte LDS DMA per lane
-  // (consecutive lanes write consecutive G bytes), G = 16 when every wave
-  // then issues the same number of copies, else 4; bf16: one 16-byte copy
-  // per lane and block.
-  static constexpr int G =
-      !F8 ? 16 : ((16 * CB) % 1024 == 0 && (2 * 16 * CB / 1024) % W == 0) ? 16 : 4;
+  // (consecutive lanes write consecutive G bytes), G = 16 when a half tile
+  // is a whole number of 1 KB copies that never straddle a row, else 4;
+  // bf16: one 16-byte copy per lane and block.  A wave stalls at each copy
+  // it issues while the memory pipeline drains, so few wide copies beat many
+  // narrow ones.  The 2*NIH copies of a tile are dealt round-robin: wave w
+  // issues copies w, w+W, ..., at most NIW of them (narrow codes wait for all
+  // of a wave's copies at once, so the counts may differ between waves).
+  static constexpr int G = !F8 ? 16 : ((16 * CB) % 1024 == 0 && CB % 16 == 0) ? 16 : 4;
   static constexpr int NIH = F8 ? 16 * CB / (64 * G) : NKQ;  // DMA copies per half tile
-  static constexpr int NIW = 2 * NIH / W;                    // DMA copies per wave per tile
+  static constexpr int NIW = (2 * NIH + W - 1) / W;          // DMA copies per wave per tile
   static constexpr int STG_TILE = F8 ? kTile * CB : 0;       // staging tile bytes
   static constexpr int CVB = PT == 3 ? 4 : 8;                // code bytes of 8 elements
   static constexpr int STG_BYTES = 2 * STG_TILE;
@@ -90,7 +93,8 @@ struct Cfg {
   static_assert(!PT || CB % G == 0, "a copy never straddles a row's scale pad");
   static_assert(NBLK * 1024 == kTile * D * 2, "tile bytes");
   static_assert(NBLK % W == 0, "each wave loads or widens the same number of blocks");
-  static_assert(!F8 || ((16 * CB) % (64 * G) == 0 && (2 * NIH) % W == 0), "narrow copy split");
+  static_assert(!F8 || (16 * CB) % (64 * G) == 0, "narrow copy split");
+  static_assert(F8 || (2 * NIH) % W == 0, "bf16 waits count the same copies in every wave");
   static_assert(F8 ? NIW <= 63 : (NBUF - 1) * LPW <= 63,
                 "outstanding loads must fit the vmcnt counter");
   static_assert(NBUF * TILE_BYTES + STG_BYTES + QLDS_BYTES + SCL_BYTES <= kLdsBytes, "LDS budget");
@@ -291,6 +295,9 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     // bytes of a half tile into the row-major staging tile.
     auto dma = [&](const TileLoad& tl, int k) __attribute__((always_inline)) {
       const int j = wave + k * W;  // copy index
+      if constexpr ((2 * C::NIH) % W != 0) {
+        if (j >= 2 * C::NIH) return;  // (wave-uniform) this wave's share is done
+      }
       const int th = j >= C::NIH ? 1 : 0;
       const int r = j - th * C::NIH;
       if constexpr (SP) {
