@@ -46,14 +46,20 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode HBM GB/s + MFMA TFLOP/s (% of peak), B=64 H=128 D=576 ctx 1k-8k"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, public spec
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, public spec
-KERNEL_SRC = os.path.join(ROOT, "mla_paged_latent_decode_amd", "csrc", "mla_kernels.hip")
+# the sources the stage-1 kernel is compiled from: counters read on one
+# version are reported only while all of them are unchanged
+KERNEL_SRCS = [os.path.join(ROOT, "mla_paged_latent_decode_amd", "csrc", f)
+               for f in ("mla_kernels.hip", "mla_device.h", "mla_internal.h")]
 COPY_BYTES = 1 << 30
 EVENT_EVERY = 4           # per-kernel events on every 4th timed step (see the timed loop)
 
 
 def kernel_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def algorithmic(inp):
@@ -547,12 +553,16 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    # Per-kernel HIP events bracket the two launches of every EVENT_EVERY-th
-    # step: each event recorded between two kernels adds a gap of a few
-    # microseconds that a caller's back-to-back launches do not have, so
-    # instrumenting every step would inflate the step time by ~4 %.
+    # Per-kernel HIP events on every EVENT_EVERY-th step, recorded by the two
+    # kernel launches themselves (mla_time_next_launch): they bracket each
+    # kernel alone, as a profiler's kernel trace does, and add no marker
+    # between the launches.  torch creates an event at its first record, so
+    # each is recorded once here before the timed loop.
     sampled = [i for i in range(K) if i % EVENT_EVERY == 0]
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in sampled}
+    for e in evs.values():
+        for x in e:
+            x.record(stream)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -561,20 +571,19 @@ def main():
         c = calls[i % 2]
         e = evs.get(i)
         if e:
-            e[0].record(stream)
+            mla.mla_time_next_launch(1, e[0], e[1])
+            if mode == mla.SPLIT_BALANCED or splits > 1:
+                mla.mla_time_next_launch(2, e[2], e[3])
         c("stage1")
-        if e:
-            e[1].record(stream)
         c("stage2")
-        if e:
-            e[2].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / K
     s1 = np.array([e[0].elapsed_time(e[1]) for e in evs.values()])
-    s2 = np.array([e[1].elapsed_time(e[2]) for e in evs.values()])
+    s2 = (np.array([e[2].elapsed_time(e[3]) for e in evs.values()])
+          if mode == mla.SPLIT_BALANCED or splits > 1 else np.zeros(len(evs)))
 
     if args.copy_calibration:
         a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)

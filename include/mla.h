@@ -430,6 +430,16 @@ mla_status mla_merge_shards(int32_t num_shards, int64_t rows, int32_t d_v, const
                             int32_t parts_dtype, const float* lse_parts, int32_t lse_base,
                             void* o, int32_t o_dtype, float* lse, void* hip_stream);
 
+/* Measurement aid: the next launch of stage `stage` (1: the attention pass
+ * with its partials, 2: the merge) made by the calling thread, by any decode
+ * entry point, records the kernel's own start into start_event and its end
+ * into stop_event (hipEvent_t values created by the caller with timing
+ * enabled; either may be NULL).  The setting then clears; a call that does
+ * not launch that stage leaves it pending.  Unlike events recorded on the
+ * stream between launches, these bracket the kernel alone.  Pure host;
+ * MLA_ERR_ARGUMENT for another stage number. */
+mla_status mla_time_next_launch(int32_t stage, void* start_event, void* stop_event);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char* mla_status_string(int32_t status);
 

@@ -30,7 +30,8 @@ from . import _build
 
 __all__ = [
     "MlaError", "mla_decode", "mla_decode_sparse", "mla_plan", "mla_check_inputs",
-    "mla_decode_noalloc", "mla_noalloc_scratch_bytes", "mla_workspace_size", "mla_pages_split_count",
+    "mla_decode_noalloc", "mla_noalloc_scratch_bytes", "mla_time_next_launch",
+    "mla_workspace_size", "mla_pages_split_count",
     "mla_status_string", "SPLIT_PER_SEQUENCE", "SPLIT_BALANCED", "library_path", "load_library",
     "MLA_BF16", "MLA_FP8_E4M3", "MLA_FP32", "MLA_FP8_E4M3_PER_TOKEN", "MLA_INT8_PER_TOKEN",
     "MLA_INT4_PER_TOKEN",
@@ -118,6 +119,8 @@ def load_library():
         lib.mla_decode_noalloc.restype = i32
         lib.mla_noalloc_scratch_bytes.argtypes = []
         lib.mla_noalloc_scratch_bytes.restype = sz
+        lib.mla_time_next_launch.argtypes = [i32, vp, vp]
+        lib.mla_time_next_launch.restype = i32
         lib.mla_check_inputs.restype = i32
         lib.mla_merge_shards.argtypes = [i32, i64, i32, vp, i32, vp, i32, vp, i32, vp, vp]
         lib.mla_merge_shards.restype = i32
@@ -444,6 +447,17 @@ def mla_decode_sparse(q, kv_cache, block_table, topk_indices, topk_lens, scale: 
 def mla_noalloc_scratch_bytes() -> int:
     """Bytes of the built-in scratch that mla_decode_noalloc uses per device."""
     return int(load_library().mla_noalloc_scratch_bytes())
+
+
+def mla_time_next_launch(stage: int, start_event, stop_event) -> None:
+    """The next launch of stage 1 or 2 made by this thread records the
+    kernel's own start and end into the two torch.cuda.Event objects (created
+    with enable_timing=True and recorded once before, so that they exist);
+    elapsed_time between them is then the kernel alone."""
+    st = load_library().mla_time_next_launch(int(stage), start_event.cuda_event,
+                                             stop_event.cuda_event)
+    if st != MLA_OK:
+        _raise(st, "mla_time_next_launch")
 
 
 def mla_decode_noalloc(q, kv_cache, block_table, seq_lens, scale: float, page_size: int,

@@ -37,6 +37,8 @@ WorkspaceLayout workspace_layout(int32_t batch, int32_t heads, int32_t d_v, int3
   return w;
 }
 
+thread_local LaunchTiming g_launch_timing[2];
+
 HeadTiling head_tiling(int32_t heads) {
   HeadTiling t;
   t.heads_per_wave = heads % 32 == 0 ? 32 : 16;
@@ -325,6 +327,12 @@ mla_status mla_decode_noalloc(const mla_shape* shape, int32_t q_len, const void*
 }
 
 size_t mla_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+mla_status mla_time_next_launch(int32_t stage, void* start_event, void* stop_event) {
+  if (stage != 1 && stage != 2) return MLA_ERR_ARGUMENT;
+  g_launch_timing[stage - 1] = LaunchTiming{start_event, stop_event};
+  return MLA_OK;
+}
 
 mla_status mla_decode_stage1(const mla_shape* shape, const void* q, const void* kv_cache,
                              const int32_t* block_table, const int32_t* seq_lens, float scale,

@@ -122,6 +122,15 @@ struct DecodeArgs {
 
 enum Stages { kStage1 = 1, kStage2 = 2, kBothStages = 3 };
 
+// Measurement aid (mla_time_next_launch): events (hipEvent_t) that the next
+// launch of stage 1 / stage 2 made by this thread records its own start and
+// end into; taken (and cleared) by that launch.  Null: a plain launch.
+struct LaunchTiming {
+  void* start = nullptr;
+  void* stop = nullptr;
+};
+extern thread_local LaunchTiming g_launch_timing[2];
+
 // Enqueues stage 1 and/or stage 2 (stage 2 only when the split layout needs
 // a merge).  Returns 0 or a HIP error code.
 int launch_decode(const DecodeArgs& a, void* stream, int stages);

@@ -28,6 +28,8 @@
 // Stage 2 (merge).  Partials (o_s, lse_s) of a sequence are combined with the
 //   log-sum-exp rule of the same article, section 十二:
 //   lse = M + ln sum_s e^(lse_s - M),  o = sum_s e^(lse_s - lse) o_s.
+#include <hip/hip_ext.h>
+
 #include "mla_device.h"
 
 namespace mla {
@@ -1418,12 +1420,27 @@ __global__ __launch_bounds__(256) void mla_stage2(Stage2Params p) {
 
 // ---------------------------------------------------------------- dispatch
 
+// A kernel launch; with events pending for this stage (mla_time_next_launch)
+// the launch records the kernel's own start and end into them.
+template <typename K, typename P>
+int launch_timed(int stage, K kernel, dim3 grid, dim3 block, hipStream_t st, const P& params) {
+  LaunchTiming& t = g_launch_timing[stage];
+  if (t.start || t.stop) {
+    const LaunchTiming ev = t;
+    t = LaunchTiming{};
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, reinterpret_cast<hipEvent_t>(ev.start),
+                          reinterpret_cast<hipEvent_t>(ev.stop), 0, params);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, params);
+  }
+  return (int)hipGetLastError();
+}
+
 template <int HPW, int W, int D, int DV, bool F8, bool SP = false, int PT = 0>
 int launch_stage1(const Stage1Params& sp, int grid, hipStream_t st) {
   constexpr int NBUF = stage1_ring_depth(HPW, W, D, F8, PT);
-  hipLaunchKernelGGL((mla_stage1<HPW, W, D, DV, NBUF, F8, SP, PT>), dim3(grid), dim3(64 * W), 0,
-                     st, sp);
-  return (int)hipGetLastError();
+  return launch_timed(0, mla_stage1<HPW, W, D, DV, NBUF, F8, SP, PT>, dim3(grid), dim3(64 * W), st,
+                      sp);
 }
 
 template <int D, int DV, bool F8, int PT = 0, bool SP = false>
@@ -1579,9 +1596,8 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   s2.kgroups = per_seq >= 32 ? 8 : per_seq >= 16 ? 4 : per_seq >= 8 ? 2 : 1;
   s2.head_groups = a.heads / (kS2Rows / s2.kgroups);
   const int grid2 = a.batch * s2.head_groups * (a.d_v / kS2Cols);
-  if (a.d_v == 512) hipLaunchKernelGGL(mla_stage2<512>, dim3(grid2), dim3(256), 0, st, s2);
-  else hipLaunchKernelGGL(mla_stage2<256>, dim3(grid2), dim3(256), 0, st, s2);
-  return (int)hipGetLastError();
+  return a.d_v == 512 ? launch_timed(1, mla_stage2<512>, dim3(grid2), dim3(256), st, s2)
+                     : launch_timed(1, mla_stage2<256>, dim3(grid2), dim3(256), st, s2);
 }
 #endif  // MLA_MAIN
 

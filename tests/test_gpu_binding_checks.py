@@ -69,3 +69,31 @@ def test_sparse_and_prepared_calls_refuse_short_buffers(mla, case):
                            o[:2].contiguous(), lse, ws)
     mla.mla_decode_sparse(q, kv, bt, idx, lens, *args, o, lse)
     torch.cuda.synchronize()
+
+
+def test_kernel_timing_events_bracket_one_launch(mla, case):
+    """mla_time_next_launch: the next stage-1 and stage-2 launches record their
+    own start and end into the events, then the setting clears (a later launch
+    leaves them as they are)."""
+    w, q, kv, bt, sl, _, _ = case
+    shape = mla.shape_of(q, kv, bt)
+    splits = 3
+    need = mla.mla_workspace_size(shape, mla.SPLIT_PER_SEQUENCE, splits)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    o = torch.empty((3, 16, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((3, 16), dtype=torch.float32, device=DEV)
+    call = mla.PreparedDecode(q, kv, bt, sl, w.scale, w.page_size, w.k_scale, splits,
+                              mla.SPLIT_PER_SEQUENCE, o, lse, ws)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()  # torch creates an event at its first record
+    mla.mla_time_next_launch(1, ev[0], ev[1])
+    mla.mla_time_next_launch(2, ev[2], ev[3])
+    call("both")
+    torch.cuda.synchronize()
+    t1, t2 = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])
+    gap = ev[1].elapsed_time(ev[2])  # stage 2 starts after stage 1 ends
+    assert 0 < t1 < 100 and 0 < t2 < 100 and gap >= 0
+    call("both")  # the setting was cleared: the events keep the first launch's times
+    torch.cuda.synchronize()
+    assert ev[0].elapsed_time(ev[1]) == t1 and ev[2].elapsed_time(ev[3]) == t2

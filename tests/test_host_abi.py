@@ -322,3 +322,12 @@ def test_split_query_argument_checks():
     # a valid query with an invalid shape still fails on the shape
     s.head_size = 400
     assert call(mla.MlaQuery(**good)) == mla.MLA_ERR_HEAD_SIZE
+
+
+def test_time_next_launch_takes_stage_1_or_2():
+    lib = mla.load_library()
+    assert lib.mla_time_next_launch(3, None, None) == mla.MLA_ERR_ARGUMENT
+    assert lib.mla_time_next_launch(0, None, None) == mla.MLA_ERR_ARGUMENT
+    # NULL events: the next launch is a plain one (nothing else changes)
+    assert lib.mla_time_next_launch(1, None, None) == mla.MLA_OK
+    assert lib.mla_time_next_launch(2, None, None) == mla.MLA_OK
