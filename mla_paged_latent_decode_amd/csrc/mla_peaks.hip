@@ -45,8 +45,9 @@ __device__ __forceinline__ void stamp(uint64_t* out, uint64_t c0, uint64_t r0) {
 // Workgroup w streams tiles w * per_wg .. (w+1) * per_wg - 1; tile t is half
 // `t & 1` of page pages[t >> 1] of a pool of 64-row pages.  W waves, NBUF
 // LDS tiles, block j of a tile copied by wave j % W.  ROWS = true: each load
-// instruction takes 64 bytes from each of 16 consecutive rows (the decode's
-// tile layout); false: 1 KB contiguous per instruction.  READ = true: each
+// instruction takes 64 bytes from each of 16 consecutive rows, each quad of
+// lanes one row's 64 contiguous bytes in a row-dependent order (the decode's
+// tile copies); false: 1 KB contiguous per instruction.  READ = true: each
 // wave then reads the whole tile back with ds_read_b128.
 template <int W, int NBUF, bool ROWS, bool READ>
 __global__ __launch_bounds__(64 * W) void stream_probe(const uint8_t* __restrict__ pool,
@@ -58,8 +59,11 @@ __global__ __launch_bounds__(64 * W) void stream_probe(const uint8_t* __restrict
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr int LPW = (kBlocks + W - 1) / W;  // most blocks any wave copies per tile
   const bool full = kBlocks % W == 0 || wave < kBlocks % W;
-  // per-lane source offset of a block: 16 rows x 64 B, or 1 KB contiguous
-  const int voff = ROWS ? (lane & 15) * kRow + 16 * (lane >> 4) : 16 * lane;
+  // per-lane source offset of a block: 16 rows x 64 B (row lane / 4, chunk
+  // (lane % 4) ^ f(row)), or 1 KB contiguous
+  const int voff = ROWS ? (lane >> 2) * kRow + 16 * ((lane & 3) ^ (2 * ((lane >> 4) & 1) +
+                                                                   ((lane >> 5) & 1)))
+                        : 16 * lane;
   const uint64_t c0 = __builtin_amdgcn_s_memtime();
   const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
   const int t0 = blockIdx.x * per_wg;
