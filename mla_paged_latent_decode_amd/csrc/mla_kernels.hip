@@ -395,31 +395,38 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
       return cv_dst + (uint32_t)sgpr_here((int)(uint32_t)(uintptr_t)ring +
                                           (x % NBUF) * C::TILE_BYTES + (wave + k * W) * 1024);
     };
+    // 8 code bytes per lane and block (4 for int4 codes): read, and the
+    // widened 8 bf16 written to the block's slot of the bf16 tile
+    using WRaw = std::conditional_t<PT == 3, uint32_t, u32x2>;
+    auto widen_read = [&](int x, int k) __attribute__((always_inline)) {
+      if constexpr (PT == 3) return ds_read_b32_asm(widen_src(x, k));
+      else return ds_read_b64_asm(widen_src(x, k));
+    };
+    auto widen_write = [&](int x, int k, WRaw v) __attribute__((always_inline)) {
+      if constexpr (PT == 3)
+        ds_write_b128_asm(widen_dst(x, k), i4x8_to_bf16x8(v));
+      else
+        ds_write_b128_asm(widen_dst(x, k), PT == 2 ? i8x8_to_bf16x8(v) : e4m3x8_to_bf16x8(v));
+    };
     // widen all of this wave's blocks of tile x, four reads in flight
-    auto widen_tile = [&](int x) __attribute__((always_inline)) {
+    auto widen_blocks = [&](int x) __attribute__((always_inline)) {
       static_for<(C::LPW + 3) / 4>([&](auto bc) __attribute__((always_inline)) {
         constexpr int k0 = 4 * decltype(bc)::value;
         constexpr int nb = C::LPW - k0 < 4 ? C::LPW - k0 : 4;
-        // 8 code bytes per lane and block (4 for int4 codes)
-        using Raw = std::conditional_t<PT == 3, uint32_t, u32x2>;
-        Raw v[nb];
+        WRaw v[nb];
         static_for<nb>([&](auto ic) __attribute__((always_inline)) {
-          if constexpr (PT == 3)
-            v[decltype(ic)::value] = ds_read_b32_asm(widen_src(x, k0 + decltype(ic)::value));
-          else
-            v[decltype(ic)::value] = ds_read_b64_asm(widen_src(x, k0 + decltype(ic)::value));
+          v[decltype(ic)::value] = widen_read(x, k0 + decltype(ic)::value);
         });
         static_for<nb>([&](auto ic) __attribute__((always_inline)) {
           constexpr int i = decltype(ic)::value;
           // issued after read i: the other nb-1-i reads and i writes
           lds_wait<nb - 1>(v[i]);
-          if constexpr (PT == 3)
-            ds_write_b128_asm(widen_dst(x, k0 + i), i4x8_to_bf16x8(v[i]));
-          else
-            ds_write_b128_asm(widen_dst(x, k0 + i),
-                              PT == 2 ? i8x8_to_bf16x8(v[i]) : e4m3x8_to_bf16x8(v[i]));
+          widen_write(x, k0 + i, v[i]);
         });
       });
+    };
+    // the tile's per-token scales (per-token caches)
+    auto widen_scales = [&](int x) __attribute__((always_inline)) {
       if constexpr (PT) {
         // the tile's 32 token scales: staging slot x % 2 (two 256-byte
         // halves, row l of a half at float l) -> ring slot x % NBUF (float t),
@@ -436,6 +443,10 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           ds_write_b32_asm(scl_ring + (x % NBUF) * 256 + 128 + lane * 4, __float_as_uint(inv));
         }
       }
+    };
+    auto widen_tile = [&](int x) __attribute__((always_inline)) {
+      widen_blocks(x);
+      widen_scales(x);
     };
     // per-token scales of the four consecutive positions t .. t+3 of ring
     // tile x, and their reciprocals
@@ -933,22 +944,53 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
             const u32x2 hi = ds_read_tr16_asm<off>(vbase1);
             return u32x4{lo[0], lo[1], hi[0], hi[1]};
           };
+          // 1-byte caches: the widening of tile i+1 rides along with these
+          // MFMAs instead of following them (its staging tile is complete
+          // and its ring slot free since the barrier at the top of this
+          // iteration).  Block k of the wave is read after step 3k and
+          // widened and written after step 3k+2: one LDS read, four
+          // conversions and one LDS write per three MFMAs.
+          constexpr bool kWidenHere = F8 && 3 * C::LPW <= NST;
+          // LDS operations after the MFMA of step s: the write of block
+          // (s-2)/3 and the read of block s/3
+          constexpr auto wops = [](int s) constexpr {
+            return kWidenHere ? ((s % 3 == 2 && s / 3 < C::LPW) ? 1 : 0) +
+                                    ((s % 3 == 0 && s / 3 < C::LPW) ? 1 : 0)
+                              : 0;
+          };
+          constexpr auto pairs = [](int s) constexpr { return s < NST ? 2 : 0; };
+          WRaw wv[kWidenHere ? C::LPW : 1];
           u32x4 a0 = vread(std::integral_constant<int, 0>{});
           u32x4 a1 = vread(std::integral_constant<int, 1>{});
           static_for<NST>([&](auto stc) __attribute__((always_inline)) {
             constexpr int st = decltype(stc)::value;
             u32x4 a2 = a1;
             if constexpr (st + 2 < NST) a2 = vread(std::integral_constant<int, st + 2>{});
-            // reads issued after step st's pair: those of st+1 and st+2
-            constexpr int later = 2 * ((st + 2 < NST ? st + 2 : NST - 1) - st);
+            // LDS operations issued after step st's pair: the pairs of steps
+            // st+1 and st+2 and the widening's operations in between
+            constexpr int later = st == 0   ? pairs(1) + pairs(2)
+                                  : st == 1 ? pairs(2) + wops(0) + pairs(3)
+                                            : wops(st - 2) + pairs(st + 1) + wops(st - 1) +
+                                                  pairs(st + 2);
             lds_wait<later>(a0);
             oacc[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, a0), (st & 1) ? p1 : p0, oacc[st >> 1], 0, 0, 0);
             dma_at(C::NKS + st);
+            if constexpr (kWidenHere) {
+              if constexpr (st % 3 == 2 && st / 3 < C::LPW) {
+                constexpr int k = st / 3;
+                // issued after block k's read: the pairs of steps 3k+3, 3k+4
+                lds_wait<pairs(3 * k + 3) + pairs(3 * k + 4)>(wv[k]);
+                widen_write(i + 1, k, wv[k]);
+              }
+              if constexpr (st % 3 == 0 && st / 3 < C::LPW) wv[st / 3] = widen_read(i + 1, st / 3);
+            }
             __builtin_amdgcn_sched_barrier(0);
             a0 = a1;
             a1 = a2;
           });
+          if constexpr (kWidenHere) widen_scales(i + 1);
+          else if constexpr (F8) widen_tile(i + 1);
         }
       } else {
         // ---- S^T over two 16-position halves x 16 heads
@@ -1062,7 +1104,7 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           });
         }
       }
-      if constexpr (F8) widen_tile(i + 1);
+      if constexpr (F8 && HPW != 32) widen_tile(i + 1);
     }
 
     }
