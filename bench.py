@@ -605,8 +605,10 @@ def main():
         ach = alg["flops"] / (s1_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
-    roof["traffic"] = load_traffic(args.workload)
-    counters = load_counters(args.workload)
+    # the stored counters were read on the planner's launch configuration;
+    # another split moves other partial bytes
+    roof["traffic"] = load_traffic(args.workload) if args.split == "plan" else None
+    counters = load_counters(args.workload) if args.split == "plan" else None
     if counters and counters.get("mfma_flops_counted"):
         # MFMA work counted by the hardware for one launch, over the measured
         # launch time: the MFMA rate from counters rather than from the method
