@@ -289,7 +289,11 @@ def run_probes(timed):
       tiles, one workgroup per CU, about the dsv3 cache's bytes per launch;
       the decode's configuration is 4 waves, ring 3, 16-row loads;
     - mfma: v_mfma_f32_32x32x16_bf16 on every SIMD;
-    - lds: ds_read_b128 by 4 and 8 waves per CU."""
+    - lds: ds_read_b128 by 4 and 8 waves per CU;
+    - tileloop: the stage-1 tile loop stripped to its copies, MFMAs, LDS
+      operand reads and softmax-like VALU work, with and without the copies,
+      on pages of N(0,1) bf16 values and on zeroed pages (same instructions
+      and bytes): the time per tile and the shader clock it ran at."""
     import ctypes
     import numpy as np
     import torch
@@ -299,6 +303,7 @@ def run_probes(timed):
     lib.mla_peak_stream.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.mla_peak_mfma.argtypes = [i32, i32, vp, vp, vp]
     lib.mla_peak_lds.argtypes = [i32, i32, i32, i32, vp, vp, vp]
+    lib.mla_peak_tileloop.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev).cuda_stream
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -328,9 +333,31 @@ def run_probes(timed):
         cycles, mhz = clock(grid)
         key = f"stream_w{waves}_ring{ring}_{'rows' if rows else 'contig'}{'_read' if read else ''}"
         out[key] = {"GBps": round(nbytes / t / 1e9, 1), "frac_of_spec": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                    "us_per_tile": round(t * 1e6 / per_wg, 3),
                     "cycles_per_tile": round(float(np.median(cycles)) / per_wg, 1),
                     "mhz": round(mhz)}
-    del pool
+    # the tile loop on pages of N(0,1) bf16 values and on zeroed pages, in two
+    # alternating passes (the clock follows the recent load with some lag)
+    normal = torch.empty(pool.numel() // 2, dtype=torch.bfloat16, device=dev)
+    normal.normal_(generator=torch.Generator(device=dev).manual_seed(1234))
+    for pas, data in ((1, "normal"), (1, "zero"), (2, "normal"), (2, "zero")):
+        if data == "zero":
+            pool.zero_()
+        else:
+            pool.view(torch.bfloat16).copy_(normal)
+        for copy in (1, 0):
+            def go_loop():
+                rc = lib.mla_peak_tileloop(pool.data_ptr(), pages.data_ptr(), grid, per_wg, copy,
+                                           cyc.data_ptr(), sink.data_ptr(), stream)
+                if rc:
+                    raise RuntimeError(f"mla_peak_tileloop failed: {rc}")
+            t = timed(go_loop)
+            cycles, mhz = clock(grid)
+            key = f"tileloop_{'copies_compute' if copy else 'compute_only'}_{data}_pass{pas}"
+            out[key] = {"us_per_tile": round(t * 1e6 / per_wg, 3),
+                        "cycles_per_tile": round(float(np.median(cycles)) / per_wg, 1),
+                        "mhz": round(mhz)}
+    del pool, normal
     iters = 2000
 
     def go_mfma():

@@ -13,6 +13,14 @@
 //   mla_peak_mfma     a dependency-free loop of v_mfma_f32_32x32x16_bf16
 //                     (the decode's contraction instruction) on every SIMD.
 //   mla_peak_lds      ds_read_b128 from LDS by 4 or 8 waves per workgroup.
+//   mla_peak_tileloop the stage-1 tile loop stripped to its resource use:
+//                     per 36 KB tile and wave, 9 copies in the decode's
+//                     pattern (ring of 3) spread over 68 MFMAs
+//                     (v_mfma_f32_32x32x16_bf16, K and V operands read from
+//                     the tile in LDS, 256 AGPR accumulators) and softmax-like
+//                     VALU work on the scores; or the compute alone.  Run on
+//                     the caller's page contents, it shows how the data (and
+//                     the HBM streaming beside the MFMAs) sets the clock.
 //
 // Every probe records, per workgroup, the shader-clock cycles (s_memtime) and
 // the 100 MHz constant-clock ticks (s_memrealtime) it ran for, so the caller
@@ -196,6 +204,127 @@ __global__ __launch_bounds__(64 * W) void lds_tr_probe(int iters, uint64_t* cycl
   if (acc == 0x9e3779b9u) sink[threadIdx.x] = acc;
 }
 
+// The tile loop of stage 1 without its bookkeeping: 4 waves, tiles as in
+// stream_probe (ring of 3, the decode's 16-row x 64-byte copies), per tile and
+// wave 36 MFMAs of S = K Q (K from the tile, Q in registers), a row max and
+// exponentials of the 16 scores per lane, and 32 MFMAs of O += V P into 16
+// accumulator blocks (V from the tile); copy k of the wave's 9 goes out after
+// MFMA step floor(68 k / 9).  COPY = false: the same compute on a tile that
+// stays in LDS (filled once).
+template <bool COPY>
+__global__ __launch_bounds__(256) void tileloop_probe(const uint8_t* __restrict__ pool,
+                                                      const int32_t* __restrict__ pages,
+                                                      int per_wg, uint64_t* cycles, float* sink) {
+  constexpr int NBUF = 3;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * kTileBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int voff = (lane >> 2) * kRow + 16 * ((lane & 3) ^ (2 * ((lane >> 4) & 1) + ((lane >> 5) & 1)));
+  const int t0 = blockIdx.x * per_wg;
+  auto base_of = [&](int i) {
+    const int t = t0 + i;
+    const int64_t page = pages[t >> 1];
+    return (uint64_t)(pool + (page * 64 + (t & 1) * 32) * (int64_t)kRow);
+  };
+  auto copy = [&](uint64_t base, int i, int k) {
+    const int j = wave + 4 * k;
+    const int src = (j / 18) * 16 * kRow + (j % 18) * 64;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, kTileBytes, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(ring + (i % NBUF) * kTileBytes + j * 1024),
+                                             16, voff + src, 0, 0, 0);
+  };
+  f32x16 o[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) o[v] = f32x16{};
+  bf16x8 q[24];
+#pragma unroll
+  for (int k = 0; k < 24; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[k][e] = (__bf16)(0.01f * (k + e + lane));
+  float lsum = 0.f;
+  if constexpr (COPY) {
+    for (int i = 0; i < NBUF - 1; ++i) {
+      const uint64_t b = base_of(i);
+#pragma unroll
+      for (int k = 0; k < 9; ++k) copy(b, i, k);
+    }
+  } else {
+    const uint64_t b = base_of(0);
+#pragma unroll
+    for (int k = 0; k < 9; ++k) copy(b, 0, k);
+    wait_vmcnt<0>();
+  }
+  __builtin_amdgcn_s_barrier();
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  for (int i = 0; i < per_wg; ++i) {
+    if constexpr (COPY) {
+      if (i + 1 < per_wg) wait_vmcnt<9>(); else wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    const bool more = COPY && i + NBUF - 1 < per_wg;
+    const uint64_t nb = more ? base_of(i + NBUF - 1) : 0;
+    auto copy_at = [&](int step) {
+#pragma unroll
+      for (int k = 0; k < 9; ++k)
+        if ((k * 68) / 9 == step && more) copy(nb, i + NBUF - 1, k);
+    };
+    const LDS_AS uint8_t* tile = (const LDS_AS uint8_t*)ring + (COPY ? (i % NBUF) : 0) * kTileBytes;
+    f32x16 s = {};
+    auto kq = [&](int ks) {
+      return *reinterpret_cast<const LDS_AS bf16x8*>(tile + (ks >> 1) * 1024 + 16 * lane);
+    };
+    bf16x8 k0 = kq(0), k1 = kq(1);
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) {
+      bf16x8 k2 = k1;
+      if (ks + 2 < 36) k2 = kq(ks + 2);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, q[ks % 24], s, 0, 0, 0);
+      copy_at(ks);
+      __builtin_amdgcn_sched_barrier(0);
+      k0 = k1;
+      k1 = k2;
+    }
+    float m = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) m = fmaxf(m, s[r]);
+    m = fmaxf(m, __shfl_xor(m, 32));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = __builtin_amdgcn_exp2f(s[r] * 0.1f - m);
+      lsum += s[r];
+    }
+    bf16x8 p0, p1;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      p0[r] = (__bf16)s[r];
+      p1[r] = (__bf16)s[8 + r];
+    }
+    auto vq = [&](int st) {
+      return *reinterpret_cast<const LDS_AS bf16x8*>(tile + ((st / 16) * 18 + st % 16) * 1024 + 16 * lane);
+    };
+    bf16x8 a0 = vq(0), a1 = vq(1);
+#pragma unroll
+    for (int st = 0; st < 32; ++st) {
+      bf16x8 a2 = a1;
+      if (st + 2 < 32) a2 = vq(st + 2);
+      o[st % 16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, (st / 16) ? p1 : p0, o[st % 16], 0, 0, 0);
+      copy_at(36 + st);
+      __builtin_amdgcn_sched_barrier(0);
+      a0 = a1;
+      a1 = a2;
+    }
+  }
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  if (threadIdx.x == 0) stamp(cycles, c0, r0);
+  float t = lsum;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) t += o[v][v];
+  if (t == 1234.5f) sink[threadIdx.x] = t;
+}
+
 template <int W, int NBUF, bool ROWS, bool READ>
 int launch_stream(const void* pool, const int32_t* pages, int grid, int per_wg, uint64_t* cyc,
                   uint32_t* sink, hipStream_t st) {
@@ -265,6 +394,22 @@ int mla_peak_lds(int grid, int waves, int iters, int tr, void* cycles, void* sin
                        (uint32_t*)sink);
   else
     return -1;
+  return (int)hipGetLastError();
+}
+
+/* Tile-loop probe: grid workgroups of 4 waves streaming per_wg tiles each
+ * (pool and pages as for mla_peak_stream), with the stage-1 loop's MFMA, LDS
+ * and VALU work per tile; copy = 0 runs the compute alone on the first tile.
+ * cycles and sink (device float [256]) as above. */
+int mla_peak_tileloop(const void* pool, const int32_t* pages, int grid, int per_wg, int copy,
+                      void* cycles, void* sink, void* stream) {
+  if (per_wg < 2 || per_wg % 2) return -1;
+  if (copy)
+    hipLaunchKernelGGL(tileloop_probe<true>, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                       (const uint8_t*)pool, pages, per_wg, (uint64_t*)cycles, (float*)sink);
+  else
+    hipLaunchKernelGGL(tileloop_probe<false>, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                       (const uint8_t*)pool, pages, per_wg, (uint64_t*)cycles, (float*)sink);
   return (int)hipGetLastError();
 }
 

@@ -31,6 +31,14 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), n
 
 
+def test_probe_library_exports_its_probes():
+    # the measured-ceiling probes bench.py --peaks calls (mla_peaks.hip)
+    from mla_paged_latent_decode_amd import _build
+    lib = ctypes.CDLL(_build.PEAKS_LIB_PATH)
+    for n in ("mla_peak_stream", "mla_peak_mfma", "mla_peak_lds", "mla_peak_tileloop"):
+        assert hasattr(lib, n), n
+
+
 def test_status_strings():
     for code in range(12):
         s = mla.mla_status_string(code)
