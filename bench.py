@@ -31,6 +31,10 @@ Extra modes:
                        load pattern, a v_mfma_f32_32x32x16_bf16 loop and
                        ds_read_b128 LDS reads
   --dcp G              time the cross-shard merge of G page shards
+  --zero-data          power study: the same batch, plan and pages with the
+                       query and the cache zeroed (same instructions and
+                       bytes, less switching power); the line says so in
+                       "data" and carries no counter traffic or CPU baseline
 """
 import argparse
 import csv
@@ -490,6 +494,7 @@ def main():
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--split", default="plan", choices=["plan", "pages", "single"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--zero-data", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--ingest-pmc", nargs="+", metavar="CSV")
     ap.add_argument("--peaks", action="store_true")
@@ -540,6 +545,9 @@ def main():
         kv = torch.from_numpy(inp.kv_bits).view(torch.float8_e4m3fn).to(dev)
     bt = torch.from_numpy(inp.block_table).to(dev)
     sl = torch.from_numpy(inp.seq_lens).to(dev)
+    if args.zero_data:
+        q.zero_()
+        kv.view(torch.uint8).zero_()  # any cache dtype (fp8 has no fill)
     # second copy of the cache with its pages moved (input preparation only)
     g = torch.Generator(device="cpu").manual_seed(1234)
     new_of_old = torch.randperm(kv.shape[0], generator=g).to(dev)
@@ -634,8 +642,9 @@ def main():
                 "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
     # the stored counters were read on the planner's launch configuration;
     # another split moves other partial bytes
-    roof["traffic"] = load_traffic(args.workload) if args.split == "plan" else None
-    counters = load_counters(args.workload) if args.split == "plan" else None
+    stored = args.split == "plan" and not args.zero_data
+    roof["traffic"] = load_traffic(args.workload) if stored else None
+    counters = load_counters(args.workload) if stored else None
     if counters and counters.get("mfma_flops_counted"):
         # MFMA work counted by the hardware for one launch, over the measured
         # launch time: the MFMA rate from counters rather than from the method
@@ -653,7 +662,8 @@ def main():
     out = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": w.kv_dtype, "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": w.kv_dtype,
+        "data": "synthetic, query and cache zeroed (power study)" if args.zero_data else "synthetic",
         "config": {"workload": f"{w.name}: {w.description}", "batch": w.batch,
                    "heads": w.num_heads, "head_size": w.head_size,
                    "kv_lora_rank": w.kv_lora_rank, "page_size": w.page_size,
@@ -671,7 +681,7 @@ def main():
         "wall_s": round(wall, 4),
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.zero_data:
         out["cpu_baseline"] = cpu_baseline(inp, alg)
     print(json.dumps(out), flush=True)
     return 0
