@@ -936,10 +936,12 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
           const uint32_t vbase0 = (uint32_t)(uintptr_t)tile + v_off0;
           const uint32_t vbase1 = (uint32_t)(uintptr_t)tile + v_off1;
           constexpr int NST = 2 * C::NVB;
-          // fragment of step st: v-block st/2, positions 16*(st%2) .. +15
+          // fragment of step st: positions 16*(st/NVB) .. +15 of v-block st%NVB
+          // (the half of the positions outer: 16 consecutive MFMAs share one
+          // weight operand and write 16 different accumulators)
           auto vread = [&](auto stc) __attribute__((always_inline)) {
             constexpr int st = decltype(stc)::value;
-            constexpr int off = ((st & 1) * C::NKQ + (st >> 1)) * 1024;
+            constexpr int off = ((st / C::NVB) * C::NKQ + st % C::NVB) * 1024;
             const u32x2 lo = ds_read_tr16_asm<off>(vbase0);
             const u32x2 hi = ds_read_tr16_asm<off>(vbase1);
             return u32x4{lo[0], lo[1], hi[0], hi[1]};
@@ -973,8 +975,8 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
                                             : wops(st - 2) + pairs(st + 1) + wops(st - 1) +
                                                   pairs(st + 2);
             lds_wait<later>(a0);
-            oacc[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, a0), (st & 1) ? p1 : p0, oacc[st >> 1], 0, 0, 0);
+            oacc[st % C::NVB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, a0), st < C::NVB ? p0 : p1, oacc[st % C::NVB], 0, 0, 0);
             dma_at(C::NKS + st);
             if constexpr (kWidenHere) {
               if constexpr (st % 3 == 2 && st / 3 < C::LPW) {
