@@ -126,7 +126,11 @@ typedef enum mla_dtype {
  *   sequence is reduced by one workgroup in a fixed order: the result of a
  *   sequence does not depend on the rest of the batch and is bitwise
  *   reproducible (the page's batch-invariant mode forces one split), and no
- *   workspace is needed.
+ *   workspace is needed.  Any fixed S keeps the same property: a sequence's
+ *   segments depend only on its own length and S, each is reduced in a fixed
+ *   order and stage 2 merges them in a fixed order, so a caller that fixes S
+ *   (rather than taking it from the batch's lengths) gets bitwise the same
+ *   result for a sequence in any batch, with up to S workgroups per sequence.
  *
  * MLA_SPLIT_BALANCED -- the batch's 32-position tiles, sequence after
  *   sequence, are cut into S equal runs ("work units"), one per workgroup and

@@ -236,6 +236,31 @@ def test_single_split_is_reproducible_and_batch_invariant(mla):
     assert np.array_equal(o4[0], o1[1]) and np.array_equal(l4[0], l1[1])
 
 
+@pytest.mark.parametrize("kv_dtype", [W.BF16, W.FP8_E4M3])
+@pytest.mark.parametrize("splits", [4, 16])
+def test_fixed_split_count_is_reproducible_and_batch_invariant(mla, kv_dtype, splits):
+    """The per-sequence split mode with a fixed split count: a sequence's
+    segments depend only on its own length and S, each is reduced in a fixed
+    tile order and stage 2 merges them in a fixed order, so its result is the
+    same bits in any batch (a deterministic mode that still spreads a long
+    sequence over S workgroups)."""
+    inp = W.small_case(seed=23, batch=6, num_heads=128, head_size=576, kv_lora_rank=512,
+                       page_size=64, seq_lens=(100, 1000, 37, 513, 64, 2000), kv_dtype=kv_dtype,
+                       k_scale=0.05 if kv_dtype == W.FP8_E4M3 else 1.0)
+    o1, l1 = run_gpu(mla, inp, splits, 0)
+    o2, l2 = run_gpu(mla, inp, splits, 0)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    order = [4, 1, 5, 0]
+    o3, l3 = run_gpu(mla, W.subset(inp, order), splits, 0)
+    assert np.array_equal(o3, o1[order]) and np.array_equal(l3, l1[order])
+    o4, l4 = run_gpu(mla, W.subset(inp, [5]), splits, 0)
+    assert np.array_equal(o4[0], o1[5]) and np.array_equal(l4[0], l1[5])
+    ro, rl = ref(inp)
+    assert_close(inp, o1, l1, ro, rl, f"{kv_dtype} S={splits}", rounding_slack=True)
+    o5, l5 = run_gpu(mla, inp, splits, 0, o_dtype=torch.float32)
+    assert_close(inp, o5, l5, ro, rl, f"{kv_dtype} S={splits} fp32 output")
+
+
 def test_split_results_are_reproducible(mla):
     inp = W.small_case(seed=19, batch=4, num_heads=128, head_size=576, kv_lora_rank=512,
                        page_size=64, seq_lens=(100, 3000, 37, 777))
