@@ -73,17 +73,19 @@ typedef enum mla_status {
                             境界と失敗), kv not bf16 / fp8 e4m3fn (per-tensor or
                             per-token scale) / per-token int8 / per-token int4, o not
                             bf16/fp32                                                    */
-  MLA_ERR_SHAPE = 5,     /* batch < 1, num_heads not a positive multiple of 16,
-                            num_blocks < 1 (empty cache), max_blocks_per_seq < 1, or a
-                            size whose byte count overflows                              */
+  MLA_ERR_SHAPE = 5,     /* batch < 1 or above MLA_MAX_BATCH, num_heads not a positive
+                            multiple of 16 or above MLA_MAX_ROWS, num_blocks < 1 (empty
+                            cache), max_blocks_per_seq < 1, a size whose byte count
+                            overflows, or a launch grid beyond the HIP limit             */
   MLA_ERR_SPLITS = 6,    /* num_kv_splits < 1 or above MLA_MAX_KV_SPLITS, or an unknown
                             split mode                                                   */
   MLA_ERR_WORKSPACE = 7, /* workspace NULL or smaller than mla_workspace_size() for the
                             same shape, split mode and split count                       */
   MLA_ERR_LAUNCH = 8,    /* HIP reported an error when the kernels were enqueued        */
   MLA_ERR_ARGUMENT = 9,  /* a non-finite or non-positive scale / k_scale, num_cus < 1,
-                            q_len outside [1, MLA_MAX_Q_LEN], topk < 1, or a misaligned
-                            pointer or query stride                                      */
+                            q_len outside [1, MLA_MAX_Q_LEN] or q_len x num_heads above
+                            MLA_MAX_ROWS, topk < 1, or a misaligned pointer or query
+                            stride                                                       */
   MLA_ERR_TABLE = 10,    /* mla_check_inputs: a length, block-table entry or top-k entry
                             out of range                                                 */
   MLA_ERR_SCRATCH = 11   /* mla_decode_noalloc: the split layout needs more workspace than
@@ -150,6 +152,8 @@ typedef enum mla_split_mode {
 #define MLA_MAX_KV_SPLITS 65536
 #define MLA_ROPE_DIM 64
 #define MLA_MAX_Q_LEN 16 /* query tokens per sequence in multi-token decode */
+#define MLA_MAX_ROWS 65536      /* query rows per sequence: num_heads x q_len */
+#define MLA_MAX_BATCH (1 << 24) /* sequences per call */
 
 /* Problem shape.  Layouts (all row-major, densely packed unless noted):
  *   q           [batch, num_heads, head_size]              q_dtype (bf16)
@@ -422,14 +426,15 @@ mla_status mla_check_inputs(const mla_shape* shape, const int32_t* block_table,
  *              (lse_base MLA_LSE_LN) or base 2 (MLA_LSE_LOG2)
  *   o          device, [rows][d_v], o_dtype MLA_BF16 or MLA_FP32, 16-byte
  *              aligned; lse device [rows] float32, natural log
- *   d_v        512 or 256 (kv_lora_rank); rows >= 1; 1 <= num_shards <=
- *              MLA_MAX_SHARDS
+ *   d_v        512 or 256 (kv_lora_rank); 1 <= rows <= MLA_MAX_MERGE_ROWS;
+ *              1 <= num_shards <= MLA_MAX_SHARDS
  * Buffers are caller-owned and may not overlap the outputs; one kernel is
  * enqueued on hip_stream; nothing is allocated.  Errors (nothing enqueued):
  * MLA_ERR_NULL, MLA_ERR_ARGUMENT (shard count, base or alignment),
  * MLA_ERR_SHAPE (rows), MLA_ERR_HEAD_SIZE (d_v), MLA_ERR_DTYPE. */
 typedef enum mla_lse_base { MLA_LSE_LN = 0, MLA_LSE_LOG2 = 1 } mla_lse_base;
 #define MLA_MAX_SHARDS 65536
+#define MLA_MAX_MERGE_ROWS ((int64_t)1 << 32)
 mla_status mla_merge_shards(int32_t num_shards, int64_t rows, int32_t d_v, const void* o_parts,
                             int32_t parts_dtype, const float* lse_parts, int32_t lse_base,
                             void* o, int32_t o_dtype, float* lse, void* hip_stream);

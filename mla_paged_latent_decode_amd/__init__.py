@@ -49,6 +49,9 @@ MLA_LSE_LN, MLA_LSE_LOG2 = 0, 1
 MLA_MAX_SHARDS = 65536
 MLA_MAX_KV_SPLITS = 65536
 MLA_MAX_Q_LEN = 16
+MLA_MAX_ROWS = 65536  # query rows per sequence: num_heads x q_len
+MLA_MAX_BATCH = 1 << 24
+MLA_MAX_MERGE_ROWS = 1 << 32
 
 
 class MlaShape(ctypes.Structure):

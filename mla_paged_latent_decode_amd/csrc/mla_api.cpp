@@ -84,8 +84,8 @@ static mla_status check_shape(const mla_shape* s) {
   if (s->kv_dtype != MLA_BF16 && s->kv_dtype != MLA_FP8_E4M3 && !per_token_kind(s->kv_dtype))
     return MLA_ERR_DTYPE;
   if (s->o_dtype != MLA_BF16 && s->o_dtype != MLA_FP32) return MLA_ERR_DTYPE;
-  if (s->batch < 1 || s->num_heads < 16 || s->num_heads % 16 != 0 || s->num_blocks < 1 ||
-      s->max_blocks_per_seq < 1)
+  if (s->batch < 1 || s->batch > MLA_MAX_BATCH || s->num_heads < 16 || s->num_heads % 16 != 0 ||
+      s->num_heads > MLA_MAX_ROWS || s->num_blocks < 1 || s->max_blocks_per_seq < 1)
     return MLA_ERR_SHAPE;
   // byte counts of the biggest buffers must fit comfortably in 64 bits
   const double kv_bytes = (double)s->num_blocks * s->page_size * s->head_size * 2.0;
@@ -101,8 +101,10 @@ static bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0
 // kernels' rows (row = token * H + head), so q [B, q_len, H, D] is q [B, rows, D].
 static bool row_shape(const mla_shape* s, int32_t q_len, mla_shape* out) {
   if (!s || q_len < 1 || q_len > MLA_MAX_Q_LEN) return false;
+  const int64_t rows = (int64_t)s->num_heads * q_len;
+  if (rows > MLA_MAX_ROWS) return false;
   *out = *s;
-  out->num_heads = s->num_heads * q_len;
+  out->num_heads = (int32_t)rows;
   return true;
 }
 
@@ -279,7 +281,8 @@ static mla_status decode_stages(const mla_shape* shape, int32_t q_len, const mla
     a.topk_idx = topk_idx;
     a.topk_stride = topk;
   }
-  return launch_decode(a, hip_stream, stages) == 0 ? MLA_OK : MLA_ERR_LAUNCH;
+  const int rc = launch_decode(a, hip_stream, stages);
+  return rc == 0 ? MLA_OK : rc == kGridTooLarge ? MLA_ERR_SHAPE : MLA_ERR_LAUNCH;
 }
 
 mla_status mla_decode(const mla_shape* shape, const void* q, const void* kv_cache,
@@ -455,7 +458,7 @@ mla_status mla_merge_shards(int32_t num_shards, int64_t rows, int32_t d_v, const
                             void* o, int32_t o_dtype, float* lse, void* hip_stream) {
   if (!o_parts || !lse_parts || !o || !lse) return MLA_ERR_NULL;
   if (num_shards < 1 || num_shards > MLA_MAX_SHARDS) return MLA_ERR_ARGUMENT;
-  if (rows < 1 || rows > ((int64_t)1 << 33)) return MLA_ERR_SHAPE;
+  if (rows < 1 || rows > MLA_MAX_MERGE_ROWS) return MLA_ERR_SHAPE;
   if (d_v != 512 && d_v != 256) return MLA_ERR_HEAD_SIZE;
   if ((parts_dtype != MLA_BF16 && parts_dtype != MLA_FP32) ||
       (o_dtype != MLA_BF16 && o_dtype != MLA_FP32))

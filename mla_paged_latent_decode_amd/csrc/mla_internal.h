@@ -133,6 +133,10 @@ extern thread_local LaunchTiming g_launch_timing[2];
 
 // Enqueues stage 1 and/or stage 2 (stage 2 only when the split layout needs
 // a merge).  Returns 0 or a HIP error code.
+// Enqueues the stages of a decode; 0, a HIP error code, or kGridTooLarge (nothing
+// enqueued) when a launch grid would exceed what HIP accepts (kMaxGrid workgroups).
+constexpr int kGridTooLarge = -1;
+constexpr int64_t kMaxGrid = 0x7fffffff;
 int launch_decode(const DecodeArgs& a, void* stream, int stages);
 
 // Cross-shard merge (mla_merge.hip).

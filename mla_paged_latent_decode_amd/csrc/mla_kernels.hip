@@ -1597,8 +1597,18 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   sp.score_log2 = a.scale * kLog2e * (tensor_scale ? a.k_scale : 1.f);
   sp.out_scale = tensor_scale ? a.k_scale : 1.f;
 
-  const int units = a.split_mode == 0 ? a.batch * a.num_splits : a.num_splits;
-  const int grid1 = (units + 7) / 8 * 8 * ht.head_chunks;
+  // stage 2's partial groups per head: about a quarter of the mean partial
+  // count per sequence (units / batch + 1), a power of two up to 8; one
+  // workgroup per (sequence, head group, 256 columns)
+  const int per_seq = a.split_mode == 0 ? a.num_splits : a.num_splits / a.batch + 1;
+  const int kgroups = per_seq >= 32 ? 8 : per_seq >= 16 ? 4 : per_seq >= 8 ? 2 : 1;
+  const int head_groups = a.heads / (kS2Rows / kgroups);
+  const int64_t units = a.split_mode == 0 ? (int64_t)a.batch * a.num_splits : a.num_splits;
+  const int64_t grid1_64 = (units + 7) / 8 * 8 * ht.head_chunks;
+  const int64_t grid2_64 = (int64_t)a.batch * head_groups * (a.d_v / kS2Cols);
+  // nothing is enqueued for a shape whose grid HIP cannot launch
+  if (grid1_64 > kMaxGrid || grid2_64 > kMaxGrid) return kGridTooLarge;
+  const int grid1 = (int)grid1_64;
   if (stages & kStage1) {
     // the group of variants: gather (+5) and cache format
     const int fmt = a.kv_pt ? 1 + a.kv_pt : (a.kv_fp8 ? 1 : 0);
@@ -1634,12 +1644,9 @@ int launch_decode(const DecodeArgs& a, void* stream, int stages) {
   s2.num_splits = a.num_splits;
   s2.seg_cost = sp.seg_cost;
   s2.len_cap = sp.len_cap;
-  // partial groups per head: about a quarter of the mean partial count per
-  // sequence (units / batch + 1), a power of two up to 8
-  const int per_seq = a.split_mode == 0 ? a.num_splits : a.num_splits / a.batch + 1;
-  s2.kgroups = per_seq >= 32 ? 8 : per_seq >= 16 ? 4 : per_seq >= 8 ? 2 : 1;
-  s2.head_groups = a.heads / (kS2Rows / s2.kgroups);
-  const int grid2 = a.batch * s2.head_groups * (a.d_v / kS2Cols);
+  s2.kgroups = kgroups;
+  s2.head_groups = head_groups;
+  const int grid2 = (int)grid2_64;
   return a.d_v == 512 ? launch_timed(1, mla_stage2<512>, dim3(grid2), dim3(256), st, s2)
                      : launch_timed(1, mla_stage2<256>, dim3(grid2), dim3(256), st, s2);
 }

@@ -139,6 +139,32 @@ def test_decode_argument_checks_fail_before_launch():
     assert _decode_raw(s, splits=16, ws=264, ws_bytes=need) == mla.MLA_ERR_ARGUMENT
 
 
+def test_size_caps_are_refused_before_launch():
+    # heads above MLA_MAX_ROWS, a batch above MLA_MAX_BATCH
+    with pytest.raises(mla.MlaError):
+        mla.mla_plan(shape(num_heads=mla.MLA_MAX_ROWS + 16), 1024, 0, 256)
+    with pytest.raises(mla.MlaError):
+        mla.mla_plan(shape(batch=mla.MLA_MAX_BATCH + 1, max_blocks_per_seq=1), 64, 0, 256)
+    assert mla.mla_plan(shape(num_heads=mla.MLA_MAX_ROWS), 1024, 0, 256)[0] == mla.SPLIT_BALANCED
+    # q_len x heads above MLA_MAX_ROWS (the product would not fit the row count)
+    lib = mla.load_library()
+    mode, splits, ws = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_size_t()
+    s = shape(num_heads=8192)
+    assert lib.mla_plan_mtp(ctypes.byref(s), 16, 1024, 0, 256, 0, ctypes.byref(mode),
+                            ctypes.byref(splits), ctypes.byref(ws)) == mla.MLA_ERR_ARGUMENT
+    assert lib.mla_plan_mtp(ctypes.byref(s), 8, 1024, 0, 256, 0, ctypes.byref(mode),
+                            ctypes.byref(splits), ctypes.byref(ws)) == mla.MLA_OK
+    # a launch grid beyond what HIP accepts is refused with nothing enqueued:
+    # 2^20 sequences x 64 splits x 512 head chunks of stage-1 workgroups
+    big = shape(batch=1 << 20, num_heads=mla.MLA_MAX_ROWS, max_blocks_per_seq=1)
+    need = mla.mla_workspace_size(big, 0, 64)
+    assert need > 0
+    assert _decode_raw(big, splits=64, ws=256, ws_bytes=need) == mla.MLA_ERR_SHAPE
+    # the shard merge's row cap keeps its grid in range
+    assert lib.mla_merge_shards(2, mla.MLA_MAX_MERGE_ROWS + 1, 512, 256, mla.MLA_BF16, 256,
+                                0, 256, mla.MLA_BF16, 256, None) == mla.MLA_ERR_SHAPE
+
+
 def test_fp8_query_is_refused():
     with pytest.raises(NotImplementedError):
         mla.mla_plan(shape(q_dtype=mla.MLA_FP8_E4M3), 100, 0, 256)
