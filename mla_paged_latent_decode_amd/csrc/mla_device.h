@@ -67,6 +67,23 @@ __device__ __forceinline__ int sgpr_here(int x) {
   return x;
 }
 
+// A read of an MFMA accumulator element (held in an AGPR) that the compiler
+// cannot reuse for a later read of the same element: a pass over all of a
+// wave's accumulators then does not keep VGPR copies of all of them alive
+// for the pass that follows (more than the VGPR file holds: spills).
+__device__ __forceinline__ float acc_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
+// A per-lane value the compiler cannot see through or move out of a loop:
+// what is derived from it is computed after this point, on every pass.
+__device__ __forceinline__ int vgpr_here(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ float wave_max_xor(float x, int mask) {
   return fmaxf(x, __shfl_xor(x, mask, 64));
 }

@@ -136,41 +136,46 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
   const int h0 = hc * C::HEADS_PER_WG + wave * HPW;  // first head of this wave
   const int H = p.heads;
 
-  // ---------------- per-lane constants of the LDS layout
-  // DMA: lane l writes slot l of a block: position t16 = l / 4, chunk
-  // c4 = (l % 4) ^ tile_swz(t16); its source offset within the 16-row page run.
-  const int dma_t16 = lane >> 2;
-  const int dma_c4 = (lane & 3) ^ tile_swz(dma_t16);
-  const int dma_voff = dma_t16 * C::SRC_ROW + 16 * dma_c4;
-  // fp8 widening: lane l converts chunk c4 = l % 4 of position t16 = l / 4
-  // of a block, read from the row-major staging tile and written to the
-  // chunk's slot of the bf16 tile layout
-  const uint32_t cv_src = (uint32_t)((lane >> 2) * C::CB + C::CVB * (lane & 3));
-  const uint32_t cv_dst = (uint32_t)(tile_slot(lane >> 2, lane & 3) * 16);
-  int qk_off_e, qk_off_o, v_off0, v_off1;
-  if constexpr (HPW == 32) {
-    // QK A operand: position t = lane % 32, chunk 2*ks + lane / 32
-    const int t = lane & 31, h2 = lane >> 5;
-    const int thb = (t >> 4) * C::NKQ * 1024;
-    qk_off_e = thb + tile_slot(t & 15, h2) * 16;      // ks even: c4 = h2
-    qk_off_o = thb + tile_slot(t & 15, 2 + h2) * 16;  // ks odd:  c4 = 2 + h2
-    // V^T A operand (transposed read): 4 positions x 16 v per 16-lane group
-    const int g = lane >> 4, i = lane & 15, half = lane >> 5;
-    const int c4 = 2 * (g & 1) + ((i >> 1) & 1);
-    v_off0 = tile_slot(4 * half + (i >> 2), c4) * 16 + 8 * (i & 1);
-    v_off1 = tile_slot(4 * half + (i >> 2) + 8, c4) * 16 + 8 * (i & 1);
-  } else {
-    qk_off_e = qk_off_o = tile_slot(lane & 15, lane >> 4) * 16;
-    const int g = lane >> 4, i = lane & 15;
-    const int t16 = 4 * g + (i >> 2);
-    v_off0 = tile_slot(t16, (i >> 1) & 1) * 16 + 8 * (i & 1);      // even v-block
-    v_off1 = tile_slot(t16, 2 + ((i >> 1) & 1)) * 16 + 8 * (i & 1);  // odd v-block
-  }
-
   const int P = p.page_size;
 
   // ---------------- one segment [ts, te) of sequence b
   auto process = [&](int b, int ts, int te, bool final_out, int slot, int vis_n) __attribute__((always_inline)) {
+    // The lane index once more, opaque to the compiler, so that the per-lane
+    // offsets below (and the epilogue's addresses) are formed per segment:
+    // derived from the kernel-wide lane they would be hoisted out of the
+    // segment loop and held, spilled to scratch, across every epilogue.
+    const int lane = vgpr_here(threadIdx.x & 63);
+    // ---------------- per-lane constants of the LDS layout
+    // DMA: lane l writes slot l of a block: position t16 = l / 4, chunk
+    // c4 = (l % 4) ^ tile_swz(t16); its source offset within the 16-row page run.
+    const int dma_t16 = lane >> 2;
+    const int dma_c4 = (lane & 3) ^ tile_swz(dma_t16);
+    const int dma_voff = dma_t16 * C::SRC_ROW + 16 * dma_c4;
+    // fp8 widening: lane l converts chunk c4 = l % 4 of position t16 = l / 4
+    // of a block, read from the row-major staging tile and written to the
+    // chunk's slot of the bf16 tile layout
+    const uint32_t cv_src = (uint32_t)((lane >> 2) * C::CB + C::CVB * (lane & 3));
+    const uint32_t cv_dst = (uint32_t)(tile_slot(lane >> 2, lane & 3) * 16);
+    int qk_off_e, qk_off_o, v_off0, v_off1;
+    if constexpr (HPW == 32) {
+      // QK A operand: position t = lane % 32, chunk 2*ks + lane / 32
+      const int t = lane & 31, h2 = lane >> 5;
+      const int thb = (t >> 4) * C::NKQ * 1024;
+      qk_off_e = thb + tile_slot(t & 15, h2) * 16;      // ks even: c4 = h2
+      qk_off_o = thb + tile_slot(t & 15, 2 + h2) * 16;  // ks odd:  c4 = 2 + h2
+      // V^T A operand (transposed read): 4 positions x 16 v per 16-lane group
+      const int g = lane >> 4, i = lane & 15, half = lane >> 5;
+      const int c4 = 2 * (g & 1) + ((i >> 1) & 1);
+      v_off0 = tile_slot(4 * half + (i >> 2), c4) * 16 + 8 * (i & 1);
+      v_off1 = tile_slot(4 * half + (i >> 2) + 8, c4) * 16 + 8 * (i & 1);
+    } else {
+      qk_off_e = qk_off_o = tile_slot(lane & 15, lane >> 4) * 16;
+      const int g = lane >> 4, i = lane & 15;
+      const int t16 = 4 * g + (i >> 2);
+      v_off0 = tile_slot(t16, (i >> 1) & 1) * 16 + 8 * (i & 1);      // even v-block
+      v_off1 = tile_slot(t16, 2 + ((i >> 1) & 1)) * 16 + 8 * (i & 1);  // odd v-block
+    }
+
     const int n_tiles = (te - ts + kTile - 1) / kTile;
     // this lane's row sees positions t < row_end (causal limit of its query
     // token; vis_n = n - q_len + 1 is the limit of token 0)
@@ -509,8 +514,16 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
     float lr_part = 0.f;      // the same over the bf16-rounded weights: normalises o
     typedef typename std::conditional<HPW == 32, f32x16, f32x4>::type acc_t;
     acc_t oacc[C::NVB];
+    {
+      // zeros from an opaque register: a constant zero vector would be kept
+      // kernel-wide (and spilled) rather than rematerialised per segment
+      const float zero = __uint_as_float((uint32_t)vgpr_here(0));
+      acc_t z;
 #pragma unroll
-    for (int vb = 0; vb < C::NVB; ++vb) oacc[vb] = acc_t{};
+      for (int r = 0; r < (int)(sizeof(acc_t) / sizeof(float)); ++r) z[r] = zero;
+#pragma unroll
+      for (int vb = 0; vb < C::NVB; ++vb) oacc[vb] = z;
+    }
 
     if constexpr (C::PIPE) {
       // ---- software-pipelined loop (bf16, 32-head waves, ring of 4: the
@@ -1165,7 +1178,8 @@ __global__ __launch_bounds__(64 * W) void mla_stage1(Stage1Params p) {
 #pragma unroll
       for (int vb = 0; vb < C::NVB; ++vb)
 #pragma unroll
-        for (int r = 0; r < (HPW == 32 ? 16 : 4); ++r) mx = fmaxf(mx, fabsf(oacc[vb][r]));
+        for (int r = 0; r < (HPW == 32 ? 16 : 4); ++r)
+          mx = fmaxf(mx, fabsf(HPW == 32 ? acc_read(oacc[vb][r]) : oacc[vb][r]));
       if constexpr (HPW == 16) mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = max_halves(mx) * inv;
       int e = 0;
