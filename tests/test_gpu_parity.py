@@ -142,6 +142,20 @@ def test_ragged_cases_fp8(mla, case, mode, splits):
     assert_close(inp, o, lse, ro, rl, label + " o=bf16", rounding_slack=True)
 
 
+@pytest.mark.parametrize("P", [512, 1024])
+@pytest.mark.parametrize("mode,splits", [(0, 1), (0, 5), (1, 9)])
+def test_large_pages_fp8(mla, P, mode, splits):
+    """Per-tensor fp8 cache in pages of 512 and 1024 rows (sequences ending
+    one row short of, and one row into, a page)."""
+    sl = (1, P - 1, P + 1, 3 * P + 5)
+    inp = W.small_case(seed=540 + P // 512, batch=len(sl), num_heads=128, head_size=576,
+                       kv_lora_rank=512, page_size=P, seq_lens=sl, extra_pages=1,
+                       kv_dtype=W.FP8_E4M3, k_scale=FP8_SCALE)
+    ro, rl = ref(inp)
+    o, lse = run_gpu(mla, inp, splits, mode, o_dtype=torch.float32)
+    assert_close(inp, o, lse, ro, rl, f"fp8 P={P} mode={mode} S={splits} o=f32")
+
+
 FINITE_E4M3 = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
 
 

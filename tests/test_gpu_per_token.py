@@ -286,3 +286,16 @@ def test_full_size_per_token(mla, name):
         o, lse = run_gpu(mla, inp, splits, mode, dev_inputs=dev_inputs)
         assert_close(o, lse, ro, rl, none_empty, f"{name} mode={mode} S={splits} o=bf16",
                      rounding_slack=True)
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("P", [512, 1024])
+@pytest.mark.parametrize("mode,splits", [(0, 1), (0, 5), (1, 9)])
+def test_large_pages(mla, P, dt, mode, splits):
+    """Pages of 512 and 1024 rows: in-page offsets beyond 64 K rows' bytes of
+    a 16-row run, and sequences that end one row into a page."""
+    sl = (1, P - 1, P + 1, 3 * P + 5)
+    inp = case(530 + P // 512, 128, 576, P, sl, dt, extra_pages=1)
+    ro, rl = ref(inp)
+    o, lse = run_gpu(mla, inp, splits, mode, o_dtype=torch.float32)
+    assert_close(o, lse, ro, rl, np.zeros(len(sl), bool), f"{dt} P={P} mode={mode} S={splits}")

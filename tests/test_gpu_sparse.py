@@ -90,6 +90,10 @@ SPARSE_CASES = [
     (64, 576, 64, (300, 2000), 200),
     (16, 320, 16, (1, 31, 33, 250, 513), 64),
     (128, 320, 32, (17, 95, 333), 72),
+    # page sizes that are no power of two (the gather divides by P) and large pages
+    (128, 576, 48, (1, 47, 48, 49, 500), 64),
+    (64, 576, 80, (3, 161, 700), 120),
+    (128, 576, 512, (1, 511, 513, 1600), 300),
 ]
 
 
@@ -152,6 +156,8 @@ QUANT_CASES = [
     (16, 576, 16, (1, 33, 64, 100), 48),
     (64, 576, 64, (300, 2000), 200),
     (128, 320, 32, (17, 95, 333), 72),
+    (128, 576, 48, (47, 49, 500), 64),
+    (128, 576, 1024, (1, 1025, 2500), 300),
 ]
 QUANT_DTYPES = [W.FP8_E4M3, W.FP8_PER_TOKEN, W.INT8_PER_TOKEN, W.INT4_PER_TOKEN]
 
