@@ -292,7 +292,8 @@ def run_probes(timed):
       1152-byte rows, pages in a seeded random order) through a ring of LDS
       tiles, one workgroup per CU, about the dsv3 cache's bytes per launch;
       the decode's configuration is 4 waves, ring 3, 16-row loads;
-    - mfma: v_mfma_f32_32x32x16_bf16 on every SIMD;
+    - mfma: v_mfma_f32_32x32x16_bf16 on every SIMD, on 8 independent
+      accumulator chains and on 1, 2 and 4 (cycles per MFMA);
     - lds: ds_read_b128 by 4 and 8 waves per CU;
     - tileloop: the stage-1 tile loop stripped to its copies, MFMAs, LDS
       operand reads and softmax-like VALU work, with and without the copies,
@@ -306,6 +307,7 @@ def run_probes(timed):
     vp, i32 = ctypes.c_void_p, ctypes.c_int
     lib.mla_peak_stream.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.mla_peak_mfma.argtypes = [i32, i32, vp, vp, vp]
+    lib.mla_peak_mfma_chain.argtypes = [i32, i32, i32, vp, vp, vp]
     lib.mla_peak_lds.argtypes = [i32, i32, i32, i32, vp, vp, vp]
     lib.mla_peak_tileloop.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
     dev = torch.device("cuda:0")
@@ -374,6 +376,14 @@ def run_probes(timed):
                                  "frac_of_spec": round(flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                                  "cycles_per_mfma": round(float(np.median(cycles)) / (iters * 8), 2),
                                  "mhz": round(mhz)}
+    for chains in (1, 2, 4):
+        def go_chain():
+            if lib.mla_peak_mfma_chain(grid, iters, chains, cyc.data_ptr(), sink.data_ptr(), stream):
+                raise RuntimeError("mla_peak_mfma_chain failed")
+        timed(go_chain)
+        cycles, mhz = clock(grid)
+        out[f"mfma_bf16_32x32x16_{chains}_chains"] = {
+            "cycles_per_mfma": round(float(np.median(cycles)) / (iters * 8), 2), "mhz": round(mhz)}
     for tr in (0, 1):
         for waves in (4, 8):
             lit = 200

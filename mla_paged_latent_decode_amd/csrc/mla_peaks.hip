@@ -12,6 +12,9 @@
 //                     (the QK^T + PV operand traffic of one tile per wave).
 //   mla_peak_mfma     a dependency-free loop of v_mfma_f32_32x32x16_bf16
 //                     (the decode's contraction instruction) on every SIMD.
+//   mla_peak_mfma_chain the same instruction on 1, 2, 4 or 8 accumulator
+//                     chains: with one chain every MFMA takes the previous
+//                     one's result as its accumulator (the decode's QK^T).
 //   mla_peak_lds      ds_read_b128 from LDS by 4 or 8 waves per workgroup.
 //   mla_peak_tileloop the stage-1 tile loop stripped to its resource use:
 //                     per 36 KB tile and wave, 9 copies in the decode's
@@ -144,6 +147,35 @@ __global__ __launch_bounds__(256) void mfma_probe(int iters, uint64_t* cycles, f
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < 8; ++c) s += acc[c][c];
+  if (s == 1234.5f) sink[threadIdx.x] = s;
+}
+
+// Each wave runs `iters` rounds of 8 v_mfma_f32_32x32x16_bf16 spread over CH
+// accumulator chains (CH = 1: each MFMA depends on the one before it).
+template <int CH>
+__global__ __launch_bounds__(256) void mfma_chain_probe(int iters, uint64_t* cycles, float* sink) {
+  static_assert(8 % CH == 0, "");
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (threadIdx.x + i));
+    b[i] = (__bf16)(0.002f * (i - 3));
+  }
+  f32x16 acc[CH] = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 8 / CH; ++r)
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) stamp(cycles, c0, r0);
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) s += acc[c][c];
   if (s == 1234.5f) sink[threadIdx.x] = s;
 }
 
@@ -367,6 +399,22 @@ int mla_peak_stream(const void* pool, const int32_t* pages, int grid, int per_wg
 int mla_peak_mfma(int grid, int iters, void* cycles, void* sink, void* stream) {
   hipLaunchKernelGGL(mfma_probe, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters,
                      (uint64_t*)cycles, (float*)sink);
+  return (int)hipGetLastError();
+}
+
+/* MFMA chain probe: as the MFMA probe, each wave's 8 MFMAs per round spread
+ * over `chains` accumulators (1, 2, 4 or 8; anything else returns -1). */
+int mla_peak_mfma_chain(int grid, int iters, int chains, void* cycles, void* sink, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  uint64_t* c = (uint64_t*)cycles;
+  float* k = (float*)sink;
+  switch (chains) {
+    case 1: hipLaunchKernelGGL(mfma_chain_probe<1>, dim3(grid), dim3(256), 0, st, iters, c, k); break;
+    case 2: hipLaunchKernelGGL(mfma_chain_probe<2>, dim3(grid), dim3(256), 0, st, iters, c, k); break;
+    case 4: hipLaunchKernelGGL(mfma_chain_probe<4>, dim3(grid), dim3(256), 0, st, iters, c, k); break;
+    case 8: hipLaunchKernelGGL(mfma_chain_probe<8>, dim3(grid), dim3(256), 0, st, iters, c, k); break;
+    default: return -1;
+  }
   return (int)hipGetLastError();
 }
 

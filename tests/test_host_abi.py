@@ -35,7 +35,8 @@ def test_probe_library_exports_its_probes():
     # the measured-ceiling probes bench.py --peaks calls (mla_peaks.hip)
     from mla_paged_latent_decode_amd import _build
     lib = ctypes.CDLL(_build.PEAKS_LIB_PATH)
-    for n in ("mla_peak_stream", "mla_peak_mfma", "mla_peak_lds", "mla_peak_tileloop"):
+    for n in ("mla_peak_stream", "mla_peak_mfma", "mla_peak_mfma_chain", "mla_peak_lds",
+              "mla_peak_tileloop"):
         assert hasattr(lib, n), n
 
 
