@@ -503,6 +503,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--split", default="plan", choices=["plan", "pages", "single"])
+    ap.add_argument("--fixed-splits", type=int, default=0, metavar="S",
+                    help="per-sequence split mode with S splits of every sequence (a fixed S "
+                         "is batch-invariant); overrides --split")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--zero-data", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -575,7 +578,10 @@ def main():
         sl = torch.from_numpy(inp.topk_lens).to(dev)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     ql = w.q_len
-    if args.split == "plan":
+    if args.fixed_splits > 0:
+        mode, splits = mla.SPLIT_PER_SEQUENCE, args.fixed_splits
+        ws_bytes = mla.mla_workspace_size(shape, mode, splits, ql)
+    elif args.split == "plan":
         mode, splits, ws_bytes = mla.mla_plan(shape, max_len, tot, cus, q_len=ql)
     elif args.split == "pages":
         mode, splits = mla.SPLIT_PER_SEQUENCE, mla.mla_pages_split_count(max_len, cus)
@@ -652,7 +658,7 @@ def main():
                 "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
     # the stored counters were read on the planner's launch configuration;
     # another split moves other partial bytes
-    stored = args.split == "plan" and not args.zero_data
+    stored = args.split == "plan" and not args.fixed_splits and not args.zero_data
     roof["traffic"] = load_traffic(args.workload) if stored else None
     counters = load_counters(args.workload) if stored else None
     if counters and counters.get("mfma_flops_counted"):
