@@ -111,6 +111,9 @@ CASES = [
     (16, 320, 16, (1, 31, 33, 250, 513)),
     (128, 320, 32, (17, 95, 333)),
     (256, 576, 64, (77, 129)),
+    (96, 576, 32, (5, 97, 300)),
+    (80, 576, 16, (1, 33, 129)),
+    (192, 576, 64, (64, 65, 400)),
 ]
 
 
